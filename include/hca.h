@@ -1,0 +1,257 @@
+/*
+ * hca.h - C ABI of the hybrid compressed-attention hot path (CSA + HCA) on gfx950.
+ *
+ * The method is DeepSeek-V4's hybrid attention as the pages describe it:
+ *   - "DeepSeek Releases V4 with Million-Token Context Optimized for AI Agents"
+ *     (botbeat.news), "Summary": CSA compresses KV entries 4x by softmax-gated
+ *     pooling with a learned positional bias and selects entries with a lightning
+ *     indexer; HCA compresses 128x and attends densely over all compressed entries.
+ *   - "DeepSeek V4: How They Crushed the Million-Token Memory Problem"
+ *     (sameershanbhag.com), "Two kinds of memory instead of one": every 4 / 128
+ *     tokens become one KV entry; the indexer uses ReLU-scored multi-head dot
+ *     products and keeps the top-k blocks; a separate sliding window keeps recent
+ *     tokens uncompressed; storage is FP8 for most KV, FP4 for the indexer and BF16
+ *     for the RoPE dimensions.
+ *   - "DeepSeek V4 infrastructure" (volanea.com), "Compression only works if the
+ *     attention path is engineered end to end": shared key-value multi-query
+ *     attention, partial rotary embeddings, a sliding-window branch and an
+ *     attention sink.
+ *
+ * Conventions for every entry point:
+ *   - Plain C.  Every call takes one descriptor whose first field `struct_size`
+ *     must equal sizeof(descriptor) (hca_struct_size reports it), and a stream
+ *     (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Every buffer pointer inside a descriptor is a DEVICE pointer owned by the
+ *     caller; rows are addressed with explicit pitches in BYTES.  The library
+ *     allocates nothing, frees nothing, never synchronizes and keeps no state
+ *     between calls other than the thread-local error message.
+ *   - Scratch memory comes from a caller-owned workspace of at least
+ *     hca_workspace_bytes() bytes, 256-byte aligned; its contents on entry do not
+ *     matter (the library clears what it needs).  Calls that share one workspace
+ *     must be ordered on one stream.
+ *   - Return value: HCA_OK (0) or a negative HCA_E_* code.  Argument errors are
+ *     detected on the host before anything is launched; HCA_E_LAUNCH reports a
+ *     launch failure.  hca_last_error() describes the last failure of the
+ *     calling thread.  Device-side CONTENTS (indices, positions, rows) are not
+ *     validated: they must satisfy the preconditions stated below, otherwise
+ *     results are undefined.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef HCA_H
+#define HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HCA_ABI_VERSION 1
+
+/* status codes */
+#define HCA_OK             0
+#define HCA_E_NULL        -1   /* a required pointer is NULL */
+#define HCA_E_SHAPE       -2   /* a size is out of range or inconsistent */
+#define HCA_E_ALIGN       -3   /* a pointer or pitch is misaligned */
+#define HCA_E_DTYPE       -4   /* unknown or disallowed element format */
+#define HCA_E_UNSUPPORTED -5   /* a valid combination this build does not implement */
+#define HCA_E_WORKSPACE   -6   /* workspace missing or too small */
+#define HCA_E_LAUNCH      -7   /* kernel launch failed */
+#define HCA_E_VERSION     -8   /* struct_size mismatch */
+
+/* element formats */
+#define HCA_F32      0   /* IEEE binary32 */
+#define HCA_BF16     1   /* bfloat16, round-to-nearest-even */
+#define HCA_FP8_E4M3 2   /* OCP FP8 E4M3FN (bias 7, max 448, no inf) */
+#define HCA_MXFP4    3   /* OCP MXFP4: E2M1 codes, 2 per byte (element 2i in the low
+                            nibble of byte i), one E8M0 scale byte per 32 elements */
+
+/* attention modes */
+#define HCA_MODE_CSA 0   /* attend to the indexer-selected entries */
+#define HCA_MODE_HCA 1   /* attend to every visible entry */
+
+/* operation ids for hca_workspace_bytes / hca_struct_size */
+#define HCA_OP_KV_COMPRESS  0
+#define HCA_OP_INDEXER_TOPK 1
+#define HCA_OP_ATTN_DECODE  2
+#define HCA_OP_ATTN_PREFILL 3
+#define HCA_STRUCT_KV_PLANES  100
+#define HCA_STRUCT_IDX_PLANES 101
+
+/*
+ * Compressed KV cache planes, one row per compressed entry (or per window token
+ * when used as raw storage).  D = D_n + D_r dims, the last D_r being the RoPE slice.
+ *   fmt HCA_F32:      f32   [rows, D] float, already rotated.
+ *   fmt HCA_FP8_E4M3: nope  [rows, D_n] E4M3 codes; value = code * scale[row]
+ *                     rope  [rows, D_r] BF16, already rotated
+ *                     scale [rows] float, a power of two (the smallest 2^e with
+ *                           max|nope| <= 448 * 2^e, 1 for an all-zero entry).
+ */
+typedef struct hca_kv_planes {
+  int32_t fmt;
+  int32_t reserved;
+  void*   f32;    int64_t f32_pitch;
+  void*   nope;   int64_t nope_pitch;
+  void*   rope;   int64_t rope_pitch;
+  void*   scale;
+} hca_kv_planes;
+
+/*
+ * Indexer vectors, one row of d_I elements per key (cache) or per (query, head).
+ *   fmt HCA_F32:      data [rows, d_I] float
+ *   fmt HCA_FP8_E4M3: data [rows, d_I] E4M3 codes, per-tensor scale 1
+ *   fmt HCA_MXFP4:    data [rows, d_I/2] packed E2M1, scales [rows, d_I/32] E8M0
+ */
+typedef struct hca_idx_planes {
+  int32_t fmt;
+  int32_t reserved;
+  void*   data;    int64_t pitch;
+  void*   scales;  int64_t scale_pitch;
+} hca_idx_planes;
+
+/*
+ * hca_kv_compress: softmax-gated pooling of aligned blocks of m raw tokens into
+ * compressed entries ("DeepSeek Releases V4 ...", botbeat.news, "Summary").
+ *
+ * For block n (raw rows block_row[n] .. block_row[n]+m-1, first token at absolute
+ * position block_pos[n], a multiple of m):
+ *   z_i     = gate_w . x_i + gate_b[i]            (x_i: raw, un-rotated, D dims)
+ *   alpha   = softmax(z) over the block's m tokens
+ *   c       = sum_i alpha_i x_i,   y = sum_i alpha_i y_i   (y: raw indexer keys)
+ *   entry   = [c_nope ; RoPE(block_pos[n] + m - 1) c_rope]
+ * RoPE is half-split: dims (i, i + D_r/2) of the slice rotate by
+ * pos * rope_base^(-2i/D_r).  Arithmetic is fp64; the entry is then encoded into
+ * `out` at row out_row[n] (f32, or FP8 nope + per-entry power-of-two scale + BF16
+ * rope), and y, when raw_idx is given, into `out_idx` (f32, FP8 with scale 1, or
+ * MXFP4), every encoding rounding to nearest-even once from fp64 (FP8 and FP4
+ * saturate).  `debug`, if not NULL, receives the pre-encoding values as f32
+ * [n_blocks, D + d_I] (d_I = 0 without raw_idx).
+ *
+ * Limits: 1 <= m <= 256, 2 <= D <= 1024, D_r even and 0 <= D_r <= D, d_I <= 256
+ * (a multiple of 32 for MXFP4).  raw/raw_idx rows are F32 or BF16 (raw_fmt).
+ * Preconditions on device data: every block's rows lie inside the raw buffers and
+ * out_row values are distinct rows of the output planes.  Needs no workspace.
+ */
+typedef struct hca_kv_compress_desc {
+  uint32_t struct_size;
+  int32_t  m, D, D_r, d_I;
+  int32_t  n_blocks;
+  double   rope_base;
+  int32_t  raw_fmt;
+  int32_t  reserved;
+  const void*    raw;      int64_t raw_pitch;
+  const void*    raw_idx;  int64_t raw_idx_pitch;
+  const int64_t* block_row;
+  const int64_t* block_pos;
+  const int64_t* out_row;
+  const float*   gate_w;   /* [D] */
+  const float*   gate_b;   /* [m] */
+  hca_kv_planes  out;
+  hca_idx_planes out_idx;  /* ignored when raw_idx is NULL */
+  float*         debug;
+} hca_kv_compress_desc;
+
+/*
+ * hca_indexer_topk: lightning-indexer scores and per-query top-k
+ * ("DeepSeek V4: How They Crushed ...", sameershanbhag.com, "Two kinds of memory
+ * instead of one").
+ *
+ * Query n belongs to sequence seq_id[n] and sits at absolute position q_pos[n];
+ * it sees entries j < V = floor((q_pos[n] + 1) / m) of its sequence, stored at
+ * key rows cache_row_start[seq] + j.  For every visible j:
+ *   d_h   = q[n, h] . key[j]                        (exact)
+ *   I_j   = sum_h w[n, h] * max(d_h, 0)
+ * Quantized operands (FP8 or MXFP4, same format for q and keys; d_I = 128,
+ * H_I a multiple of 16, <= 64): d_h is exact in binary32, and I_j is summed in
+ * binary32, un-fused, as (S_0 + S_1) + (S_2 + S_3) where S_g adds, from +0,
+ * the terms fl(w_h * max(d_h, +0)) of heads h = 16T + 4g + i in order T = 0,1,..
+ * then i = 0..3.  F32 operands: dots and the head sum in fp64, sequential,
+ * un-fused (V <= 4096 per query).
+ * Output: idx[n, 0..k) = the min(k, V) entries with the largest I (equal scores:
+ * lower j first), in ascending j, padded with -1; `score` (optional) gets their
+ * scores in the same order (f32, or f64 for F32 operands).
+ * max_visible must bound V for every query.  q and keys share `fmt`; `q` has
+ * Nq*H_I rows (row n*H_I + h).  w is [Nq, H_I] f32 with w >= 0.
+ */
+typedef struct hca_indexer_topk_desc {
+  uint32_t struct_size;
+  int32_t  Nq, B, H_I, d_I, k, m;
+  int32_t  reserved;
+  int64_t  max_visible;
+  hca_idx_planes q;
+  const float*   w;
+  hca_idx_planes keys;
+  const int64_t* cache_row_start;   /* [B] */
+  const int32_t* seq_id;            /* [Nq] */
+  const int64_t* q_pos;             /* [Nq] */
+  int32_t*       idx;               /* [Nq, k] */
+  void*          score;             /* [Nq, k] or NULL */
+  void*          workspace;
+  size_t         workspace_bytes;
+} hca_indexer_topk_desc;
+
+/*
+ * hca_attn_decode / hca_attn_prefill: shared-KV multi-query attention with one
+ * softmax over compressed entries, the sliding window and a sink
+ * ("DeepSeek V4 infrastructure", volanea.com, "Compression only works if the
+ * attention path is engineered end to end").
+ *
+ * Query n (sequence b = seq_id[n], position t = q_pos[n]) attends, with every one
+ * of its H heads, to the same key=value vectors:
+ *   - CSA: the entries idx[n, 0..k) that are >= 0 (an ascending, -1 padded list
+ *     as hca_indexer_topk writes it);  HCA: every entry j < floor((t+1)/m);
+ *   - the window tokens u = max(0, t-n_win+1) .. t read from the ring `win`
+ *     (row b*win_cap + u mod win_cap, un-rotated, io_fmt), RoPE-rotated at u;
+ * and entry j lives at cache row cache_row_start[b] + j (an idx value outside
+ * [0, floor((t+1)/m)) is skipped, never dereferenced).  The query's RoPE slice
+ * is rotated at t.  With logits l_a = tau * q_hat . kappa_a and the per-head sink
+ * logit sigma_h (not scaled by tau, zero value vector):
+ *   M = max(sigma_h, max_a l_a)
+ *   o = sum_a e^(l_a - M) kappa_a / (e^(sigma_h - M) + sum_a e^(l_a - M))
+ *   lse = M + log(e^(sigma_h - M) + sum_a e^(l_a - M))        (optional output)
+ * io_fmt HCA_F32 needs cache fmt HCA_F32 (fp64 arithmetic, any D <= 1024, at most
+ * 8192 keys per query); io_fmt HCA_BF16 needs cache fmt HCA_FP8_E4M3, D = 512,
+ * D_r = 64, H a multiple of 16 up to 64 (BF16 MFMA, fp32 softmax).
+ * The ring must hold every window token of every query: win_cap >= n_win plus the
+ * spread of the query positions of one sequence.  max_visible bounds
+ * floor((t+1)/m) over all queries.  hca_attn_prefill takes the same descriptor
+ * for a chunk of consecutive query positions and differs only in scheduling.
+ */
+typedef struct hca_attn_desc {
+  uint32_t struct_size;
+  int32_t  Nq, B, H, D, D_r, mode, m, k, n_win, win_cap;
+  float    tau;
+  int32_t  io_fmt;
+  double   rope_base;
+  int64_t  max_visible;
+  const void*    q;                 /* [Nq, H, D] io_fmt, un-rotated */
+  hca_kv_planes  cache;
+  const int64_t* cache_row_start;   /* [B] */
+  const int32_t* idx;               /* [Nq, k] (CSA), else NULL */
+  const void*    win;    int64_t win_pitch;
+  const float*   sink;              /* [H] */
+  const int32_t* seq_id;            /* [Nq] */
+  const int64_t* q_pos;             /* [Nq] */
+  void*          o;                 /* [Nq, H, D] io_fmt */
+  float*         lse;               /* [Nq, H] or NULL */
+  void*          workspace;
+  size_t         workspace_bytes;
+} hca_attn_desc;
+
+int         hca_abi_version(void);
+const char* hca_last_error(void);
+/* sizeof the descriptor of an HCA_OP_* id, or of an HCA_STRUCT_* plane struct; 0 if unknown */
+size_t      hca_struct_size(int which);
+/* workspace bytes the call described by (op, desc) needs; validates desc like the call */
+int         hca_workspace_bytes(int op, const void* desc, size_t* bytes);
+
+int hca_kv_compress(const hca_kv_compress_desc* desc, void* stream);
+int hca_indexer_topk(const hca_indexer_topk_desc* desc, void* stream);
+int hca_attn_decode(const hca_attn_desc* desc, void* stream);
+int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HCA_H */

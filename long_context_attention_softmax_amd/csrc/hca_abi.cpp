@@ -1,0 +1,321 @@
+// C ABI of the hybrid compressed-attention library: host-side argument checks,
+// workspace sizing and kernel dispatch.  Every check runs before anything is
+// launched, so argument errors never touch the device.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "../../include/hca.h"
+#include "hca_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define REQUIRE(cond, code, ...) \
+  do { if (!(cond)) return fail(code, __VA_ARGS__); } while (0)
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_kv_planes(const hca_kv_planes& p, int D, int D_r, const char* what, bool need) {
+  if (p.fmt == HCA_F32) {
+    if (!need) return HCA_OK;
+    REQUIRE(p.f32, HCA_E_NULL, "%s.f32 is NULL", what);
+    REQUIRE(p.f32_pitch >= 4LL * D, HCA_E_SHAPE, "%s.f32_pitch %lld < 4*D", what, (long long)p.f32_pitch);
+    REQUIRE(aligned(p.f32, 4) && p.f32_pitch % 4 == 0, HCA_E_ALIGN, "%s.f32 not 4-byte aligned", what);
+  } else if (p.fmt == HCA_FP8_E4M3) {
+    if (!need) return HCA_OK;
+    REQUIRE(p.nope && p.rope && p.scale, HCA_E_NULL, "%s: nope/rope/scale plane is NULL", what);
+    REQUIRE(p.nope_pitch >= D - D_r, HCA_E_SHAPE, "%s.nope_pitch too small", what);
+    REQUIRE(p.rope_pitch >= 2LL * D_r, HCA_E_SHAPE, "%s.rope_pitch too small", what);
+    REQUIRE(aligned(p.rope, 2) && p.rope_pitch % 2 == 0 && aligned(p.scale, 4), HCA_E_ALIGN,
+            "%s: rope must be 2-byte and scale 4-byte aligned", what);
+  } else {
+    return fail(HCA_E_DTYPE, "%s.fmt %d is not F32 or FP8_E4M3", what, p.fmt);
+  }
+  return HCA_OK;
+}
+
+int elem_bytes(int fmt) { return fmt == HCA_F32 ? 4 : (fmt == HCA_BF16 ? 2 : 1); }
+
+// ------------------------------------------------------------------ kv_compress
+int validate_kv_compress(const hca_kv_compress_desc* d) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_kv_compress_desc), HCA_E_VERSION,
+          "struct_size %u != %zu", d->struct_size, sizeof(hca_kv_compress_desc));
+  REQUIRE(d->m >= 1 && d->m <= 256, HCA_E_SHAPE, "m=%d outside [1, 256]", d->m);
+  REQUIRE(d->D >= 2 && d->D <= 1024, HCA_E_SHAPE, "D=%d outside [2, 1024]", d->D);
+  REQUIRE(d->D_r >= 0 && d->D_r <= d->D && d->D_r % 2 == 0, HCA_E_SHAPE, "D_r=%d must be even, <= D", d->D_r);
+  REQUIRE(d->n_blocks >= 0, HCA_E_SHAPE, "n_blocks=%d < 0", d->n_blocks);
+  REQUIRE(d->raw_fmt == HCA_F32 || d->raw_fmt == HCA_BF16, HCA_E_DTYPE, "raw_fmt %d not F32/BF16", d->raw_fmt);
+  REQUIRE(d->rope_base > 0.0, HCA_E_SHAPE, "rope_base must be > 0");
+  if (d->n_blocks == 0) return HCA_OK;
+  REQUIRE(d->raw && d->block_row && d->block_pos && d->out_row && d->gate_w && d->gate_b,
+          HCA_E_NULL, "raw, block_row, block_pos, out_row, gate_w and gate_b are required");
+  const int eb = elem_bytes(d->raw_fmt);
+  REQUIRE(d->raw_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE, "raw_pitch too small");
+  REQUIRE(aligned(d->raw, eb) && d->raw_pitch % eb == 0, HCA_E_ALIGN, "raw misaligned");
+  REQUIRE(aligned(d->gate_w, 4) && aligned(d->gate_b, 4) && aligned(d->block_row, 8) &&
+          aligned(d->block_pos, 8) && aligned(d->out_row, 8), HCA_E_ALIGN, "gate or block arrays misaligned");
+  int rc = check_kv_planes(d->out, d->D, d->D_r, "out", true);
+  if (rc) return rc;
+  if (d->raw_idx) {
+    REQUIRE(d->d_I >= 1 && d->d_I <= 256, HCA_E_SHAPE, "d_I=%d outside [1, 256]", d->d_I);
+    REQUIRE(d->raw_idx_pitch >= (int64_t)eb * d->d_I && aligned(d->raw_idx, eb) && d->raw_idx_pitch % eb == 0,
+            HCA_E_SHAPE, "raw_idx pitch/alignment");
+    const hca_idx_planes& o = d->out_idx;
+    REQUIRE(o.data, HCA_E_NULL, "out_idx.data is NULL");
+    if (o.fmt == HCA_F32) {
+      REQUIRE(o.pitch >= 4LL * d->d_I && aligned(o.data, 4) && o.pitch % 4 == 0, HCA_E_SHAPE, "out_idx f32 pitch");
+    } else if (o.fmt == HCA_FP8_E4M3) {
+      REQUIRE(o.pitch >= d->d_I, HCA_E_SHAPE, "out_idx fp8 pitch");
+    } else if (o.fmt == HCA_MXFP4) {
+      REQUIRE(d->d_I % 32 == 0, HCA_E_SHAPE, "MXFP4 needs d_I %% 32 == 0");
+      REQUIRE(o.scales, HCA_E_NULL, "out_idx.scales is NULL");
+      REQUIRE(o.pitch >= d->d_I / 2 && o.scale_pitch >= d->d_I / 32, HCA_E_SHAPE, "out_idx mxfp4 pitch");
+    } else {
+      return fail(HCA_E_DTYPE, "out_idx.fmt %d unknown", o.fmt);
+    }
+  }
+  return HCA_OK;
+}
+
+// ----------------------------------------------------------------- indexer_topk
+int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_indexer_topk_desc), HCA_E_VERSION,
+          "struct_size %u != %zu", d->struct_size, sizeof(hca_indexer_topk_desc));
+  REQUIRE(d->Nq >= 0 && d->B >= 1 && d->H_I >= 1 && d->d_I >= 1 && d->m >= 1, HCA_E_SHAPE,
+          "Nq>=0, B>=1, H_I>=1, d_I>=1, m>=1 required");
+  REQUIRE(d->k >= 1 && d->k <= (1 << 20), HCA_E_SHAPE, "k=%d outside [1, 2^20]", d->k);
+  REQUIRE(d->max_visible >= 0 && d->max_visible < (1LL << 31), HCA_E_SHAPE, "max_visible out of range");
+  const int fmt = d->q.fmt;
+  REQUIRE(fmt == d->keys.fmt, HCA_E_DTYPE, "q.fmt %d != keys.fmt %d", fmt, d->keys.fmt);
+  REQUIRE(fmt == HCA_F32 || fmt == HCA_FP8_E4M3 || fmt == HCA_MXFP4, HCA_E_DTYPE, "indexer fmt %d unknown", fmt);
+  if (fmt == HCA_F32) {
+    REQUIRE(d->max_visible <= 4096, HCA_E_UNSUPPORTED, "F32 indexer supports at most 4096 visible entries");
+    REQUIRE((int64_t)d->H_I * d->d_I <= 16384, HCA_E_UNSUPPORTED, "F32 indexer needs H_I*d_I <= 16384");
+  } else {
+    REQUIRE(d->d_I == 128, HCA_E_UNSUPPORTED, "quantized indexer needs d_I = 128 (got %d)", d->d_I);
+    REQUIRE(d->H_I % 16 == 0 && d->H_I <= 64, HCA_E_UNSUPPORTED, "quantized indexer needs H_I in {16,32,48,64}");
+  }
+  *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt);
+  if (d->Nq == 0) return HCA_OK;
+  REQUIRE(d->q.data && d->keys.data && d->w && d->cache_row_start && d->seq_id && d->q_pos && d->idx,
+          HCA_E_NULL, "q, keys, w, cache_row_start, seq_id, q_pos and idx are required");
+  const int64_t row_bytes = fmt == HCA_F32 ? 4LL * d->d_I : (fmt == HCA_FP8_E4M3 ? d->d_I : d->d_I / 2);
+  REQUIRE(d->q.pitch >= row_bytes && d->keys.pitch >= row_bytes, HCA_E_SHAPE, "q/keys pitch < row bytes");
+  if (fmt != HCA_F32) {
+    REQUIRE(aligned(d->q.data, 16) && aligned(d->keys.data, 16) && d->q.pitch % 16 == 0 && d->keys.pitch % 16 == 0,
+            HCA_E_ALIGN, "quantized q/keys need 16-byte aligned rows");
+  } else {
+    REQUIRE(aligned(d->q.data, 4) && aligned(d->keys.data, 4) && d->q.pitch % 4 == 0 && d->keys.pitch % 4 == 0,
+            HCA_E_ALIGN, "f32 q/keys need 4-byte aligned rows");
+  }
+  if (fmt == HCA_MXFP4)
+    REQUIRE(d->q.scales && d->keys.scales && d->q.scale_pitch >= 4 && d->keys.scale_pitch >= 4, HCA_E_NULL,
+            "MXFP4 q/keys need scale planes");
+  REQUIRE(aligned(d->w, 4) && aligned(d->idx, 4) && aligned(d->cache_row_start, 8) && aligned(d->q_pos, 8) &&
+          aligned(d->seq_id, 4), HCA_E_ALIGN, "w/idx/cache_row_start/q_pos/seq_id misaligned");
+  REQUIRE(d->workspace && d->workspace_bytes >= *ws, HCA_E_WORKSPACE, "workspace needs %zu bytes, got %zu",
+          *ws, d->workspace_bytes);
+  REQUIRE(aligned(d->workspace, 256), HCA_E_ALIGN, "workspace must be 256-byte aligned");
+  return HCA_OK;
+}
+
+// ---------------------------------------------------------------------- attention
+int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size %u != %zu",
+          d->struct_size, sizeof(hca_attn_desc));
+  REQUIRE(d->Nq >= 0 && d->B >= 1 && d->H >= 1 && d->m >= 1 && d->n_win >= 0, HCA_E_SHAPE,
+          "Nq>=0, B>=1, H>=1, m>=1, n_win>=0 required");
+  REQUIRE(d->mode == HCA_MODE_CSA || d->mode == HCA_MODE_HCA, HCA_E_SHAPE, "mode %d unknown", d->mode);
+  REQUIRE(d->mode == HCA_MODE_HCA || (d->k >= 1 && d->k <= (1 << 20)), HCA_E_SHAPE, "CSA needs 1 <= k <= 2^20");
+  REQUIRE(d->win_cap >= 1 && d->win_cap >= d->n_win, HCA_E_SHAPE, "win_cap must be >= max(1, n_win)");
+  REQUIRE(d->max_visible >= 0 && d->max_visible < (1LL << 31), HCA_E_SHAPE, "max_visible out of range");
+  REQUIRE(d->D_r >= 0 && d->D_r % 2 == 0 && d->D_r <= d->D, HCA_E_SHAPE, "D_r must be even and <= D");
+  REQUIRE(d->rope_base > 0.0, HCA_E_SHAPE, "rope_base must be > 0");
+  const int64_t max_set = (d->mode == HCA_MODE_CSA ? (int64_t)d->k : d->max_visible) + d->n_win;
+  if (d->io_fmt == HCA_F32) {
+    REQUIRE(d->cache.fmt == HCA_F32, HCA_E_DTYPE, "io_fmt F32 needs an F32 cache");
+    REQUIRE(d->D <= 1024 && d->D >= 2, HCA_E_SHAPE, "F32 attention needs 2 <= D <= 1024");
+    REQUIRE(d->D_r <= 1024, HCA_E_SHAPE, "D_r too large");
+    REQUIRE(max_set <= 4096, HCA_E_UNSUPPORTED, "F32 attention supports at most 4096 keys per query");
+  } else if (d->io_fmt == HCA_BF16) {
+    REQUIRE(d->cache.fmt == HCA_FP8_E4M3, HCA_E_DTYPE, "io_fmt BF16 needs an FP8_E4M3 cache");
+    REQUIRE(d->D == 512 && d->D_r == 64, HCA_E_UNSUPPORTED, "BF16 attention needs D=512, D_r=64");
+    REQUIRE(d->H % 16 == 0 && d->H <= 64, HCA_E_UNSUPPORTED, "BF16 attention needs H in {16,32,48,64}");
+  } else {
+    return fail(HCA_E_DTYPE, "io_fmt %d is not F32 or BF16", d->io_fmt);
+  }
+  *ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
+                                       d->io_fmt == HCA_F32, prefill);
+  if (d->Nq == 0) return HCA_OK;
+  REQUIRE(d->q && d->o && d->win && d->sink && d->seq_id && d->q_pos && d->cache_row_start, HCA_E_NULL,
+          "q, o, win, sink, seq_id, q_pos and cache_row_start are required");
+  REQUIRE(d->mode == HCA_MODE_HCA || d->idx, HCA_E_NULL, "CSA needs idx");
+  int rc = check_kv_planes(d->cache, d->D, d->D_r, "cache", true);
+  if (rc) return rc;
+  const int eb = elem_bytes(d->io_fmt);
+  REQUIRE(d->win_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE, "win_pitch too small");
+  if (d->io_fmt == HCA_BF16) {
+    REQUIRE(aligned(d->q, 16) && aligned(d->o, 2) && aligned(d->win, 16) && d->win_pitch % 16 == 0 &&
+            aligned(d->cache.nope, 16) && d->cache.nope_pitch % 16 == 0 && aligned(d->cache.rope, 16) &&
+            d->cache.rope_pitch % 16 == 0, HCA_E_ALIGN, "BF16 attention needs 16-byte aligned rows");
+  } else {
+    REQUIRE(aligned(d->q, 4) && aligned(d->o, 4) && aligned(d->win, 4) && d->win_pitch % 4 == 0,
+            HCA_E_ALIGN, "F32 attention needs 4-byte aligned rows");
+  }
+  REQUIRE(aligned(d->sink, 4) && aligned(d->seq_id, 4) && aligned(d->q_pos, 8) && aligned(d->cache_row_start, 8) &&
+          (!d->idx || aligned(d->idx, 4)) && (!d->lse || aligned(d->lse, 4)), HCA_E_ALIGN, "index arrays misaligned");
+  if (*ws) {
+    REQUIRE(d->workspace && d->workspace_bytes >= *ws, HCA_E_WORKSPACE, "workspace needs %zu bytes, got %zu",
+            *ws, d->workspace_bytes);
+    REQUIRE(aligned(d->workspace, 256), HCA_E_ALIGN, "workspace must be 256-byte aligned");
+  }
+  return HCA_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(HCA_E_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return HCA_OK;
+}
+
+int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
+  size_t ws = 0;
+  int rc = validate_attn(d, prefill, &ws);
+  if (rc) return rc;
+  if (d->Nq == 0) return HCA_OK;
+  hca::AttnArgs a{};
+  a.Nq = d->Nq; a.H = d->H; a.D = d->D; a.D_r = d->D_r; a.mode = d->mode; a.m = d->m;
+  a.k = d->mode == HCA_MODE_CSA ? d->k : 0; a.n_win = d->n_win; a.win_cap = d->win_cap;
+  a.io_f32 = d->io_fmt == HCA_F32; a.tau = d->tau; a.rope_base = d->rope_base;
+  a.max_visible = d->max_visible; a.q = d->q; a.cache_fmt = d->cache.fmt;
+  a.c_f32 = static_cast<const char*>(d->cache.f32); a.c_f32_pitch = d->cache.f32_pitch;
+  a.c_nope = static_cast<const char*>(d->cache.nope); a.c_nope_pitch = d->cache.nope_pitch;
+  a.c_rope = static_cast<const char*>(d->cache.rope); a.c_rope_pitch = d->cache.rope_pitch;
+  a.c_scale = static_cast<const float*>(d->cache.scale);
+  a.cache_row_start = d->cache_row_start; a.idx = d->mode == HCA_MODE_CSA ? d->idx : nullptr;
+  a.win = static_cast<const char*>(d->win); a.win_pitch = d->win_pitch;
+  a.sink = d->sink; a.seq_id = d->seq_id; a.q_pos = d->q_pos; a.o = d->o; a.lse = d->lse;
+  a.workspace = d->workspace; a.prefill = prefill;
+  return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hca_abi_version(void) { return HCA_ABI_VERSION; }
+
+const char* hca_last_error(void) { return g_err.c_str(); }
+
+size_t hca_struct_size(int which) {
+  switch (which) {
+    case HCA_OP_KV_COMPRESS: return sizeof(hca_kv_compress_desc);
+    case HCA_OP_INDEXER_TOPK: return sizeof(hca_indexer_topk_desc);
+    case HCA_OP_ATTN_DECODE:
+    case HCA_OP_ATTN_PREFILL: return sizeof(hca_attn_desc);
+    case HCA_STRUCT_KV_PLANES: return sizeof(hca_kv_planes);
+    case HCA_STRUCT_IDX_PLANES: return sizeof(hca_idx_planes);
+    default: return 0;
+  }
+}
+
+int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
+  REQUIRE(bytes, HCA_E_NULL, "bytes is NULL");
+  *bytes = 0;
+  size_t ws = 0;
+  int rc;
+  switch (op) {
+    case HCA_OP_KV_COMPRESS: rc = validate_kv_compress(static_cast<const hca_kv_compress_desc*>(desc)); break;
+    case HCA_OP_INDEXER_TOPK: {
+      // the size depends only on shapes: validate those, not the buffers
+      const hca_indexer_topk_desc* d = static_cast<const hca_indexer_topk_desc*>(desc);
+      REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+      REQUIRE(d->struct_size == sizeof(hca_indexer_topk_desc), HCA_E_VERSION, "struct_size mismatch");
+      REQUIRE(d->Nq >= 0 && d->max_visible >= 0, HCA_E_SHAPE, "Nq and max_visible must be >= 0");
+      ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, d->q.fmt);
+      rc = HCA_OK;
+      break;
+    }
+    case HCA_OP_ATTN_DECODE:
+    case HCA_OP_ATTN_PREFILL: {
+      const hca_attn_desc* d = static_cast<const hca_attn_desc*>(desc);
+      REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+      REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size mismatch");
+      REQUIRE(d->Nq >= 0 && d->H >= 1 && d->D >= 1 && d->max_visible >= 0, HCA_E_SHAPE, "bad shapes");
+      ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
+                                          d->io_fmt == HCA_F32, op == HCA_OP_ATTN_PREFILL);
+      rc = HCA_OK;
+      break;
+    }
+    default: return fail(HCA_E_SHAPE, "unknown op %d", op);
+  }
+  if (rc) return rc;
+  *bytes = ws;
+  return HCA_OK;
+}
+
+int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
+  int rc = validate_kv_compress(d);
+  if (rc) return rc;
+  if (d->n_blocks == 0) return HCA_OK;
+  hca::PoolArgs a{};
+  a.m = d->m; a.D = d->D; a.D_r = d->D_r; a.d_I = d->raw_idx ? d->d_I : 0; a.n_blocks = d->n_blocks;
+  a.rope_base = d->rope_base; a.raw_is_f32 = d->raw_fmt == HCA_F32;
+  a.raw = d->raw; a.raw_pitch = d->raw_pitch; a.raw_idx = d->raw_idx; a.raw_idx_pitch = d->raw_idx_pitch;
+  a.block_row = d->block_row; a.block_pos = d->block_pos; a.out_row = d->out_row;
+  a.gate_w = d->gate_w; a.gate_b = d->gate_b;
+  a.kv_fmt = d->out.fmt;
+  a.out_f32 = static_cast<char*>(d->out.f32); a.out_f32_pitch = d->out.f32_pitch;
+  a.out_nope = static_cast<char*>(d->out.nope); a.nope_pitch = d->out.nope_pitch;
+  a.out_rope = static_cast<char*>(d->out.rope); a.rope_pitch = d->out.rope_pitch;
+  a.out_scale = static_cast<float*>(d->out.scale);
+  a.idx_fmt = d->raw_idx ? d->out_idx.fmt : -1;
+  a.out_idx = static_cast<char*>(d->out_idx.data); a.idx_pitch = d->out_idx.pitch;
+  a.out_idx_scales = static_cast<char*>(d->out_idx.scales); a.idx_scale_pitch = d->out_idx.scale_pitch;
+  a.debug = d->debug;
+  return launched(hca::launch_pool(a, static_cast<hipStream_t>(stream)));
+}
+
+int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
+  size_t ws = 0;
+  int rc = validate_indexer(d, &ws);
+  if (rc) return rc;
+  if (d->Nq == 0) return HCA_OK;
+  hca::IndexerArgs a{};
+  a.Nq = d->Nq; a.H_I = d->H_I; a.d_I = d->d_I; a.k = d->k; a.m = d->m; a.fmt = d->q.fmt;
+  a.max_visible = d->max_visible;
+  a.score_pitch = (d->max_visible + 63) / 64 * 64;
+  a.q = static_cast<const char*>(d->q.data); a.q_pitch = d->q.pitch;
+  a.q_scales = static_cast<const uint8_t*>(d->q.scales); a.q_scale_pitch = d->q.scale_pitch;
+  a.w = d->w;
+  a.keys = static_cast<const char*>(d->keys.data); a.key_pitch = d->keys.pitch;
+  a.key_scales = static_cast<const uint8_t*>(d->keys.scales); a.key_scale_pitch = d->keys.scale_pitch;
+  a.cache_row_start = d->cache_row_start; a.seq_id = d->seq_id; a.q_pos = d->q_pos;
+  a.idx = d->idx; a.score_out = d->score;
+  a.scores = d->workspace;
+  size_t sb = (size_t)d->Nq * a.score_pitch * (a.fmt == HCA_F32 ? 8 : 4);
+  sb = (sb + 255) / 256 * 256;
+  a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(d->workspace) + sb);
+  return launched(hca::launch_indexer_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }
+
+int hca_attn_prefill(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 1); }
+
+}  // extern "C"

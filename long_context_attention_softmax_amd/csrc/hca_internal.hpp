@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI layer (hca_abi.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hca {
+
+struct PoolArgs {
+  int m, D, D_r, d_I, n_blocks;
+  double rope_base;
+  int raw_is_f32;
+  const void* raw; int64_t raw_pitch;
+  const void* raw_idx; int64_t raw_idx_pitch;
+  const int64_t* block_row; const int64_t* block_pos; const int64_t* out_row;
+  const float* gate_w; const float* gate_b;
+  int kv_fmt;                         // HCA_F32 | HCA_FP8_E4M3
+  char* out_f32; int64_t out_f32_pitch;
+  char* out_nope; int64_t nope_pitch;
+  char* out_rope; int64_t rope_pitch;
+  float* out_scale;
+  int idx_fmt;                        // HCA_F32 | HCA_FP8_E4M3 | HCA_MXFP4 ; -1 = none
+  char* out_idx; int64_t idx_pitch;
+  char* out_idx_scales; int64_t idx_scale_pitch;
+  float* debug;
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+
+struct IndexerArgs {
+  int Nq, H_I, d_I, k, m, fmt;        // fmt: HCA_F32 | HCA_FP8_E4M3 | HCA_MXFP4
+  int64_t max_visible, score_pitch;   // score_pitch: elements per query row of the workspace
+  const char* q; int64_t q_pitch; const uint8_t* q_scales; int64_t q_scale_pitch;
+  const float* w;
+  const char* keys; int64_t key_pitch; const uint8_t* key_scales; int64_t key_scale_pitch;
+  const int64_t* cache_row_start; const int32_t* seq_id; const int64_t* q_pos;
+  int32_t* idx; void* score_out;
+  void* scores;                       // workspace: f32 (quantized) or f64 (F32) [Nq, score_pitch]
+  uint32_t* hist;                     // workspace: [Nq, 2048] (quantized only)
+};
+hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt);
+
+struct AttnArgs {
+  int Nq, H, D, D_r, mode, m, k, n_win, win_cap, io_f32;
+  float tau; double rope_base;
+  int64_t max_visible;
+  const void* q;
+  int cache_fmt;
+  const char* c_f32; int64_t c_f32_pitch;
+  const char* c_nope; int64_t c_nope_pitch;
+  const char* c_rope; int64_t c_rope_pitch;
+  const float* c_scale;
+  const int64_t* cache_row_start; const int32_t* idx;
+  const char* win; int64_t win_pitch;
+  const float* sink; const int32_t* seq_id; const int64_t* q_pos;
+  void* o; float* lse;
+  void* workspace;
+  int prefill;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
+                                 int64_t max_visible, int io_f32, int prefill);
+
+}  // namespace hca

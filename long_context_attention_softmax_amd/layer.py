@@ -1,0 +1,119 @@
+"""One attention layer's device buffers and its step through the four entry points.
+
+A step, per layer ("DeepSeek Releases V4 ..." (botbeat.news), "Summary";
+"DeepSeek V4: How They Crushed the Million-Token Memory Problem"
+(sameershanbhag.com), "Two kinds of memory instead of one"):
+  1. hca_kv_compress pools the blocks the new tokens complete;
+  2. CSA only: hca_indexer_topk scores the visible entries and keeps the top-k;
+  3. hca_attn_decode / hca_attn_prefill attends with one softmax over the entries,
+     the window and the sink.
+All three are enqueued on the current stream with no host round trip.
+
+``DeviceLayer.from_host`` takes any object carrying the layer's host arrays
+(numpy) under the attribute names used below, uploads them once, and keeps them
+resident; ``step()`` then only launches kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _abi as A
+from .ops import IdxCache, KVCache, hca_attn_decode, hca_attn_prefill, hca_indexer_topk, hca_kv_compress
+
+
+def _t(x, device, dtype=None):
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.from_numpy(a).to(device)
+    return t if dtype is None else t.view(dtype)
+
+
+class DeviceLayer:
+    """Resident buffers of one layer (CSA or HCA) for a batch of queries."""
+
+    def __init__(self):
+        self.idx: Optional[torch.Tensor] = None
+        self.o: Optional[torch.Tensor] = None
+        self.lse: Optional[torch.Tensor] = None
+
+    @classmethod
+    def from_host(cls, lay, g, device="cuda") -> "DeviceLayer":
+        d = cls()
+        d.mode = A.MODE_CSA if lay.mode == "csa" else A.MODE_HCA
+        d.m, d.g, d.device = lay.m, g, torch.device(device)
+        d.f32 = lay.fmt == "f32"
+        dev = d.device
+        if d.f32:
+            d.cache = KVCache(f32=_t(lay.cache_f32, dev))
+            d.win = _t(lay.win, dev)
+            d.q = _t(lay.q, dev)
+        else:
+            d.cache = KVCache(nope=_t(lay.cache_nope, dev), rope=_t(lay.cache_rope, dev, torch.bfloat16),
+                              scale=_t(lay.cache_scale, dev))
+            d.win = _t(lay.win, dev, torch.bfloat16)
+            d.q = _t(lay.q, dev, torch.bfloat16)
+        d.W_cap = lay.W_cap
+        d.cache_row_start = _t(lay.cache_row_start.astype(np.int64), dev)
+        d.q_pos = _t(lay.q_pos.astype(np.int64), dev)
+        d.seq_id = _t(lay.seq_id.astype(np.int32), dev)
+        d.sink = _t(lay.sink.astype(np.float32), dev)
+        d.gate_w = _t(lay.gate_w.astype(np.float32), dev)
+        d.gate_b = _t(lay.gate_b.astype(np.float32), dev)
+        p = lay.pool
+        d.block_row = _t(p["block_row"].astype(np.int64), dev)
+        d.block_pos = _t(p["block_pos"].astype(np.int64), dev)
+        d.out_row = _t(p["out_row"].astype(np.int64), dev)
+        d.max_visible = int(((lay.q_pos + 1) // lay.m).max()) if len(lay.q_pos) else 0
+        d.Nq = len(lay.q_pos)
+        d.win_idx = None
+        if d.mode == A.MODE_CSA:
+            fmt = {"f32": A.F32, "fp8": A.FP8_E4M3, "mxfp4": A.MXFP4}[lay.idx_fmt]
+            if fmt == A.F32:
+                d.keys = IdxCache(_t(lay.idx_f32, dev), fmt)
+                d.qI = IdxCache(_t(lay.q_I, dev), fmt)
+            elif fmt == A.FP8_E4M3:
+                d.keys = IdxCache(_t(lay.idx_fp8, dev), fmt)
+                d.qI = IdxCache(_t(lay.q_I, dev), fmt)
+            else:
+                d.keys = IdxCache(_t(lay.idx_codes, dev), fmt, _t(lay.idx_scales, dev))
+                d.qI = IdxCache(_t(lay.q_I, dev), fmt, _t(lay.q_I_scales, dev))
+            d.w = _t(lay.w.astype(np.float32), dev)
+            if getattr(lay, "win_idx", None) is not None:
+                d.win_idx = _t(lay.win_idx, dev, None if d.f32 else torch.bfloat16)
+            d.idx = torch.empty((d.Nq, g.topk), dtype=torch.int32, device=dev)
+        d.o = torch.empty_like(d.q)
+        d.lse = torch.empty((d.Nq, g.H), dtype=torch.float32, device=dev)
+        return d
+
+    # ----------------------------------------------------------------- steps
+    def pool(self, debug: Optional[torch.Tensor] = None):
+        g = self.g
+        hca_kv_compress(self.win, self.block_row, self.block_pos, self.out_row, self.gate_w, self.gate_b,
+                        self.cache, m=self.m, D_r=g.D_r, rope_base=g.rope_base,
+                        raw_idx=self.win_idx if self.mode == A.MODE_CSA else None,
+                        out_idx=self.keys if self.mode == A.MODE_CSA else None, debug=debug)
+
+    def select(self, score: Optional[torch.Tensor] = None):
+        g = self.g
+        return hca_indexer_topk(self.qI, self.w, self.keys, self.cache_row_start, self.seq_id, self.q_pos,
+                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx, score=score)
+
+    def attend(self, prefill: bool = False):
+        g = self.g
+        fn = hca_attn_prefill if prefill else hca_attn_decode
+        return fn(self.q, self.cache, self.cache_row_start, self.win, self.sink, self.seq_id, self.q_pos,
+                  mode=self.mode, m=self.m, n_win=g.n_win, D_r=g.D_r, max_visible=self.max_visible,
+                  k=g.topk if self.mode == A.MODE_CSA else 0,
+                  idx=self.idx if self.mode == A.MODE_CSA else None, tau=g.tau,
+                  rope_base=g.rope_base, o=self.o, lse=self.lse)
+
+    def step(self, prefill: bool = False, pool: bool = True):
+        if pool:
+            self.pool()
+        if self.mode == A.MODE_CSA:
+            self.select()
+        return self.attend(prefill)

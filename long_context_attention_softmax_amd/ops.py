@@ -1,0 +1,237 @@
+"""Python boundary over the C ABI: the four entry points with the C names.
+
+Each function checks dtypes, devices and layouts of PyTorch tensors, fills the
+descriptor with raw device pointers and row pitches, and calls the library on the
+current HIP stream.  Outputs are written into caller tensors (or allocated here);
+workspaces are allocated once per (device, op) and reused (the library needs no
+particular contents in them).  There is no fallback: every result comes from the
+HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _abi as A
+
+_WS: dict = {}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+
+
+def _pitch(t: torch.Tensor) -> int:
+    """Row pitch in bytes of a tensor whose last dim is contiguous and whose leading
+    dims flatten to rows."""
+    if t.stride(-1) != 1:
+        raise ValueError("last dim must be contiguous")
+    for i in range(t.dim() - 2):
+        if t.stride(i) != t.stride(i + 1) * t.shape[i + 1]:
+            raise ValueError("leading dims must flatten into rows")
+    return (t.stride(-2) if t.dim() >= 2 else t.shape[-1]) * t.element_size()
+
+
+def _i64(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
+    if t.dtype != torch.int64 or t.numel() < n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int64 tensor of >= {n} elements")
+    return t
+
+
+def _workspace(op: int, nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (op, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:]
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class KVCache:
+    """Compressed KV planes: ``f32`` [N, D] float, or FP8 ``nope`` [N, D_n] uint8 +
+    ``rope`` [N, D_r] int16/bfloat16 bits + ``scale`` [N] float."""
+    f32: Optional[torch.Tensor] = None
+    nope: Optional[torch.Tensor] = None
+    rope: Optional[torch.Tensor] = None
+    scale: Optional[torch.Tensor] = None
+
+    @property
+    def fmt(self) -> int:
+        return A.F32 if self.f32 is not None else A.FP8_E4M3
+
+    def planes(self) -> A.KvPlanes:
+        p = A.KvPlanes()
+        p.fmt = self.fmt
+        if self.f32 is not None:
+            _need_cuda(self.f32)
+            if self.f32.dtype != torch.float32:
+                raise ValueError("f32 plane must be float32")
+            p.f32, p.f32_pitch = _ptr(self.f32), _pitch(self.f32)
+        else:
+            _need_cuda(self.nope, self.rope, self.scale)
+            if self.nope.dtype != torch.uint8 or self.rope.element_size() != 2 or self.scale.dtype != torch.float32:
+                raise ValueError("FP8 planes: nope uint8, rope 16-bit, scale float32")
+            p.nope, p.nope_pitch = _ptr(self.nope), _pitch(self.nope)
+            p.rope, p.rope_pitch = _ptr(self.rope), _pitch(self.rope)
+            p.scale = _ptr(self.scale)
+        return p
+
+
+@dataclass
+class IdxCache:
+    """Indexer vectors: f32 [N, d_I] float, FP8 [N, d_I] uint8, or MXFP4 packed
+    [N, d_I/2] uint8 + ``scales`` [N, d_I/32] uint8."""
+    data: torch.Tensor
+    fmt: int
+    scales: Optional[torch.Tensor] = None
+
+    def planes(self) -> A.IdxPlanes:
+        _need_cuda(self.data, self.scales)
+        p = A.IdxPlanes()
+        p.fmt = self.fmt
+        d = self.data.reshape(-1, self.data.shape[-1])
+        p.data, p.pitch = _ptr(d), _pitch(d)
+        if self.scales is not None:
+            s = self.scales.reshape(-1, self.scales.shape[-1])
+            p.scales, p.scale_pitch = _ptr(s), _pitch(s)
+        return p
+
+
+def _raw_fmt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return A.F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return A.BF16
+    raise ValueError("raw rows must be float32 or bfloat16 (bits)")
+
+
+def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch.Tensor,
+                    out_row: torch.Tensor, gate_w: torch.Tensor, gate_b: torch.Tensor,
+                    out: KVCache, *, m: int, D_r: int, rope_base: float = 10000.0,
+                    raw_idx: Optional[torch.Tensor] = None, out_idx: Optional[IdxCache] = None,
+                    debug: Optional[torch.Tensor] = None) -> None:
+    """Pool the listed blocks of ``raw`` rows into ``out`` (and ``out_idx``)."""
+    raw2 = raw.reshape(-1, raw.shape[-1])
+    n = block_row.numel()
+    _need_cuda(raw2, block_row, block_pos, out_row, gate_w, gate_b, raw_idx, debug)
+    d = A.new_desc(A.KvCompressDesc)
+    d.m, d.D, d.D_r, d.n_blocks, d.rope_base = m, raw2.shape[1], D_r, n, rope_base
+    d.raw_fmt = _raw_fmt(raw2)
+    d.raw, d.raw_pitch = _ptr(raw2), _pitch(raw2)
+    d.block_row = _ptr(_i64(block_row, n, "block_row"))
+    d.block_pos = _ptr(_i64(block_pos, n, "block_pos"))
+    d.out_row = _ptr(_i64(out_row, n, "out_row"))
+    if gate_w.dtype != torch.float32 or gate_b.dtype != torch.float32:
+        raise ValueError("gate_w and gate_b must be float32")
+    d.gate_w, d.gate_b = _ptr(gate_w.contiguous()), _ptr(gate_b.contiguous())
+    d.out = out.planes()
+    if raw_idx is not None:
+        ri = raw_idx.reshape(-1, raw_idx.shape[-1])
+        if _raw_fmt(ri) != d.raw_fmt:
+            raise ValueError("raw_idx must have raw's dtype")
+        d.d_I = ri.shape[1]
+        d.raw_idx, d.raw_idx_pitch = _ptr(ri), _pitch(ri)
+        d.out_idx = out_idx.planes()
+    if debug is not None:
+        d.debug = _ptr(debug)
+    A.check(A.lib.hca_kv_compress(ctypes.byref(d), _stream()))
+
+
+def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: torch.Tensor,
+                     seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
+                     max_visible: int, idx: Optional[torch.Tensor] = None,
+                     score: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k entries per query.  q.data is [Nq, H_I, ...]; returns idx [Nq, k] int32."""
+    Nq, H_I = q.data.shape[0], q.data.shape[1]
+    d_I = q.data.shape[-1] * (2 if q.fmt == A.MXFP4 else 1)
+    _need_cuda(w, cache_row_start, seq_id, q_pos, idx, score)
+    if idx is None:
+        idx = torch.empty((Nq, k), dtype=torch.int32, device=w.device)
+    d = A.new_desc(A.IndexerTopkDesc)
+    d.Nq, d.B, d.H_I, d.d_I, d.k, d.m = Nq, cache_row_start.numel(), H_I, d_I, k, m
+    d.max_visible = max_visible
+    d.q = q.planes()
+    d.keys = keys.planes()
+    if w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError("w must be contiguous float32 [Nq, H_I]")
+    d.w = _ptr(w)
+    d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    if seq_id.dtype != torch.int32:
+        raise ValueError("seq_id must be int32")
+    d.seq_id = _ptr(seq_id)
+    d.q_pos = _ptr(_i64(q_pos, Nq, "q_pos"))
+    d.idx = _ptr(idx)
+    d.score = _ptr(score)
+    nb = A.workspace_bytes(A.OP_INDEXER_TOPK, d)
+    ws = _workspace(A.OP_INDEXER_TOPK, nb, w.device)
+    d.workspace, d.workspace_bytes = _ptr(ws), nb
+    A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
+    return idx
+
+
+def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: torch.Tensor,
+          win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
+          mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
+          idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
+          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    Nq, H, D = q.shape
+    _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
+    io = A.F32 if q.dtype == torch.float32 else A.BF16
+    if io == A.BF16 and q.dtype != torch.bfloat16:
+        q = q.view(torch.bfloat16)
+    if o is None:
+        o = torch.empty_like(q)
+    d = A.new_desc(A.AttnDesc)
+    d.Nq, d.B, d.H, d.D, d.D_r = Nq, cache_row_start.numel(), H, D, D_r
+    d.mode, d.m, d.k, d.n_win, d.win_cap = mode, m, k, n_win, win.shape[-2]
+    d.tau, d.io_fmt, d.rope_base, d.max_visible = tau, io, rope_base, max_visible
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [Nq, H, D]")
+    d.q = _ptr(q)
+    d.cache = cache.planes()
+    d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    if idx is not None:
+        if idx.dtype != torch.int32 or not idx.is_contiguous():
+            raise ValueError("idx must be contiguous int32 [Nq, k]")
+        d.idx = _ptr(idx)
+    w2 = win.reshape(-1, win.shape[-1])
+    d.win, d.win_pitch = _ptr(w2), _pitch(w2)
+    d.sink = _ptr(sink.contiguous())
+    d.seq_id = _ptr(seq_id)
+    d.q_pos = _ptr(_i64(q_pos, Nq, "q_pos"))
+    d.o = _ptr(o)
+    d.lse = _ptr(lse)
+    op = A.OP_ATTN_PREFILL if prefill else A.OP_ATTN_DECODE
+    nb = A.workspace_bytes(op, d)
+    ws = _workspace(op, nb, q.device)
+    d.workspace, d.workspace_bytes = _ptr(ws), nb
+    fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
+    A.check(fn(ctypes.byref(d), _stream()))
+    return o
+
+
+def hca_attn_decode(*args, **kw) -> torch.Tensor:
+    """One-softmax attention of decode queries (see include/hca.h)."""
+    return _attn(False, *args, **kw)
+
+
+def hca_attn_prefill(*args, **kw) -> torch.Tensor:
+    """One-softmax attention of a chunk of consecutive query positions."""
+    return _attn(True, *args, **kw)

@@ -70,7 +70,7 @@ def encode_entry(entry: np.ndarray, D_r: int, kv_fmt: str):
     codes, n_fr = quant.fp8_encode(nope / s[:, None], return_fragile=True)
     bits, r_fr = quant.bf16_encode(rp, return_fragile=True)
     fragile = np.concatenate([n_fr | s_fr[:, None], r_fr], axis=1)
-    return dict(nope=codes, rope=bits, scale=s.astype(np.float32), fragile=fragile)
+    return dict(nope=codes, rope=bits, scale=s.astype(np.float32), fragile=fragile, scale_fragile=s_fr)
 
 
 def encode_idx(y_hat: np.ndarray, idx_fmt: str):

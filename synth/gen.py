@@ -81,7 +81,7 @@ def _fp8_entries(rng, n: int, D_n: int, chunk: int = 1 << 16):
 
 def _bf16_normal(rng, shape, std=1.0, chunk_rows: int = 1 << 16):
     out = np.empty(shape, np.uint16)
-    flat = out.reshape(shape[0], -1)
+    flat = out.reshape(shape[0], int(np.prod(shape[1:])))
     for s in range(0, shape[0], chunk_rows):
         t = min(shape[0], s + chunk_rows)
         flat[s:t] = bf16_bits(_normal(rng, (t - s, flat.shape[1]), std))
@@ -90,7 +90,7 @@ def _bf16_normal(rng, shape, std=1.0, chunk_rows: int = 1 << 16):
 
 def _fp8_normal(rng, shape, std, chunk_rows: int = 1 << 16):
     out = np.empty(shape, np.uint8)
-    flat = out.reshape(shape[0], -1)
+    flat = out.reshape(shape[0], int(np.prod(shape[1:])))
     for s in range(0, shape[0], chunk_rows):
         t = min(shape[0], s + chunk_rows)
         flat[s:t] = fp8_codes(_normal(rng, (t - s, flat.shape[1]), std))

@@ -1,0 +1,109 @@
+"""Shared helpers of the GPU parity tests: run a workload layer on the HIP path and
+compare each stage with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import step as ostep
+
+TOL_QUANT = 2e-2     # per-row relative error, BF16/FP8 paths
+TOL_F32 = 1e-5       # per-row relative error, f32 path
+
+
+def row_rel_err(o: np.ndarray, ref: np.ndarray) -> float:
+    """max over (query, head) rows of max|o - ref| / max|ref|."""
+    o = np.asarray(o, np.float64).reshape(-1, o.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((np.abs(o - ref).max(axis=1) / den).max())
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_codes_equal(got, want, fragile, what):
+    got, want = np.asarray(got), np.asarray(want)
+    bad = got != want
+    if fragile is not None:
+        bad &= ~np.asarray(fragile, bool)
+    n = int(bad.sum())
+    assert n == 0, f"{what}: {n} mismatching codes (of {bad.size}); first at {np.argwhere(bad)[:3].tolist()}"
+
+
+def check_pool(dev, pooled, lay):
+    """Compare the rows the GPU pooled with the oracle's encodings."""
+    rows = torch.from_numpy(np.asarray(pooled["out_row"], np.int64)).to(dev.device)
+    kv = pooled["kv"]
+    if rows.numel() == 0:
+        return
+    if dev.f32:
+        got = to_np(dev.cache.f32[rows])
+        assert_codes_equal(got.view(np.uint32), kv["f32"].view(np.uint32), kv["fragile"], "pooled f32 entry")
+    else:
+        D_n = kv["nope"].shape[1]
+        fr = kv["fragile"]
+        sc_ok = ~kv["scale_fragile"]
+        got_s = to_np(dev.cache.scale[rows])
+        assert np.array_equal(got_s[sc_ok], kv["scale"][sc_ok]), "pooled entry scales differ"
+        keep = sc_ok & (got_s == kv["scale"])
+        assert_codes_equal(to_np(dev.cache.nope[rows])[keep], kv["nope"][keep], fr[keep, :D_n], "pooled FP8 nope")
+        assert_codes_equal(to_np(dev.cache.rope[rows]).view(np.uint16), kv["rope"], fr[:, D_n:], "pooled BF16 rope")
+    if "idx" in pooled:
+        ix = pooled["idx"]
+        if "f32" in ix:
+            got = to_np(dev.keys.data[rows])
+            assert_codes_equal(got.view(np.uint32), ix["f32"].view(np.uint32), ix["fragile"], "pooled f32 key")
+        elif "fp8" in ix:
+            assert_codes_equal(to_np(dev.keys.data[rows]), ix["fp8"], ix["fragile"], "pooled FP8 key")
+        else:
+            got_c = to_np(dev.keys.data[rows])
+            got_s = to_np(dev.keys.scales[rows])
+            fr = ix["fragile"]
+            blk_fr = fr.reshape(fr.shape[0], -1, 32).any(axis=2)
+            assert_codes_equal(got_s, ix["scales"], blk_fr, "pooled MXFP4 key scales")
+            # compare element codes through their nibbles
+            lo_g, hi_g = got_c & 15, got_c >> 4
+            lo_w, hi_w = ix["codes"] & 15, ix["codes"] >> 4
+            assert_codes_equal(lo_g, lo_w, fr[:, 0::2], "pooled MXFP4 key (even)")
+            assert_codes_equal(hi_g, hi_w, fr[:, 1::2], "pooled MXFP4 key (odd)")
+
+
+def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, check_scores=True):
+    """Run the layer's step on the GPU and compare every stage with the oracle.
+
+    Returns (oracle result, device layer)."""
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    dev = dev or DeviceLayer.from_host(lay, g)
+    tol = tol if tol is not None else (TOL_F32 if dev.f32 else TOL_QUANT)
+    dev.pool()
+    score = None
+    if dev.mode == 0:
+        score = torch.zeros((dev.Nq, g.topk), dtype=torch.float64 if dev.f32 else torch.float32,
+                            device=dev.device)
+        dev.select(score=score)
+    o = dev.attend(prefill=prefill)
+    torch.cuda.synchronize()
+    ref = ostep.run_layer(lay, g, queries=queries)
+    qs = ref["queries"]
+    check_pool(dev, ref["pooled"], lay)
+    if dev.mode == 0:
+        got_idx = to_np(dev.idx)[qs]
+        for n in range(len(qs)):
+            assert np.array_equal(got_idx[n], ref["idx"][n]), \
+                f"top-k set differs for query {qs[n]} (t={lay.q_pos[qs[n]]})"
+    got_o = to_np(o)[qs]
+    got_o = got_o.astype(np.float64) if dev.f32 else bf16_values(got_o)
+    err = row_rel_err(got_o, ref["o"])
+    assert err <= tol, f"output rel err {err:.3e} > {tol}"
+    lse = to_np(dev.lse)[qs]
+    # lse is stored as float32
+    assert np.allclose(lse, ref["lse"], rtol=1e-4 if not dev.f32 else 1e-6, atol=1e-3 if not dev.f32 else 1e-6)
+    return ref, dev, err

@@ -1,0 +1,169 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/hca.h declares, the ctypes mirrors match the C struct sizes, and host-side
+validation rejects bad arguments with the documented codes before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hca.h")
+
+A = pytest.importorskip("long_context_attention_softmax_amd._abi",
+                        reason="HIP library not built (run __graft_entry__.build())")
+
+FAKE = 0x100000          # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(hca_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) == set(A.EXPORTS)
+    for n in names:
+        assert hasattr(A.lib, n), n
+
+
+def test_version_and_struct_sizes():
+    assert A.lib.hca_abi_version() == 1
+    for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
+                    (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
+                    (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
+        assert A.lib.hca_struct_size(op) == ctypes.sizeof(cls), cls
+    assert A.lib.hca_struct_size(12345) == 0
+
+
+def call(fn, desc):
+    return getattr(A.lib, fn)(ctypes.byref(desc), None)
+
+
+def kv_desc(**kw):
+    d = A.new_desc(A.KvCompressDesc)
+    d.m, d.D, d.D_r, d.n_blocks, d.rope_base, d.raw_fmt = 4, 512, 64, 2, 1e4, A.BF16
+    d.raw, d.raw_pitch = FAKE, 1024
+    d.block_row = d.block_pos = d.out_row = d.gate_w = d.gate_b = FAKE
+    d.out.fmt = A.FP8_E4M3
+    d.out.nope, d.out.nope_pitch, d.out.rope, d.out.rope_pitch, d.out.scale = FAKE, 448, FAKE, 128, FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_kv_compress_validation():
+    assert A.lib.hca_kv_compress(None, None) == -1
+    d = kv_desc()
+    d.struct_size = 8
+    assert call("hca_kv_compress", d) == -8
+    assert call("hca_kv_compress", kv_desc(m=0)) == -2
+    assert call("hca_kv_compress", kv_desc(m=300)) == -2
+    assert call("hca_kv_compress", kv_desc(D_r=63)) == -2
+    assert call("hca_kv_compress", kv_desc(raw_fmt=A.FP8_E4M3)) == -4
+    assert call("hca_kv_compress", kv_desc(raw=None)) == -1
+    assert call("hca_kv_compress", kv_desc(raw_pitch=100)) == -2
+    assert call("hca_kv_compress", kv_desc(raw=FAKE + 1)) == -3
+    d = kv_desc()
+    d.out.fmt = 7
+    assert call("hca_kv_compress", d) == -4
+    d = kv_desc()
+    d.out.scale = None
+    assert call("hca_kv_compress", d) == -1
+    d = kv_desc(raw_idx=FAKE, raw_idx_pitch=256, d_I=128)
+    d.out_idx.fmt, d.out_idx.data, d.out_idx.pitch = A.MXFP4, FAKE, 64
+    assert call("hca_kv_compress", d) == -1          # MXFP4 without scales
+    d.d_I = 100
+    d.out_idx.scales, d.out_idx.scale_pitch = FAKE, 4
+    assert call("hca_kv_compress", d) == -2          # d_I not a multiple of 32
+    assert b"multiple of 32" in A.lib.hca_last_error() or b"32" in A.lib.hca_last_error()
+    assert call("hca_kv_compress", kv_desc(n_blocks=0, raw=None)) == 0   # nothing to do
+
+
+def idx_desc(**kw):
+    d = A.new_desc(A.IndexerTopkDesc)
+    d.Nq, d.B, d.H_I, d.d_I, d.k, d.m, d.max_visible = 8, 8, 64, 128, 512, 4, 32768
+    d.q.fmt = d.keys.fmt = A.FP8_E4M3
+    d.q.data, d.q.pitch, d.keys.data, d.keys.pitch = FAKE, 128, FAKE, 128
+    d.w = d.cache_row_start = d.seq_id = d.q_pos = d.idx = FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_indexer_validation_and_workspace():
+    n = ctypes.c_size_t(0)
+    d = idx_desc()
+    assert A.lib.hca_workspace_bytes(A.OP_INDEXER_TOPK, ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 8 * 32768 * 4 + 8 * 2048 * 4
+    d.workspace, d.workspace_bytes = FAKE, n.value - 1
+    assert call("hca_indexer_topk", d) == -6
+    d.workspace = None
+    assert call("hca_indexer_topk", d) == -6
+    assert call("hca_indexer_topk", idx_desc(d_I=64)) == -5
+    assert call("hca_indexer_topk", idx_desc(H_I=20)) == -5
+    assert call("hca_indexer_topk", idx_desc(k=0)) == -2
+    d = idx_desc()
+    d.keys.fmt = A.MXFP4
+    assert call("hca_indexer_topk", d) == -4
+    d = idx_desc()
+    d.q.fmt = d.keys.fmt = A.F32
+    d.max_visible = 5000
+    assert call("hca_indexer_topk", d) == -5
+    d = idx_desc(w=None)
+    d.workspace, d.workspace_bytes = FAKE, 1 << 30
+    assert call("hca_indexer_topk", d) == -1
+    d = idx_desc()
+    d.q.data = FAKE + 8
+    d.workspace, d.workspace_bytes = FAKE, 1 << 30
+    assert call("hca_indexer_topk", d) == -3
+    assert call("hca_indexer_topk", idx_desc(Nq=0)) == 0
+
+
+def attn_desc(**kw):
+    d = A.new_desc(A.AttnDesc)
+    d.Nq, d.B, d.H, d.D, d.D_r, d.mode, d.m, d.k, d.n_win, d.win_cap = 8, 8, 64, 512, 64, 0, 4, 512, 128, 128
+    d.tau, d.io_fmt, d.rope_base, d.max_visible = 1.0, A.BF16, 1e4, 32768
+    d.q = d.o = d.win = d.sink = d.seq_id = d.q_pos = d.cache_row_start = d.idx = FAKE
+    d.win_pitch = 1024
+    d.cache.fmt = A.FP8_E4M3
+    d.cache.nope, d.cache.nope_pitch, d.cache.rope, d.cache.rope_pitch, d.cache.scale = FAKE, 448, FAKE, 128, FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_attention_validation():
+    n = ctypes.c_size_t(0)
+    d = attn_desc()
+    assert A.lib.hca_workspace_bytes(A.OP_ATTN_DECODE, ctypes.byref(d), ctypes.byref(n)) == 0
+    if n.value:
+        d.workspace, d.workspace_bytes = FAKE, n.value - 1
+        assert call("hca_attn_decode", d) == -6
+    assert call("hca_attn_decode", attn_desc(D=256)) == -5
+    assert call("hca_attn_decode", attn_desc(H=40)) == -5
+    assert call("hca_attn_decode", attn_desc(io_fmt=A.FP8_E4M3)) == -4
+    assert call("hca_attn_decode", attn_desc(win_cap=64)) == -2
+    assert call("hca_attn_decode", attn_desc(mode=5)) == -2
+    assert call("hca_attn_decode", attn_desc(idx=None, workspace=FAKE, workspace_bytes=1 << 40)) == -1
+    d = attn_desc(io_fmt=A.F32, D=128, D_r=32)
+    d.cache.fmt = A.FP8_E4M3
+    assert call("hca_attn_prefill", d) == -4
+    d = attn_desc(io_fmt=A.F32, D=128, D_r=32, k=8000)
+    d.cache.fmt = A.F32
+    assert call("hca_attn_decode", d) == -5
+    d = attn_desc(q=FAKE + 4, workspace=FAKE, workspace_bytes=1 << 40)
+    assert call("hca_attn_decode", d) == -3
+    assert call("hca_attn_decode", attn_desc(Nq=0)) == 0
+    assert b"" != A.lib.hca_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    from long_context_attention_softmax_amd import ops
+    x = torch.zeros(8, 512, dtype=torch.bfloat16)
+    i = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        ops.hca_kv_compress(x, i, i, i, torch.zeros(512), torch.zeros(4), ops.KVCache(f32=torch.zeros(4, 512)),
+                            m=4, D_r=64)
