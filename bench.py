@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the hybrid compressed-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: for each layer, pool the
+blocks the new token completes, score + top-k with the lightning indexer (CSA),
+and attend with one softmax over the entries, the window and the sink.
+
+Primary workload (``value``): the ragged interleaved CSA+HCA decode layer pair -
+32 sequences with seeded log-uniform context lengths in [4096, 1048576], 64 query
+heads, D = 512 (448 FP8 + 64 BF16 RoPE), FP8 indexer 64x128, top-512, window 128.
+``value`` is decoded tokens per second (one token per sequence per step through
+both layers).  Secondary fields of the same line: CSA decode at 128K (8 x 131072),
+HCA decode at 1M (4 x 1048576) and the MXFP4 prefill indexer of a 4096-token chunk
+after a 1M prefix (TFLOP/s of the scoring kernel).
+
+Inputs are seeded synthetic data shaped like those workloads, resident in HBM
+before timing; each workload is replicated until the replicas exceed 1 GiB and the
+steps rotate through them, so the 256 MiB last-level cache cannot serve them.
+``roofline`` reports the dominant kernel (the CSA indexer scoring kernel) against
+the 8 TB/s HBM peak, timed by HIP events recorded around it on its own stream.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the primary
+workload on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s and HBM GB/s at 1M ctx (CSA+HCA); prefill indexer TFLOPs"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
+ENTRY_BYTES = 448 + 128 + 4          # FP8 nope + BF16 rope + f32 scale
+TOKEN_BYTES = 512 * 2                # raw BF16 window token
+KEY_BYTES = 128                      # FP8 indexer key
+QO_BYTES = 2 * 64 * 512 * 2          # BF16 q and o
+QI_W_BYTES = 64 * 128 + 64 * 4       # FP8 indexer query + f32 head weights
+
+
+# ---------------------------------------------------------------- byte models
+def csa_bytes(lengths, k=512, n_win=128):
+    """Algorithmic HBM bytes of one CSA decode step (query at t = L - 1), each
+    byte once: indexer keys of the visible entries, the k gathered entries, the
+    window tokens, q/o, q_I/w, and the pooled entry + key (write) plus the raw
+    indexer-key tokens it reads when the new token completes a block."""
+    total = 0
+    keys = 0
+    for L in lengths:
+        V = L // 4
+        keys += V * KEY_BYTES + QI_W_BYTES
+        total += V * KEY_BYTES + QI_W_BYTES + min(k, V) * ENTRY_BYTES
+        total += min(n_win, L) * TOKEN_BYTES + QO_BYTES
+        if L % 4 == 0:
+            total += ENTRY_BYTES + KEY_BYTES + 4 * 128 * 2
+    return total, keys
+
+
+def hca_bytes(lengths, n_win=128):
+    total = 0
+    ent = 0
+    for L in lengths:
+        V = L // 128
+        ent += V * ENTRY_BYTES
+        total += V * ENTRY_BYTES + min(n_win, L) * TOKEN_BYTES + QO_BYTES
+        if L % 128 == 0:
+            total += ENTRY_BYTES
+    return total, ent
+
+
+def prefill_indexer_flops(prefix, T, H_I=64, d_I=128):
+    t = prefix + np.arange(T, dtype=np.int64)
+    pairs = int(((t + 1) // 4).sum())
+    return pairs * H_I * d_I * 2, pairs
+
+
+# ---------------------------------------------------------------- GPU timing
+class Timed:
+    def __init__(self, name, layer_sets, prefill=False):
+        self.name, self.sets, self.prefill = name, layer_sets, prefill
+
+    def run(self, steps, warmup, prof_layer=0, prof_kind="select"):
+        import torch
+        R = len(self.sets)
+        for i in range(warmup):
+            for lay in self.sets[i % R]:
+                lay.step(prefill=self.prefill)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:          # create the handles before passing them to the library
+            a.record()
+            b.record()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            for li, lay in enumerate(self.sets[i % R]):
+                p = evs[i] if li == prof_layer else None
+                lay.step(prefill=self.prefill, prof_select=p if prof_kind == "select" else None,
+                         prof_attend=p if prof_kind == "attend" else None)
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        return total_ms / steps, kern_ms
+
+
+def replicate(layers, step_bytes, min_total=1 << 30, cap=64):
+    reps = max(2, min(cap, math.ceil(min_total / max(step_bytes, 1))))
+    sets = [layers]
+    for _ in range(reps - 1):
+        sets.append([l.clone() for l in layers])
+    return sets
+
+
+def device_layers(w):
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    return [DeviceLayer.from_host(l, w.g) for l in w.layers]
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, sample_every=1, repeats=5):
+    """The fp64 oracle on every ``sample_every``-th sequence of the workload, both
+    layers, full step (pooling, scores, top-k, attention); median of ``repeats`` runs."""
+    from oracle import step as ostep
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    sel = np.arange(0, w.B, sample_every)
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        for lay in w.layers:
+            qs = np.flatnonzero(np.isin(lay.seq_id, sel))
+            ostep.run_layer(lay, w.g, queries=qs)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": round(len(sel) / t, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(sel)} of {w.B} sequences (every {sample_every}th; lengths "
+                      f"{[int(x) for x in w.lengths[sel]]}), both layers, full step, median of {repeats} "
+                      f"({t:.2f} s per pass)"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true", help="time the primary workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|hca|prefill)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences are independent, so more GPUs shard the batch with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth.configs import config_by_name
+    torch.cuda.set_device(0)
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    out = {}
+    secondary = {}
+    only = args.only
+
+    # ---- primary: ragged CSA+HCA layer pair ---------------------------------
+    if only in (None, "ragged"):
+        cfg = config_by_name("ragged_pair_32")
+        t0 = time.time()
+        w5 = synth.make(cfg)
+        L = [int(x) for x in w5.lengths]
+        cb, ckeys = csa_bytes(L)
+        hb, _ = hca_bytes(L)
+        log(f"[bench] ragged pair: generated in {time.time() - t0:.1f}s, {cb / 1e6:.1f} + {hb / 1e6:.1f} MB/step")
+        sets = replicate(device_layers(w5), cb + hb)
+        log(f"[bench] ragged pair: {len(sets)} replicas resident")
+        ms, kern = Timed("ragged", sets).run(args.steps, args.warmup, prof_layer=0, prof_kind="select")
+        kern_avg = float(kern.mean())
+        step_bytes = cb + hb
+        out.update(dict(
+            value=round(w5.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+            hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1), bytes_per_step=step_bytes,
+            config={"workload": "ragged_pair_32", "batch": w5.B, "context_lengths": L,
+                    "layers": "CSA (m=4, FP8 indexer 64x128, top-512) + HCA (m=128)",
+                    "heads": 64, "head_dim": 512, "window": 128, "replicas": len(sets)},
+            roofline={"bound": "hbm", "kernel": "score_quant_kernel<FP8> (CSA indexer scoring)",
+                      "achieved": round(ckeys / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                      "unit": "GB/s", "frac": round(ckeys / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "traffic": None, "algorithmic_bytes_per_launch": ckeys,
+                      "avg_launch_ms": round(kern_avg, 5)}))
+        log(f"[bench] ragged pair: {ms:.4f} ms/step, scoring kernel {kern_avg:.4f} ms")
+        del sets
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary or only:
+        # ---- CSA decode at 128K --------------------------------------------
+        if only in (None, "csa"):
+            w2 = synth.make("csa_decode_128k")
+            L2 = [int(x) for x in w2.lengths]
+            cb2, ck2 = csa_bytes(L2)
+            sets = replicate(device_layers(w2), cb2)
+            ms2, k2 = Timed("csa", sets).run(args.steps, args.warmup, prof_kind="select")
+            secondary["csa_decode_128k"] = dict(
+                tokens_per_s=round(w2.B / (ms2 * 1e-3), 1), ms_per_step=round(ms2, 4),
+                hbm_gbps=round(cb2 / (ms2 * 1e-3) / 1e9, 1),
+                hbm_frac=round(cb2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), bytes_per_step=cb2,
+                scoring_kernel_ms=round(float(k2.mean()), 5),
+                scoring_kernel_gbps=round(ck2 / (float(k2.mean()) * 1e-3) / 1e9, 1), replicas=len(sets))
+            log(f"[bench] csa 128k: {ms2:.4f} ms/step")
+            del sets
+            torch.cuda.empty_cache()
+        # ---- HCA decode at 1M ----------------------------------------------
+        if only in (None, "hca"):
+            w3 = synth.make("hca_decode_1m")
+            L3 = [int(x) for x in w3.lengths]
+            hb3, _ = hca_bytes(L3)
+            sets = replicate(device_layers(w3), hb3)
+            ms3, k3 = Timed("hca", sets).run(args.steps, args.warmup, prof_kind="attend")
+            secondary["hca_decode_1m"] = dict(
+                tokens_per_s=round(w3.B / (ms3 * 1e-3), 1), ms_per_step=round(ms3, 4),
+                hbm_gbps=round(hb3 / (ms3 * 1e-3) / 1e9, 1),
+                hbm_frac=round(hb3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), bytes_per_step=hb3,
+                attention_kernel_ms=round(float(k3.mean()), 5), replicas=len(sets))
+            log(f"[bench] hca 1m: {ms3:.4f} ms/step")
+            del sets
+            torch.cuda.empty_cache()
+        # ---- prefill indexer (MXFP4) -----------------------------------------
+        if only in (None, "prefill"):
+            w4 = synth.make("csa_prefill_1m")
+            flops, pairs = prefill_indexer_flops(w4.prefix, w4.T)
+            lays = device_layers(w4)
+            csa4 = lays[0]
+            steps4 = max(3, min(10, args.steps // 10))
+            for _ in range(2):
+                csa4.pool()
+                csa4.select()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps4)]
+            for a, b in evs:
+                a.record()
+                b.record()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s0.record()
+            for i in range(steps4):
+                for lay in lays:
+                    lay.pool()
+                csa4.select(prof=evs[i])
+                csa4.attend(prefill=True)
+            s1.record()
+            torch.cuda.synchronize()
+            chunk_ms = s0.elapsed_time(s1) / steps4
+            kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+            secondary["csa_prefill_1m"] = dict(
+                indexer_scoring_tflops=round(flops / (kms * 1e-3) / 1e12, 1),
+                indexer_scoring_ms=round(kms, 3),
+                fp8_peak_frac=round(flops / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                fp4_peak_frac=round(flops / (kms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                scoring_flop=flops, visible_pairs=pairs, chunk_ms=round(chunk_ms, 3),
+                chunk_tokens_per_s=round(w4.T / (chunk_ms * 1e-3), 1))
+            log(f"[bench] prefill: chunk {chunk_ms:.3f} ms, scoring {kms:.3f} ms")
+            del lays, csa4
+            torch.cuda.empty_cache()
+
+    if only is None and not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w5)
+
+    line = {"metric": METRIC, "value": out.get("value"), "unit": out.get("unit", "tokens/s"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": out.get("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8+bf16 (fp32 accumulate)", "data": "synthetic (seeded)",
+            "config": out.get("config", {"workload": only}),
+            "hbm_gbps": out.get("hbm_gbps"), "roofline": out.get("roofline"),
+            "cpu_baseline": out.get("cpu_baseline"), "secondary": secondary}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -189,6 +189,10 @@ typedef struct hca_indexer_topk_desc {
   void*          score;             /* [Nq, k] or NULL */
   void*          workspace;
   size_t         workspace_bytes;
+  /* optional hipEvent_t pair (as void*) recorded on the stream immediately before
+     and after the scoring kernel, for timing it in isolation; NULL = none */
+  void*          prof_begin;
+  void*          prof_end;
 } hca_indexer_topk_desc;
 
 /*
@@ -237,6 +241,10 @@ typedef struct hca_attn_desc {
   float*         lse;               /* [Nq, H] or NULL */
   void*          workspace;
   size_t         workspace_bytes;
+  /* optional hipEvent_t pair recorded immediately before and after the attention
+     kernel (the split combine excluded); NULL = none */
+  void*          prof_begin;
+  void*          prof_end;
 } hca_attn_desc;
 
 int         hca_abi_version(void);

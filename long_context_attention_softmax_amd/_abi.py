@@ -56,7 +56,8 @@ class IndexerTopkDesc(ctypes.Structure):
                 ("max_visible", c_int64), ("q", IdxPlanes), ("w", c_void_p), ("keys", IdxPlanes),
                 ("cache_row_start", c_void_p), ("seq_id", c_void_p), ("q_pos", c_void_p),
                 ("idx", c_void_p), ("score", c_void_p),
-                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                ("prof_begin", c_void_p), ("prof_end", c_void_p)]
 
 
 class AttnDesc(ctypes.Structure):
@@ -67,7 +68,8 @@ class AttnDesc(ctypes.Structure):
                 ("q", c_void_p), ("cache", KvPlanes), ("cache_row_start", c_void_p),
                 ("idx", c_void_p), ("win", c_void_p), ("win_pitch", c_int64), ("sink", c_void_p),
                 ("seq_id", c_void_p), ("q_pos", c_void_p), ("o", c_void_p), ("lse", c_void_p),
-                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                ("prof_begin", c_void_p), ("prof_end", c_void_p)]
 
 
 class HcaError(RuntimeError):

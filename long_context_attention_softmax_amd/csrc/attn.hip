@@ -458,19 +458,23 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Nq == 0) return hipSuccess;
   if (a.io_f32) {
+    if (a.prof_begin) hipEventRecord(a.prof_begin, s);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
+    if (a.prof_end) hipEventRecord(a.prof_end, s);
     return hipGetLastError();
   }
   int S, kps;
   split_plan(a.Nq, a.mode, a.k, a.n_win, a.max_visible, a.prefill, &S, &kps);
   const int nw = a.H / 16;
   dim3 grid(S, a.Nq);
+  if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   switch (nw) {
     case 1: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, a, S, kps); break;
     case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, a, S, kps); break;
     case 3: hipLaunchKernelGGL(attn_bf16_kernel<3>, grid, dim3(192), 0, s, a, S, kps); break;
     default: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a, S, kps); break;
   }
+  if (a.prof_end) hipEventRecord(a.prof_end, s);
   if (S > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a, S, kps);
   return hipGetLastError();
 }

@@ -211,6 +211,7 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   a.win = static_cast<const char*>(d->win); a.win_pitch = d->win_pitch;
   a.sink = d->sink; a.seq_id = d->seq_id; a.q_pos = d->q_pos; a.o = d->o; a.lse = d->lse;
   a.workspace = d->workspace; a.prefill = prefill;
+  a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
   return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -311,6 +312,7 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
   size_t sb = (size_t)d->Nq * a.score_pitch * (a.fmt == HCA_F32 ? 8 : 4);
   sb = (sb + 255) / 256 * 256;
   a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(d->workspace) + sb);
+  a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
   return launched(hca::launch_indexer_topk(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -37,6 +37,7 @@ struct IndexerArgs {
   int32_t* idx; void* score_out;
   void* scores;                       // workspace: f32 (quantized) or f64 (F32) [Nq, score_pitch]
   uint32_t* hist;                     // workspace: [Nq, 2048] (quantized only)
+  hipEvent_t prof_begin, prof_end;    // optional, around the scoring kernel
 };
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt);
@@ -57,6 +58,7 @@ struct AttnArgs {
   void* o; float* lse;
   void* workspace;
   int prefill;
+  hipEvent_t prof_begin, prof_end;    // optional, around the attention kernel
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,

@@ -423,10 +423,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   if (a.Nq == 0) return hipSuccess;
   const int64_t chunks_f64 = (a.max_visible + 255) / 256;
   if (a.fmt == HCA_F32) {
+    if (a.prof_begin) hipEventRecord(a.prof_begin, s);
     if (a.max_visible > 0) {
       size_t lds = (size_t)a.H_I * a.d_I * sizeof(float);
       hipLaunchKernelGGL(score_f64_kernel, dim3((unsigned)chunks_f64, a.Nq), dim3(256), lds, s, a);
     }
+    if (a.prof_end) hipEventRecord(a.prof_end, s);
     hipLaunchKernelGGL(select_small_f64_kernel, dim3(a.Nq), dim3(256), 0, s, a);
     return hipGetLastError();
   }
@@ -437,12 +439,14 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
+  if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
     if (a.fmt == HCA_FP8_E4M3)
       hipLaunchKernelGGL(score_quant_kernel<HCA_FP8_E4M3>, dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
     else
       hipLaunchKernelGGL(score_quant_kernel<HCA_MXFP4>, dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
   }
+  if (a.prof_end) hipEventRecord(a.prof_end, s);
   hipLaunchKernelGGL(select_radix_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -97,23 +97,36 @@ class DeviceLayer:
                         raw_idx=self.win_idx if self.mode == A.MODE_CSA else None,
                         out_idx=self.keys if self.mode == A.MODE_CSA else None, debug=debug)
 
-    def select(self, score: Optional[torch.Tensor] = None):
+    def select(self, score: Optional[torch.Tensor] = None, prof=None):
         g = self.g
         return hca_indexer_topk(self.qI, self.w, self.keys, self.cache_row_start, self.seq_id, self.q_pos,
-                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx, score=score)
+                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx, score=score,
+                                prof=prof)
 
-    def attend(self, prefill: bool = False):
+    def attend(self, prefill: bool = False, prof=None):
         g = self.g
         fn = hca_attn_prefill if prefill else hca_attn_decode
         return fn(self.q, self.cache, self.cache_row_start, self.win, self.sink, self.seq_id, self.q_pos,
                   mode=self.mode, m=self.m, n_win=g.n_win, D_r=g.D_r, max_visible=self.max_visible,
                   k=g.topk if self.mode == A.MODE_CSA else 0,
                   idx=self.idx if self.mode == A.MODE_CSA else None, tau=g.tau,
-                  rope_base=g.rope_base, o=self.o, lse=self.lse)
+                  rope_base=g.rope_base, o=self.o, lse=self.lse, prof=prof)
 
-    def step(self, prefill: bool = False, pool: bool = True):
+    def step(self, prefill: bool = False, pool: bool = True, prof_select=None, prof_attend=None):
         if pool:
             self.pool()
         if self.mode == A.MODE_CSA:
-            self.select()
-        return self.attend(prefill)
+            self.select(prof=prof_select)
+        return self.attend(prefill, prof=prof_attend)
+
+    def clone(self) -> "DeviceLayer":
+        """An independent copy of every device buffer (same shapes and contents)."""
+        c = DeviceLayer()
+        for k, v in self.__dict__.items():
+            if isinstance(v, torch.Tensor):
+                v = v.clone()
+            elif isinstance(v, (KVCache, IdxCache)):
+                v = type(v)(**{f: (getattr(v, f).clone() if isinstance(getattr(v, f), torch.Tensor)
+                                   else getattr(v, f)) for f in v.__dataclass_fields__})
+            setattr(c, k, v)
+        return c

@@ -157,7 +157,7 @@ def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch
 def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: torch.Tensor,
                      seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
                      max_visible: int, idx: Optional[torch.Tensor] = None,
-                     score: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     score: Optional[torch.Tensor] = None, prof=None) -> torch.Tensor:
     """Top-k entries per query.  q.data is [Nq, H_I, ...]; returns idx [Nq, k] int32."""
     Nq, H_I = q.data.shape[0], q.data.shape[1]
     d_I = q.data.shape[-1] * (2 if q.fmt == A.MXFP4 else 1)
@@ -182,6 +182,8 @@ def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_sta
     nb = A.workspace_bytes(A.OP_INDEXER_TOPK, d)
     ws = _workspace(A.OP_INDEXER_TOPK, nb, w.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
+    if prof is not None:
+        d.prof_begin, d.prof_end = prof[0].cuda_event, prof[1].cuda_event
     A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
     return idx
 
@@ -190,7 +192,7 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: torch
           win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
           mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
           idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
-          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None) -> torch.Tensor:
     Nq, H, D = q.shape
     _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
     io = A.F32 if q.dtype == torch.float32 else A.BF16
@@ -222,6 +224,8 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: torch
     nb = A.workspace_bytes(op, d)
     ws = _workspace(op, nb, q.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
+    if prof is not None:
+        d.prof_begin, d.prof_end = prof[0].cuda_event, prof[1].cuda_event
     fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
     A.check(fn(ctypes.byref(d), _stream()))
     return o
