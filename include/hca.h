@@ -128,8 +128,9 @@ typedef struct hca_idx_planes {
  * saturate).  `debug`, if not NULL, receives the pre-encoding values as f32
  * [n_blocks, D + d_I] (d_I = 0 without raw_idx).
  *
- * Limits: 1 <= m <= 256, 2 <= D <= 1024, D_r even and 0 <= D_r <= D, d_I <= 256
- * (a multiple of 32 for MXFP4).  raw/raw_idx rows are F32 or BF16 (raw_fmt).
+ * Limits: 1 <= m <= 256, D a multiple of 8 up to 1024, D_r even and <= D, d_I a
+ * multiple of 8 up to 256 (of 32 for MXFP4).  raw/raw_idx rows are F32 or BF16
+ * (raw_fmt) and 16-byte aligned, as is gate_w.
  * Preconditions on device data: every block's rows lie inside the raw buffers and
  * out_row values are distinct rows of the output planes.  Needs no workspace.
  */

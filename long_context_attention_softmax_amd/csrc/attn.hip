@@ -161,11 +161,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-// cos/sin of pos * inv (fp64 angle, reduced to [-pi, pi] in fp64, evaluated in fp32)
-__device__ __forceinline__ void rope_cs(int64_t pos, double inv, float* c, float* s) {
-  double th = (double)pos * inv;
-  th -= kTwoPi * rint(th / kTwoPi);
-  sincosf((float)th, s, c);
+// cos/sin of pos * inv: the angle is formed in fp64 and reduced to a fraction of a
+// turn in [-1/2, 1/2] (exact enough at positions ~1e6), then evaluated by the
+// hardware sine/cosine, whose argument is in turns.  inv_turn = inv / (2 pi).
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv_turn, float* c, float* s) {
+  double turns = (double)pos * inv_turn;
+  turns -= rint(turns);
+  const float f = (float)turns;
+  *s = __builtin_amdgcn_sinf(f);
+  *c = __builtin_amdgcn_cosf(f);
 }
 
 struct PartialPtrs {
@@ -236,19 +240,20 @@ __device__ __forceinline__ void stage_chunk(const AttnArgs& a, const SetInfo& si
         w[v * 4] = x.x; w[v * 4 + 1] = x.y; w[v * 4 + 2] = x.z; w[v * 4 + 3] = x.w;
       }
       if (seg == 7) {   // dims 448..511: rotate pairs (448+i, 480+i) at u
-        float rot[64];
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-          float c, s;
-          rope_cs(u, s_inv[i], &c, &s);
-          const uint16_t h0 = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
-          const uint16_t h1 = (uint16_t)(w[16 + (i >> 1)] >> (16 * (i & 1)));
-          const float x0 = bf16_to_f32(h0), x1 = bf16_to_f32(h1);
-          rot[i] = x0 * c - x1 * s;
-          rot[32 + i] = x0 * s + x1 * c;
+        uint32_t rw[32];
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) {        // pairs i = 2*i2, 2*i2+1 share words
+          float c0, s0, c1, s1;
+          rope_cs(u, s_inv[2 * i2], &c0, &s0);
+          rope_cs(u, s_inv[2 * i2 + 1], &c1, &s1);
+          const uint32_t lo = w[i2], hi = w[16 + i2];
+          const float a0 = bf16_to_f32((uint16_t)lo), a1 = bf16_to_f32((uint16_t)(lo >> 16));
+          const float b0 = bf16_to_f32((uint16_t)hi), b1 = bf16_to_f32((uint16_t)(hi >> 16));
+          rw[i2] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+          rw[16 + i2] = pack_bf16x2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
         }
 #pragma unroll
-        for (int i = 0; i < 32; ++i) w[i] = pack_bf16x2(rot[2 * i], rot[2 * i + 1]);
+        for (int i = 0; i < 32; ++i) w[i] = rw[i];
       }
     }
     uint4* dst = reinterpret_cast<uint4*>(Ks + kk * kKsPitch + seg * 64);
@@ -273,7 +278,7 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
   const int p_end = min(n_set, p_beg + keys_per_split);
   const int b = a.seq_id[n];
   const int64_t t = a.q_pos[n];
-  if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr);
+  if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr) / kTwoPi;   // turns per position
   __syncthreads();
 
   // Q operands: lane (r, g) of wave w holds head 16w + r, dims 32s + 8g .. +7

@@ -55,7 +55,7 @@ int validate_kv_compress(const hca_kv_compress_desc* d) {
   REQUIRE(d->struct_size == sizeof(hca_kv_compress_desc), HCA_E_VERSION,
           "struct_size %u != %zu", d->struct_size, sizeof(hca_kv_compress_desc));
   REQUIRE(d->m >= 1 && d->m <= 256, HCA_E_SHAPE, "m=%d outside [1, 256]", d->m);
-  REQUIRE(d->D >= 2 && d->D <= 1024, HCA_E_SHAPE, "D=%d outside [2, 1024]", d->D);
+  REQUIRE(d->D >= 8 && d->D <= 1024 && d->D % 8 == 0, HCA_E_SHAPE, "D=%d must be a multiple of 8 in [8, 1024]", d->D);
   REQUIRE(d->D_r >= 0 && d->D_r <= d->D && d->D_r % 2 == 0, HCA_E_SHAPE, "D_r=%d must be even, <= D", d->D_r);
   REQUIRE(d->n_blocks >= 0, HCA_E_SHAPE, "n_blocks=%d < 0", d->n_blocks);
   REQUIRE(d->raw_fmt == HCA_F32 || d->raw_fmt == HCA_BF16, HCA_E_DTYPE, "raw_fmt %d not F32/BF16", d->raw_fmt);
@@ -65,15 +65,15 @@ int validate_kv_compress(const hca_kv_compress_desc* d) {
           HCA_E_NULL, "raw, block_row, block_pos, out_row, gate_w and gate_b are required");
   const int eb = elem_bytes(d->raw_fmt);
   REQUIRE(d->raw_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE, "raw_pitch too small");
-  REQUIRE(aligned(d->raw, eb) && d->raw_pitch % eb == 0, HCA_E_ALIGN, "raw misaligned");
-  REQUIRE(aligned(d->gate_w, 4) && aligned(d->gate_b, 4) && aligned(d->block_row, 8) &&
+  REQUIRE(aligned(d->raw, 16) && d->raw_pitch % 16 == 0, HCA_E_ALIGN, "raw rows must be 16-byte aligned");
+  REQUIRE(aligned(d->gate_w, 16) && aligned(d->gate_b, 4) && aligned(d->block_row, 8) &&
           aligned(d->block_pos, 8) && aligned(d->out_row, 8), HCA_E_ALIGN, "gate or block arrays misaligned");
   int rc = check_kv_planes(d->out, d->D, d->D_r, "out", true);
   if (rc) return rc;
   if (d->raw_idx) {
-    REQUIRE(d->d_I >= 1 && d->d_I <= 256, HCA_E_SHAPE, "d_I=%d outside [1, 256]", d->d_I);
-    REQUIRE(d->raw_idx_pitch >= (int64_t)eb * d->d_I && aligned(d->raw_idx, eb) && d->raw_idx_pitch % eb == 0,
-            HCA_E_SHAPE, "raw_idx pitch/alignment");
+    REQUIRE(d->d_I >= 8 && d->d_I <= 256 && d->d_I % 8 == 0, HCA_E_SHAPE, "d_I=%d must be a multiple of 8 in [8, 256]", d->d_I);
+    REQUIRE(d->raw_idx_pitch >= (int64_t)eb * d->d_I, HCA_E_SHAPE, "raw_idx pitch too small");
+    REQUIRE(aligned(d->raw_idx, 16) && d->raw_idx_pitch % 16 == 0, HCA_E_ALIGN, "raw_idx rows must be 16-byte aligned");
     const hca_idx_planes& o = d->out_idx;
     REQUIRE(o.data, HCA_E_NULL, "out_idx.data is NULL");
     if (o.fmt == HCA_F32) {
@@ -109,6 +109,7 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
   } else {
     REQUIRE(d->d_I == 128, HCA_E_UNSUPPORTED, "quantized indexer needs d_I = 128 (got %d)", d->d_I);
     REQUIRE(d->H_I % 16 == 0 && d->H_I <= 64, HCA_E_UNSUPPORTED, "quantized indexer needs H_I in {16,32,48,64}");
+    REQUIRE(d->max_visible <= 2048LL * 4096, HCA_E_UNSUPPORTED, "quantized indexer supports at most 2^23 visible entries");
   }
   *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt);
   if (d->Nq == 0) return HCA_OK;
@@ -308,10 +309,8 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
   a.key_scales = static_cast<const uint8_t*>(d->keys.scales); a.key_scale_pitch = d->keys.scale_pitch;
   a.cache_row_start = d->cache_row_start; a.seq_id = d->seq_id; a.q_pos = d->q_pos;
   a.idx = d->idx; a.score_out = d->score;
-  a.scores = d->workspace;
-  size_t sb = (size_t)d->Nq * a.score_pitch * (a.fmt == HCA_F32 ? 8 : 4);
-  sb = (sb + 255) / 256 * 256;
-  a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(d->workspace) + sb);
+  a.scores = d->workspace;             // the workspace layout is laid out by the launcher
+  a.hist = nullptr;
   a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
   return launched(hca::launch_indexer_topk(a, static_cast<hipStream_t>(stream)));
 }

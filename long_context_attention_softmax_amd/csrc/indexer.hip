@@ -30,11 +30,9 @@ namespace hca {
 
 namespace {
 
-constexpr int kScoreThreads = 256;        // 4 waves x 64 entries
-constexpr int kEntriesPerWG = 256;
+constexpr int kScoreThreads = 256;        // 4 waves
 constexpr int kBins = 2048;               // first radix digit: key bits 31..21
 constexpr int kSelectThreads = 1024;
-constexpr int kCandCap = 4096;
 constexpr int kSmallV = 4096;
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -127,8 +125,12 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 }
 
 // -------------------------------------------------------- quantized operands
-// One workgroup scores 256 consecutive entries of one query: each wave takes 64
-// entries as four 16-entry MFMA tiles; rows of the MFMA are indexer heads.
+constexpr int kTilesPerWave = 8;                         // 8 x 16 entries per wave
+constexpr int kEntriesPerWG2 = 4 * 16 * kTilesPerWave;   // 512
+
+// One workgroup scores 512 consecutive entries of one query; each wave owns 128
+// entries (eight 16-entry MFMA tiles) and issues all their key loads before the
+// first MFMA.  Rows of the MFMA are indexer heads, columns entries.
 template <int FMT>
 __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
@@ -137,17 +139,39 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
   const int r = lane & 15, g = lane >> 4;
   const int n = blockIdx.y;
   const int64_t V = visible(a, n);
-  const int64_t ebase = (int64_t)blockIdx.x * kEntriesPerWG;
+  const int64_t ebase = (int64_t)blockIdx.x * kEntriesPerWG2;
   if (ebase >= V) return;                               // uniform over the workgroup
+  const int64_t row0 = a.cache_row_start[a.seq_id[n]];
+  const int64_t wbase = ebase + wave * 16 * kTilesPerWave;
+
+  // key loads for all tiles of this wave first (lane (r, g): entry r, bytes of group g)
+  uint4 kr0[kTilesPerWave], kr1[kTilesPerWave];
+  int ks[kTilesPerWave];
+#pragma unroll
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    const int64_t j = wbase + 16 * t + r;
+    kr0[t] = make_uint4(0, 0, 0, 0);
+    kr1[t] = make_uint4(0, 0, 0, 0);
+    ks[t] = 127;
+    if (j < V) {
+      if (FMT == HCA_FP8_E4M3) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 32 * g);
+        kr0[t] = p[0];
+        kr1[t] = p[1];
+      } else {
+        kr0[t] = *reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 16 * g);
+        ks[t] = a.key_scales[(row0 + j) * a.key_scale_pitch + g];
+      }
+    }
+  }
   for (int i = tid; i < kBins; i += kScoreThreads) s_hist[i] = 0;
 
   const int HT = a.H_I / 16;                            // head tiles (<= 4)
-  const int64_t row0 = a.cache_row_start[a.seq_id[n]];
-  // A operands: query head rows; lane (r, g) holds head 16T + r
   v8bf qa[4][4];
   v8i qf4[4];
   int qs[4];
   float wv[4][4];
+#pragma unroll
   for (int T = 0; T < 4; ++T) {
     if (T < HT) {
       const int64_t qr = (int64_t)n * a.H_I + 16 * T + r;
@@ -164,61 +188,56 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
         qf4[T] = v;
         qs[T] = a.q_scales[qr * a.q_scale_pitch + g];
       }
+#pragma unroll
       for (int i = 0; i < 4; ++i) wv[T][i] = a.w[(int64_t)n * a.H_I + 16 * T + 4 * g + i];
     }
   }
   __syncthreads();
 
-  for (int tile = 0; tile < 4; ++tile) {
-    const int64_t j = ebase + wave * 64 + tile * 16 + r;
-    const bool valid = j < V;
+  float* sc = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
+#pragma unroll
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    const int64_t j = wbase + 16 * t + r;
     v4f acc[4];
     if (FMT == HCA_FP8_E4M3) {
-      uint4 u0 = {0, 0, 0, 0}, u1 = {0, 0, 0, 0};
-      if (valid) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 32 * g);
-        u0 = p[0];
-        u1 = p[1];
-      }
-      v8bf kb[4] = {fp8x8_to_bf16(u0.x, u0.y), fp8x8_to_bf16(u0.z, u0.w),
-                    fp8x8_to_bf16(u1.x, u1.y), fp8x8_to_bf16(u1.z, u1.w)};
+      v8bf kb[4] = {fp8x8_to_bf16(kr0[t].x, kr0[t].y), fp8x8_to_bf16(kr0[t].z, kr0[t].w),
+                    fp8x8_to_bf16(kr1[t].x, kr1[t].y), fp8x8_to_bf16(kr1[t].z, kr1[t].w)};
+#pragma unroll
       for (int T = 0; T < 4; ++T) {
         if (T < HT) {
           v4f c = {0.f, 0.f, 0.f, 0.f};
-          for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s], kb[s], c, 0, 0, 0);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s2], kb[s2], c, 0, 0, 0);
           acc[T] = c;
         }
       }
     } else {
-      uint4 u = {0, 0, 0, 0};
-      int ks = 127;
-      if (valid) {
-        u = *reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 16 * g);
-        ks = a.key_scales[(row0 + j) * a.key_scale_pitch + g];
-      }
-      v8i kv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+      v8i kv = {(int)kr0[t].x, (int)kr0[t].y, (int)kr0[t].z, (int)kr0[t].w, 0, 0, 0, 0};
+#pragma unroll
       for (int T = 0; T < 4; ++T) {
         if (T < HT) {
           v4f c = {0.f, 0.f, 0.f, 0.f};
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf4[T], kv, c, 4, 4, 0, qs[T], 0, ks);
+          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf4[T], kv, c, 4, 4, 0, qs[T], 0, ks[t]);
         }
       }
     }
     // canonical head sum
     float S = 0.0f;
+#pragma unroll
     for (int T = 0; T < 4; ++T) {
       if (T < HT) {
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float d = acc[T][i];
-          float t = wv[T][i] * (d > 0.0f ? d : 0.0f);
-          S = S + t;
+          const float d = acc[T][i];
+          const float term = wv[T][i] * (d > 0.0f ? d : 0.0f);
+          S = S + term;
         }
       }
     }
     S = S + __shfl_xor(S, 16, 64);
     S = S + __shfl_xor(S, 32, 64);
-    if (g == 0 && valid) {
-      reinterpret_cast<float*>(a.scores)[(int64_t)n * a.score_pitch + j] = S;
+    if (g == 0 && j < V) {
+      sc[j] = S;
       atomicAdd(&s_hist[float_key(S) >> 21], 1u);
     }
   }
@@ -236,8 +255,33 @@ __global__ void __launch_bounds__(256) zero_kernel(uint4* p, int64_t n16) {
 }
 
 // ------------------------------------------------------------------- select
-// Exclusive scan over the 1024 threads of a workgroup (scan order = thread order).
+// Top-k in three parallel phases over the materialized scores.  The first radix
+// digit (key bits 31..21) was histogrammed by the scoring kernel.
+//   collect:   every 4096-entry chunk counts its keys above the threshold digit d1
+//              and appends those in d1 (the candidates) to a per-query list;
+//   threshold: one workgroup per query resolves digits 2 and 3 on the candidates,
+//              giving the exact k-th key T and how many keys equal to T to keep
+//              (the lowest indices), and turns per-chunk counts into output offsets;
+//   emit:      every chunk writes its selected indices, ascending, at its offset.
+constexpr int kChunk1 = 4096;
+constexpr int kCandCap2 = 8192;
+constexpr int kMaxChunks = 2048;
+
+struct SelectWs {
+  uint32_t* cand_count;   // [Nq] (cleared with the histogram)
+  uint32_t* cand_key;     // [Nq, kCandCap2]
+  int32_t* cand_idx;      // [Nq, kCandCap2]
+  uint32_t* chunk_gt;     // [Nq, nch]
+  uint32_t* out_off;      // [Nq, nch]
+  uint32_t* eq_before;    // [Nq, nch]
+  uint32_t* state;        // [Nq, 2]: threshold key, number of equal keys kept
+  int nch;
+};
+
+// Exclusive scan over the threads of a workgroup of NT threads (order = thread id).
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+  constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -248,174 +292,270 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    uint32_t t = lane < kSelectThreads / 64 ? s_wave[lane] : 0;
+    uint32_t t = lane < NWV ? s_wave[lane] : 0;
     uint32_t u = t;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       uint32_t y = __shfl_up(u, o, 64);
       if (lane >= o) u += y;
     }
-    if (lane < kSelectThreads / 64) s_wave[lane] = u - t;   // exclusive wave offsets
-    if (lane == kSelectThreads / 64 - 1) s_wave[kSelectThreads / 64] = u;
+    if (lane < NWV) s_wave[lane] = u - t;
+    if (lane == NWV - 1) s_wave[NWV] = u;
   }
   __syncthreads();
-  uint32_t r = s_wave[wave] + x - v;
-  *total = s_wave[kSelectThreads / 64];
+  uint32_t res = s_wave[wave] + x - v;
+  *total = s_wave[NWV];
   __syncthreads();
-  return r;
+  return res;
 }
 
-// Given a histogram (counts per digit, digits ordered by key), find the digit that
-// holds the need-th largest key.  Returns the digit and sets *need to the rank
-// still needed inside it.
+// The digit holding the need-th largest key of a histogram (digits ordered by key);
+// *need becomes the rank still needed inside that digit.
+template <int NT>
 __device__ int find_digit(const uint32_t* hist, int nbins, uint32_t* need, uint32_t* s_wave,
                           int* s_found, uint32_t* s_need) {
   const int tid = threadIdx.x;
   if (tid == 0) { *s_found = 0; *s_need = 1; }
-  // thread t covers digits [per*t', per*t'+per) counted from the top
-  const int per = nbins / kSelectThreads;           // 2 (2048 bins) or 1 (1024 bins)
-  const int top = nbins - 1 - tid * per;            // highest digit of this thread
+  const int per = nbins / NT;
+  const int top = nbins - 1 - tid * per;
   uint32_t c = 0;
   for (int q = 0; q < per; ++q) c += hist[top - q];
   uint32_t tot;
-  uint32_t above = block_exclusive_scan(c, s_wave, &tot);
+  uint32_t above = block_exclusive_scan<NT>(c, s_wave, &tot);
   const uint32_t nd = *need;
   for (int q = 0; q < per; ++q) {
-    uint32_t h = hist[top - q];
-    if (above < nd && nd <= above + h) {
-      *s_found = top - q;
-      *s_need = nd - above;
-    }
+    const uint32_t h = hist[top - q];
+    if (above < nd && nd <= above + h) { *s_found = top - q; *s_need = nd - above; }
     above += h;
   }
   __syncthreads();
   *need = *s_need;
-  int d = *s_found;
+  const int d = *s_found;
   __syncthreads();
   return d;
 }
 
-__global__ void __launch_bounds__(kSelectThreads) select_radix_kernel(IndexerArgs a) {
+__global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
   __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_ck[kCandCap];
-  __shared__ int32_t s_cj[kCandCap];
+  __shared__ uint32_t s_wave[256 / 64 + 1];
+  __shared__ int s_found;
+  __shared__ uint32_t s_need;
+  const int n = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int64_t V = visible(a, n);
+  const int64_t K = V < a.k ? V : a.k;
+  const int64_t j0 = (int64_t)c * kChunk1;
+  if (V <= K || j0 >= V) return;
+  const uint32_t* gh = a.hist + (int64_t)n * kBins;
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
+  __syncthreads();
+  uint32_t need = (uint32_t)K;
+  const uint32_t d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
+  uint32_t gt = 0;
+  for (int64_t j = j0 + tid; j < j1; j += 256) {
+    const uint32_t key = float_key(sc[j]);
+    const uint32_t dg = key >> 21;
+    gt += dg > d1;
+    if (dg == d1) {
+      const uint32_t p = atomicAdd(&ws.cand_count[n], 1u);
+      if (p < (uint32_t)kCandCap2) {
+        ws.cand_key[(int64_t)n * kCandCap2 + p] = key;
+        ws.cand_idx[(int64_t)n * kCandCap2 + p] = (int32_t)j;
+      }
+    }
+  }
+  uint32_t tot;
+  block_exclusive_scan<256>(gt, s_wave, &tot);
+  if (tid == 0) ws.chunk_gt[(int64_t)n * ws.nch + c] = tot;
+}
+
+__global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(IndexerArgs a, SelectWs ws) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_ck[kCandCap2];
+  __shared__ int32_t s_cj[kCandCap2];
+  __shared__ uint32_t s_selc[kMaxChunks];
+  __shared__ uint32_t s_eqc[kMaxChunks];
   __shared__ uint32_t s_wave[kSelectThreads / 64 + 1];
   __shared__ int s_found;
-  __shared__ uint32_t s_need, s_ncand;
-  const int tid = threadIdx.x;
-  const int n = blockIdx.x;
+  __shared__ uint32_t s_need;
+  const int n = blockIdx.x, tid = threadIdx.x;
   const int64_t V = visible(a, n);
-  const uint32_t K = (uint32_t)(V < a.k ? V : a.k);
-  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
-  float* so = reinterpret_cast<float*>(a.score_out);
-  int32_t* out = a.idx + (int64_t)n * a.k;
-  uint32_t* gh = a.hist + (int64_t)n * kBins;
-
-  for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = gh[i];
-  __syncthreads();
-
-  uint32_t T = 0, take_eq = 0;          // threshold key and how many keys == T to keep
-  if ((int64_t)K < V) {
-    uint32_t need = K;
-    const int d1 = find_digit(s_hist, kBins, &need, s_wave, &s_found, &s_need);
-    uint32_t prefix = (uint32_t)d1;
-    const uint32_t n1 = s_hist[d1];
-    const bool in_lds = n1 <= (uint32_t)kCandCap;
-    if (in_lds) {
-      if (tid == 0) s_ncand = 0;
-      __syncthreads();
-      for (int64_t j = tid; j < V; j += kSelectThreads) {
-        uint32_t key = float_key(sc[j]);
-        if ((key >> 21) == prefix) {
-          uint32_t p = atomicAdd(&s_ncand, 1u);
-          if (p < (uint32_t)kCandCap) {
-            s_ck[p] = key;
-            s_cj[p] = (int32_t)j;
-          }
-        }
-      }
-      __syncthreads();
-    }
-    // digits 2 (bits 20..10) and 3 (bits 9..0)
-    for (int round = 0; round < 2; ++round) {
-      const int shift = round == 0 ? 10 : 0;
-      const int nbits = round == 0 ? 11 : 10;
-      const int nb = 1 << nbits;
-      for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = 0;
-      __syncthreads();
-      if (in_lds) {
-        for (uint32_t c = tid; c < n1; c += kSelectThreads) {
-          uint32_t key = s_ck[c];
-          if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
-        }
-      } else {
-        for (int64_t j = tid; j < V; j += kSelectThreads) {
-          uint32_t key = float_key(sc[j]);
-          if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
-        }
-      }
-      __syncthreads();
-      const int dd = find_digit(s_hist, nb < 1024 ? 1024 : nb, &need, s_wave, &s_found, &s_need);
-      prefix = (prefix << nbits) | (uint32_t)dd;
-    }
-    T = prefix;
-    take_eq = need;
-  } else {
-    T = 0;              // every visible entry is kept
-    take_eq = 0xFFFFFFFFu;
+  const int64_t K = V < a.k ? V : a.k;
+  if (V <= K) {
+    if (tid == 0) { ws.state[2 * n] = 0; ws.state[2 * n + 1] = 0xFFFFFFFFu; }
+    return;
   }
+  const int nch = (int)((V + kChunk1 - 1) / kChunk1);
+  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  const uint32_t* gh = a.hist + (int64_t)n * kBins;
+  for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = gh[i];
+  for (int i = tid; i < nch; i += kSelectThreads) { s_selc[i] = 0; s_eqc[i] = 0; }
+  __syncthreads();
+  uint32_t need = (uint32_t)K;
+  const uint32_t d1 = (uint32_t)find_digit<kSelectThreads>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+  const uint32_t n1 = ws.cand_count[n];
+  const bool in_lds = n1 <= (uint32_t)kCandCap2;
+  if (in_lds) {
+    for (uint32_t i = tid; i < n1; i += kSelectThreads) {
+      s_ck[i] = ws.cand_key[(int64_t)n * kCandCap2 + i];
+      s_cj[i] = ws.cand_idx[(int64_t)n * kCandCap2 + i];
+    }
+  }
+  __syncthreads();
+  uint32_t prefix = d1;
+  for (int round = 0; round < 2; ++round) {
+    const int shift = round == 0 ? 10 : 0;
+    const int nbits = round == 0 ? 11 : 10;
+    const int nb = 1 << nbits;
+    for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = 0;
+    __syncthreads();
+    if (in_lds) {
+      for (uint32_t i = tid; i < n1; i += kSelectThreads) {
+        const uint32_t key = s_ck[i];
+        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
+      }
+    } else {
+      for (int64_t j = tid; j < V; j += kSelectThreads) {
+        const uint32_t key = float_key(sc[j]);
+        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    const int dd = find_digit<kSelectThreads>(s_hist, nb, &need, s_wave, &s_found, &s_need);
+    prefix = (prefix << nbits) | (uint32_t)dd;
+  }
+  const uint32_t T = prefix, take_eq = need;
+  // per-chunk counts of the candidates above T and equal to T
+  if (in_lds) {
+    for (uint32_t i = tid; i < n1; i += kSelectThreads) {
+      const uint32_t key = s_ck[i];
+      const int ch = s_cj[i] / kChunk1;
+      if (key > T) atomicAdd(&s_selc[ch], 1u);
+      else if (key == T) atomicAdd(&s_eqc[ch], 1u);
+    }
+  } else {
+    for (int64_t j = tid; j < V; j += kSelectThreads) {
+      const uint32_t key = float_key(sc[j]);
+      if ((key >> 21) != d1) continue;
+      const int ch = (int)(j / kChunk1);
+      if (key > T) atomicAdd(&s_selc[ch], 1u);
+      else if (key == T) atomicAdd(&s_eqc[ch], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t off = 0, eqb = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      ws.out_off[(int64_t)n * ws.nch + ch] = off;
+      ws.eq_before[(int64_t)n * ws.nch + ch] = eqb;
+      const uint32_t eq_keep = eqb >= take_eq ? 0 : (s_eqc[ch] < take_eq - eqb ? s_eqc[ch] : take_eq - eqb);
+      off += ws.chunk_gt[(int64_t)n * ws.nch + ch] + s_selc[ch] + eq_keep;
+      eqb += s_eqc[ch];
+    }
+    ws.state[2 * n] = T;
+    ws.state[2 * n + 1] = take_eq;
+  }
+}
 
-  // ordered output pass: tiles of 4 consecutive entries per thread
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int64_t base = 0; base < V; base += 4 * kSelectThreads) {
-    const int64_t j0 = base + 4 * (int64_t)tid;
+__global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectWs ws) {
+  __shared__ uint32_t s_wave[256 / 64 + 1];
+  const int n = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int64_t V = visible(a, n);
+  const int64_t K = V < a.k ? V : a.k;
+  const int64_t j0 = (int64_t)c * kChunk1;
+  int32_t* out = a.idx + (int64_t)n * a.k;
+  float* so = reinterpret_cast<float*>(a.score_out);
+  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  if (V <= K) {                     // every visible entry is kept, at its own position
+    for (int64_t j = j0 + tid; j < V && j < j0 + kChunk1; j += 256) {
+      out[j] = (int32_t)j;
+      if (so) so[(int64_t)n * a.k + j] = sc[j];
+    }
+    if (c == 0)
+      for (int64_t p = V + tid; p < a.k; p += 256) {
+        out[p] = -1;
+        if (so) so[(int64_t)n * a.k + p] = 0.0f;
+      }
+    return;
+  }
+  if (j0 >= V) return;
+  const uint32_t T = ws.state[2 * n], take_eq = ws.state[2 * n + 1];
+  uint32_t pos_base = ws.out_off[(int64_t)n * ws.nch + c];
+  uint32_t eqb = ws.eq_before[(int64_t)n * ws.nch + c];
+  const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
+  uint32_t run_sel = 0;
+  for (int64_t base = j0; base < j1; base += 4 * 256) {
+    const int64_t jt = base + 4 * (int64_t)tid;
     uint32_t kk[4];
-    int ngt = 0, neq = 0;
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-      int64_t j = j0 + e;
       kk[e] = 0;
-      if (j < V) {
-        kk[e] = float_key(sc[j]);
-        if ((int64_t)K >= V) { ngt++; }
-        else if (kk[e] > T) ngt++;
-        else if (kk[e] == T) neq++;
+      if (jt + e < j1) {
+        kk[e] = float_key(sc[jt + e]);
+        ngt += kk[e] > T;
+        neq += kk[e] == T;
       }
     }
     uint32_t tot;
-    const uint32_t pre = block_exclusive_scan((uint32_t)ngt | ((uint32_t)neq << 16), s_wave, &tot);
-    uint32_t gt_before = run_gt + (pre & 0xFFFF);
-    uint32_t eq_before = run_eq + (pre >> 16);
+    const uint32_t pre = block_exclusive_scan<256>(ngt | (neq << 16), s_wave, &tot);
+    uint32_t gt_before = pre & 0xFFFF;
+    uint32_t eq_before = eqb + (pre >> 16);
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-      int64_t j = j0 + e;
-      if (j >= V) break;
-      bool is_gt = ((int64_t)K >= V) || kk[e] > T;
-      bool is_eq = !is_gt && kk[e] == T;
+      if (jt + e >= j1) break;
+      const bool is_gt = kk[e] > T, is_eq = kk[e] == T;
+      const uint32_t eq_sel_before = (eq_before < take_eq ? eq_before : take_eq) - (eqb < take_eq ? eqb : take_eq);
       if (is_gt || (is_eq && eq_before < take_eq)) {
-        uint32_t pos = gt_before + (eq_before < take_eq ? eq_before : take_eq);
-        if (pos >= K) continue;      // only reachable with inconsistent counts
-        out[pos] = (int32_t)j;
-        if (so) so[(int64_t)n * a.k + pos] = sc[j];
+        const uint32_t pos = pos_base + run_sel + gt_before + eq_sel_before;
+        if (pos < (uint32_t)K) {
+          out[pos] = (int32_t)(jt + e);
+          if (so) so[(int64_t)n * a.k + pos] = sc[jt + e];
+        }
       }
-      if (is_gt) gt_before++;
-      if (is_eq) eq_before++;
+      gt_before += is_gt;
+      eq_before += is_eq;
     }
-    run_gt += tot & 0xFFFF;
-    run_eq += tot >> 16;
-  }
-  for (int p = (int)K + tid; p < a.k; p += kSelectThreads) {
-    out[p] = -1;
-    if (so) so[(int64_t)n * a.k + p] = 0.0f;
+    // selected in this tile: all above T plus the kept equal keys
+    const uint32_t tile_eq_end = eqb + (tot >> 16);
+    const uint32_t kept_eq = (tile_eq_end < take_eq ? tile_eq_end : take_eq) - (eqb < take_eq ? eqb : take_eq);
+    run_sel += (tot & 0xFFFF) + kept_eq;
+    eqb = tile_eq_end;
   }
 }
 
 }  // namespace
 
-size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt) {
+namespace {
+struct WsLayout {
+  size_t scores, hist, cand_key, cand_idx, chunk_gt, out_off, eq_before, state, total;
+  int nch;
+};
+WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  WsLayout L{};
   const int64_t pitch = (max_visible + 63) / 64 * 64;
-  size_t b = (size_t)Nq * pitch * (fmt == HCA_F32 ? 8 : 4);
-  b = (b + 255) / 256 * 256;
-  if (fmt != HCA_F32) b += (size_t)Nq * kBins * 4;
-  return b;
+  L.scores = 0;
+  size_t o = up((size_t)Nq * pitch * (fmt == HCA_F32 ? 8 : 4));
+  L.total = o;
+  if (fmt == HCA_F32) return L;
+  L.nch = (int)((max_visible + kChunk1 - 1) / kChunk1);
+  if (L.nch < 1) L.nch = 1;
+  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 1) * 4);        // histogram + candidate count
+  L.cand_key = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
+  L.cand_idx = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
+  L.chunk_gt = o; o = up(o + (size_t)Nq * L.nch * 4);
+  L.out_off = o; o = up(o + (size_t)Nq * L.nch * 4);
+  L.eq_before = o; o = up(o + (size_t)Nq * L.nch * 4);
+  L.state = o; o = up(o + (size_t)Nq * 2 * 4);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt) {
+  return ws_layout(Nq, max_visible, fmt).total;
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
@@ -432,13 +572,26 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(select_small_f64_kernel, dim3(a.Nq), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const int64_t chunks = (a.max_visible + kEntriesPerWG - 1) / kEntriesPerWG;
+  const WsLayout L = ws_layout(a.Nq, a.max_visible, a.fmt);
+  char* wsb = static_cast<char*>(a.scores);
+  a.hist = reinterpret_cast<uint32_t*>(wsb + L.hist);
+  SelectWs sw;
+  sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
+  sw.cand_key = reinterpret_cast<uint32_t*>(wsb + L.cand_key);
+  sw.cand_idx = reinterpret_cast<int32_t*>(wsb + L.cand_idx);
+  sw.chunk_gt = reinterpret_cast<uint32_t*>(wsb + L.chunk_gt);
+  sw.out_off = reinterpret_cast<uint32_t*>(wsb + L.out_off);
+  sw.eq_before = reinterpret_cast<uint32_t*>(wsb + L.eq_before);
+  sw.state = reinterpret_cast<uint32_t*>(wsb + L.state);
+  sw.nch = L.nch;
   {
-    // the first radix digit is histogrammed by the scoring kernel: clear it first
-    const int64_t n16 = (int64_t)a.Nq * kBins * 4 / 16;
+    // the scoring kernel histograms the first digit and the collect phase counts
+    // candidates: clear both first (they are adjacent)
+    const int64_t n16 = ((int64_t)a.Nq * (kBins + 1) * 4 + 15) / 16;
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
+  const int64_t chunks = (a.max_visible + kEntriesPerWG2 - 1) / kEntriesPerWG2;
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
     if (a.fmt == HCA_FP8_E4M3)
@@ -447,7 +600,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
       hipLaunchKernelGGL(score_quant_kernel<HCA_MXFP4>, dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
-  hipLaunchKernelGGL(select_radix_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a);
+  dim3 cgrid((unsigned)L.nch, a.Nq);
+  hipLaunchKernelGGL(select_collect_kernel, cgrid, dim3(256), 0, s, a, sw);
+  hipLaunchKernelGGL(select_threshold_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a, sw);
+  hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
   return hipGetLastError();
 }
 

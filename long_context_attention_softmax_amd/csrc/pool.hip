@@ -20,16 +20,56 @@ namespace {
 constexpr int kPoolThreads = 256;
 constexpr int kMaxM = 256, kMaxD = 1024, kMaxDI = 256;
 
-__device__ __forceinline__ double load_raw(const char* base, int64_t pitch, int64_t row, int d, int is_f32) {
+// 8 consecutive raw elements [8g, 8g+8) of row `row` as fp64 (BF16 or f32 storage)
+__device__ __forceinline__ void load8(const char* base, int64_t pitch, int64_t row, int g, int is_f32,
+                                      double out[8]) {
   const char* p = base + row * pitch;
-  if (is_f32) return (double)reinterpret_cast<const float*>(p)[d];
-  return (double)bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[d]);
+  if (is_f32) {
+    const float4* q = reinterpret_cast<const float4*>(p) + 2 * g;
+    float4 a = q[0], b = q[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    uint4 u = reinterpret_cast<const uint4*>(p)[g];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = (double)bf16_to_f32((uint16_t)w[i]);
+      out[2 * i + 1] = (double)bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  }
+}
+
+// Partial weighted sums of one wave over the tokens i = wave, wave+4, ... of the block,
+// four tokens in flight at a time; lane handles 8-element groups g = lane, lane+64, ...
+__device__ __forceinline__ void pool_partial(const char* base, int64_t pitch, int64_t r0, int m, int ngroups,
+                                             int is_f32, const double* alpha, double* part, int wave, int lane) {
+  for (int g = lane; g < ngroups; g += 64) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i0 = wave; i0 < m; i0 += 16) {
+      double x[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i0 + 4 * j < m) load8(base, pitch, r0 + i0 + 4 * j, g, is_f32, x[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i0 + 4 * j < m) {
+          const double al = alpha[i0 + 4 * j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += al * x[j][e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[8 * g + e] = acc[e];
+  }
 }
 
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   __shared__ double s_z[kMaxM];
   __shared__ double s_c[kMaxD];
   __shared__ double s_y[kMaxDI];
+  __shared__ double s_part[4][kMaxD];
+  __shared__ double s_party[4][kMaxDI];
   __shared__ double s_red[kPoolThreads / 64];
   __shared__ double s_bamax[kMaxDI / 32];
 
@@ -40,14 +80,31 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   const int64_t orow = a.out_row[nb];
   const char* raw = static_cast<const char*>(a.raw);
   const char* raw_idx = static_cast<const char*>(a.raw_idx);
+  const int ng = a.D / 8, ngi = a.d_I / 8;
 
-  // gate logits z_i = g . x_i + b_i : one wave per token, lanes over dims
-  for (int i = wave; i < a.m; i += kPoolThreads / 64) {
-    double acc = 0.0;
-    for (int d = lane; d < a.D; d += 64)
-      acc += (double)a.gate_w[d] * load_raw(raw, a.raw_pitch, r0 + i, d, a.raw_is_f32);
-    acc = wave_sum(acc);
-    if (lane == 0) s_z[i] = acc + (double)a.gate_b[i];
+  // gate logits z_i = g . x_i + b_i : wave w takes tokens w, w+4, ...; four at a time
+  for (int i0 = wave; i0 < a.m; i0 += 16) {
+    double acc[4] = {0, 0, 0, 0};
+    for (int g = lane; g < ng; g += 64) {
+      const float4* gw4 = reinterpret_cast<const float4*>(a.gate_w) + 2 * g;
+      const float4 ga = gw4[0], gb = gw4[1];
+      const double gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      double x[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i0 + 4 * j < a.m) load8(raw, a.raw_pitch, r0 + i0 + 4 * j, g, a.raw_is_f32, x[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i0 + 4 * j < a.m) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j] += gw[e] * x[j][e];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double z = wave_sum(acc[j]);
+      if (lane == 0 && i0 + 4 * j < a.m) s_z[i0 + 4 * j] = z + (double)a.gate_b[i0 + 4 * j];
+    }
   }
   __syncthreads();
   // softmax over the block (wave 0)
@@ -61,19 +118,16 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
     for (int i = lane; i < a.m; i += 64) s_z[i] = s_z[i] / sum;
   }
   __syncthreads();
-  // weighted sums, sequential over the block's tokens
-  for (int d = tid; d < a.D; d += kPoolThreads) {
-    double c = 0.0;
-    for (int i = 0; i < a.m; ++i) c += s_z[i] * load_raw(raw, a.raw_pitch, r0 + i, d, a.raw_is_f32);
-    s_c[d] = c;
-  }
-  if (a.idx_fmt >= 0) {
-    for (int d = tid; d < a.d_I; d += kPoolThreads) {
-      double y = 0.0;
-      for (int i = 0; i < a.m; ++i) y += s_z[i] * load_raw(raw_idx, a.raw_idx_pitch, r0 + i, d, a.raw_is_f32);
-      s_y[d] = y;
-    }
-  }
+  // weighted sums: per-wave partials over interleaved tokens, merged in wave order
+  pool_partial(raw, a.raw_pitch, r0, a.m, ng, a.raw_is_f32, s_z, s_part[wave], wave, lane);
+  if (a.idx_fmt >= 0)
+    pool_partial(raw_idx, a.raw_idx_pitch, r0, a.m, ngi, a.raw_is_f32, s_z, s_party[wave], wave, lane);
+  __syncthreads();
+  for (int d = tid; d < a.D; d += kPoolThreads)
+    s_c[d] = ((s_part[0][d] + s_part[1][d]) + s_part[2][d]) + s_part[3][d];
+  if (a.idx_fmt >= 0)
+    for (int d = tid; d < a.d_I; d += kPoolThreads)
+      s_y[d] = ((s_party[0][d] + s_party[1][d]) + s_party[2][d]) + s_party[3][d];
   __syncthreads();
   // half-split RoPE of the entry's slice at the block's last position
   const int half = a.D_r / 2, D_n = a.D - a.D_r;

@@ -104,6 +104,10 @@ def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, che
     err = row_rel_err(got_o, ref["o"])
     assert err <= tol, f"output rel err {err:.3e} > {tol}"
     lse = to_np(dev.lse)[qs]
-    # lse is stored as float32
-    assert np.allclose(lse, ref["lse"], rtol=1e-4 if not dev.f32 else 1e-6, atol=1e-3 if not dev.f32 else 1e-6)
+    # lse: float32 storage on the f32 path; on the BF16 path a relative error r of the
+    # softmax normalizer is an absolute error ~r of its log, so the output bar applies
+    if dev.f32:
+        assert np.allclose(lse, ref["lse"], rtol=1e-6, atol=1e-6)
+    else:
+        assert np.abs(lse - ref["lse"]).max() <= TOL_QUANT, np.abs(lse - ref["lse"]).max()
     return ref, dev, err

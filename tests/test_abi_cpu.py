@@ -74,10 +74,13 @@ def test_kv_compress_validation():
     d = kv_desc(raw_idx=FAKE, raw_idx_pitch=256, d_I=128)
     d.out_idx.fmt, d.out_idx.data, d.out_idx.pitch = A.MXFP4, FAKE, 64
     assert call("hca_kv_compress", d) == -1          # MXFP4 without scales
-    d.d_I = 100
+    d.d_I = 104
     d.out_idx.scales, d.out_idx.scale_pitch = FAKE, 4
     assert call("hca_kv_compress", d) == -2          # d_I not a multiple of 32
-    assert b"multiple of 32" in A.lib.hca_last_error() or b"32" in A.lib.hca_last_error()
+    assert b"32" in A.lib.hca_last_error()
+    d.d_I = 100
+    assert call("hca_kv_compress", d) == -2          # d_I not a multiple of 8
+    assert call("hca_kv_compress", kv_desc(D=500)) == -2
     assert call("hca_kv_compress", kv_desc(n_blocks=0, raw=None)) == 0   # nothing to do
 
 
@@ -96,7 +99,7 @@ def test_indexer_validation_and_workspace():
     n = ctypes.c_size_t(0)
     d = idx_desc()
     assert A.lib.hca_workspace_bytes(A.OP_INDEXER_TOPK, ctypes.byref(d), ctypes.byref(n)) == 0
-    assert n.value == 8 * 32768 * 4 + 8 * 2048 * 4
+    assert n.value >= 8 * 32768 * 4 + 8 * 2048 * 4      # scores + first-digit histograms + ...
     d.workspace, d.workspace_bytes = FAKE, n.value - 1
     assert call("hca_indexer_topk", d) == -6
     d.workspace = None
