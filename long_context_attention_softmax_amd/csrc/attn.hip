@@ -45,17 +45,9 @@ __device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
   int64_t V = (t + 1) / a.m;
   if (V > a.max_visible) V = a.max_visible;
   si.V = V;
-  if (a.mode == HCA_MODE_CSA) {
-    const int32_t* ix = a.idx + (int64_t)n * a.k;
-    int c = 0;
-    // ascending list padded with -1: count the valid prefix by binary search on the first -1
-    int lo = 0, hi = a.k;
-    while (lo < hi) { int mid = (lo + hi) >> 1; if (ix[mid] >= 0) lo = mid + 1; else hi = mid; }
-    c = lo;
-    si.n_ent = c;
-  } else {
-    si.n_ent = (int)V;
-  }
+  // CSA: the list is ascending and -1 padded, so its valid entries are a prefix of
+  // at most min(k, V) slots; invalid slots inside it are masked when staged
+  si.n_ent = (int)(a.mode == HCA_MODE_CSA ? (V < a.k ? V : a.k) : V);
   si.u0 = t - a.n_win + 1 > 0 ? t - a.n_win + 1 : 0;
   si.n_w = (int)(t - si.u0 + 1);
   if (a.n_win == 0) si.n_w = 0;
@@ -149,6 +141,8 @@ constexpr int kD = 512, kDr = 64, kDn = 448;
 constexpr int kChunk = 32;                 // keys staged per step
 constexpr int kKsPitch = kD + 8;           // bf16 elements per LDS key row (pad vs bank conflicts)
 constexpr int kPPitch = kChunk + 8;
+constexpr int kMaxSplitKeys = 1024;        // keys of one slice (index list preloaded in LDS)
+constexpr int kMaxSplits = 4096;
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
@@ -188,77 +182,93 @@ __device__ __forceinline__ PartialPtrs partial_ptrs(void* ws, int Nq, int S, int
   return p;
 }
 
-// Stage set positions [p0, p0 + 32) of query n into Ks as BF16 rows.
-__device__ __forceinline__ void stage_chunk(const AttnArgs& a, const SetInfo& si, int n, int b,
-                                            int p0, int p_end, __bf16* Ks, uint8_t* kvalid,
-                                            const double* s_inv, int nthreads) {
-  for (int task = threadIdx.x; task < kChunk * 8; task += nthreads) {
-    const int kk = task >> 3, seg = task & 7;
-    const int p = p0 + kk;
-    uint32_t w[32];
-    const int64_t j = (p < si.n_ent && a.mode == HCA_MODE_CSA) ? a.idx[(int64_t)n * a.k + p] : p;
-    const bool ok = p < p_end && (p >= si.n_ent || (j >= 0 && j < si.V));
-    if (seg == 0) kvalid[kk] = ok;
-    if (!ok) {
+// Staging of set positions [p0, p0 + 32) of a query into Ks as BF16 rows.
+// Task (kk, seg): key kk of the chunk, dims [64 seg, 64 seg + 64).  Every branch
+// keeps its data in named registers and writes LDS itself (no aggregates that
+// would be placed in scratch memory).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc) {
+  v2bf v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI);
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+
+// 16 FP8 codes -> 16 BF16 values times the power-of-two scale (exact)
+__device__ __forceinline__ void cvt16(uint4 x, float sc, uint4* dst) {
+  dst[0] = make_uint4(cvt2<false>(x.x, sc), cvt2<true>(x.x, sc), cvt2<false>(x.y, sc), cvt2<true>(x.y, sc));
+  dst[1] = make_uint4(cvt2<false>(x.z, sc), cvt2<true>(x.z, sc), cvt2<false>(x.w, sc), cvt2<true>(x.w, sc));
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// rotate the 32 pairs (i, 32 + i) of a 64-element BF16 RoPE slice held as 8 uint4
+// at position u; writes the rotated slice to dst[0..7]
+__device__ __forceinline__ void rope64(const uint4 (&x)[8], int64_t u, const double* s_inv, uint4* dst) {
+  uint32_t outw[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) w[i] = 0;
-    } else if (p < si.n_ent) {
-      const int64_t row = si.row0 + j;
-      if (seg < 7) {
-        const float sc = a.c_scale[row];
-        const uint4* src = reinterpret_cast<const uint4*>(a.c_nope + row * a.c_nope_pitch + seg * 64);
+  for (int i2 = 0; i2 < 16; ++i2) {          // pairs 2*i2 and 2*i2+1 share a word
+    float c0, s0, c1, s1;
+    rope_cs(u, s_inv[2 * i2], &c0, &s0);
+    rope_cs(u, s_inv[2 * i2 + 1], &c1, &s1);
+    const uint32_t lo = word(x[i2 >> 2], i2 & 3), hi = word(x[4 + (i2 >> 2)], i2 & 3);
+    const float a0 = bf16_to_f32((uint16_t)lo), a1 = bf16_to_f32((uint16_t)(lo >> 16));
+    const float b0 = bf16_to_f32((uint16_t)hi), b1 = bf16_to_f32((uint16_t)(hi >> 16));
+    outw[i2] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+    outw[16 + i2] = pack_bf16x2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+  }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint4 u = src[v];
-          uint32_t x[4] = {u.x, u.y, u.z, u.w};
+  for (int v = 0; v < 8; ++v) dst[v] = make_uint4(outw[4 * v], outw[4 * v + 1], outw[4 * v + 2], outw[4 * v + 3]);
+}
+
+__device__ __forceinline__ void stage_task(const AttnArgs& a, const SetInfo& si, int b, int p0, int p_beg,
+                                           int p_end, const int32_t* s_idx, int task, __bf16* Ks,
+                                           uint8_t* kvalid, const double* s_inv) {
+  const int kk = task >> 3, seg = task & 7;
+  const int p = p0 + kk;
+  uint4* dst = reinterpret_cast<uint4*>(Ks + kk * kKsPitch + seg * 64);
+  bool ok = p < p_end;
+  int64_t row = 0;
+  if (ok && p < si.n_ent) {
+    const int64_t j = (a.mode == HCA_MODE_CSA) ? (int64_t)s_idx[p - p_beg] : p;
+    ok = j >= 0 && j < si.V;
+    row = si.row0 + j;
+  }
+  if (seg == 0) kvalid[kk] = ok;
+  if (!ok) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[e], sc, false);
-            v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[e], sc, true);
-            uint32_t ulo, uhi;
-            __builtin_memcpy(&ulo, &lo, 4);
-            __builtin_memcpy(&uhi, &hi, 4);
-            w[v * 8 + e * 2] = ulo;
-            w[v * 8 + e * 2 + 1] = uhi;
-          }
-        }
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(a.c_rope + row * a.c_rope_pitch);
+    for (int v = 0; v < 8; ++v) dst[v] = z;
+  } else if (p < si.n_ent && seg < 7) {            // entry: FP8 nope dims
+    const uint4* src = reinterpret_cast<const uint4*>(a.c_nope + row * a.c_nope_pitch + seg * 64);
+    const uint4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
+    const float sc = a.c_scale[row];
+    cvt16(x0, sc, dst + 0);
+    cvt16(x1, sc, dst + 2);
+    cvt16(x2, sc, dst + 4);
+    cvt16(x3, sc, dst + 6);
+  } else if (p < si.n_ent) {                       // entry: BF16 RoPE dims (already rotated)
+    const uint4* src = reinterpret_cast<const uint4*>(a.c_rope + row * a.c_rope_pitch);
+    uint4 x[8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          uint4 u = src[v];
-          w[v * 4] = u.x; w[v * 4 + 1] = u.y; w[v * 4 + 2] = u.z; w[v * 4 + 3] = u.w;
-        }
-      }
+    for (int v = 0; v < 8; ++v) x[v] = src[v];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) dst[v] = x[v];
+  } else {                                         // window token, raw BF16
+    const int64_t u = si.u0 + (p - si.n_ent);
+    const int64_t wrow = (int64_t)b * a.win_cap + u % a.win_cap;
+    const uint4* src = reinterpret_cast<const uint4*>(a.win + wrow * a.win_pitch + seg * 128);
+    uint4 x[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) x[v] = src[v];
+    if (seg == 7) {
+      rope64(x, u, s_inv, dst);
     } else {
-      const int64_t u = si.u0 + (p - si.n_ent);
-      const int64_t row = (int64_t)b * a.win_cap + u % a.win_cap;
-      const uint4* src = reinterpret_cast<const uint4*>(a.win + row * a.win_pitch + seg * 128);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        uint4 x = src[v];
-        w[v * 4] = x.x; w[v * 4 + 1] = x.y; w[v * 4 + 2] = x.z; w[v * 4 + 3] = x.w;
-      }
-      if (seg == 7) {   // dims 448..511: rotate pairs (448+i, 480+i) at u
-        uint32_t rw[32];
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) {        // pairs i = 2*i2, 2*i2+1 share words
-          float c0, s0, c1, s1;
-          rope_cs(u, s_inv[2 * i2], &c0, &s0);
-          rope_cs(u, s_inv[2 * i2 + 1], &c1, &s1);
-          const uint32_t lo = w[i2], hi = w[16 + i2];
-          const float a0 = bf16_to_f32((uint16_t)lo), a1 = bf16_to_f32((uint16_t)(lo >> 16));
-          const float b0 = bf16_to_f32((uint16_t)hi), b1 = bf16_to_f32((uint16_t)(hi >> 16));
-          rw[i2] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-          rw[16 + i2] = pack_bf16x2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) w[i] = rw[i];
-      }
+      for (int v = 0; v < 8; ++v) dst[v] = x[v];
     }
-    uint4* dst = reinterpret_cast<uint4*>(Ks + kk * kKsPitch + seg * 64);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) dst[v] = make_uint4(w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]);
   }
 }
 
@@ -268,6 +278,7 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
   __shared__ __attribute__((aligned(16))) __bf16 Pb[NW][16 * kPPitch];
   __shared__ double s_inv[32];
   __shared__ uint8_t s_kval[kChunk];
+  __shared__ int32_t s_idx[kMaxSplitKeys];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, n = blockIdx.y;
@@ -279,7 +290,12 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
   const int b = a.seq_id[n];
   const int64_t t = a.q_pos[n];
   if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr) / kTwoPi;   // turns per position
+  if (a.mode == HCA_MODE_CSA) {
+    const int p_ent_end = min(p_end, si.n_ent);
+    for (int p = p_beg + tid; p < p_ent_end; p += 64 * NW) s_idx[p - p_beg] = a.idx[(int64_t)n * a.k + p];
+  }
   __syncthreads();
+  constexpr int TPT = (kChunk * 8) / (64 * NW);      // staging tasks per thread
 
   // Q operands: lane (r, g) of wave w holds head 16w + r, dims 32s + 8g .. +7
   const int head = 16 * wave + r;
@@ -307,7 +323,8 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
   float l_run[4] = {0.f, 0.f, 0.f, 0.f};
 
   for (int p0 = p_beg; p0 < p_end; p0 += kChunk) {
-    stage_chunk(a, si, n, b, p0, p_end, Ks, s_kval, s_inv, 64 * NW);
+#pragma unroll
+    for (int q = 0; q < TPT; ++q) stage_task(a, si, b, p0, p_beg, p_end, s_idx, tid + q * 64 * NW, Ks, s_kval, s_inv);
     __syncthreads();
     // S = Q K^T for 32 keys: two 16-key tiles
     v4f sc[2];
@@ -322,29 +339,45 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
       }
       sc[kt] = c;
     }
-    // online softmax for heads 4g + i (this lane's rows); key = p0 + 16kt + r
-    float alpha[4];
+    // online softmax for heads 4g + i (this lane's rows); key = p0 + 16kt + r.
+    // m_run is a reference maximum: probabilities are exp2(x - m_run), and O is
+    // rescaled only when a row's maximum exceeds its reference by more than 2^8
+    // (wave-uniform branch); the final normalization makes the choice exact.
+    float x0[4], x1[4], mx[4];
+    bool need = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x0 = s_kval[r] ? sc[0][i] * qscale : -INFINITY;
-      float x1 = s_kval[16 + r] ? sc[1][i] * qscale : -INFINITY;
-      float mx = fmaxf(x0, x1);
+      x0[i] = s_kval[r] ? sc[0][i] * qscale : -INFINITY;
+      x1[i] = s_kval[16 + r] ? sc[1][i] * qscale : -INFINITY;
+      float m = fmaxf(x0[i], x1[i]);
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const float m_new = fmaxf(m_run[i], mx);
-      const float al = (m_new == -INFINITY) ? 1.0f : exp2f(m_run[i] - m_new);
-      const float e0 = (m_new == -INFINITY) ? 0.0f : exp2f(x0 - m_new);
-      const float e1 = (m_new == -INFINITY) ? 0.0f : exp2f(x1 - m_new);
-      l_run[i] = l_run[i] * al + (e0 + e1);
-      m_run[i] = m_new;
-      alpha[i] = al;
-      Pb[wave][(4 * g + i) * kPPitch + r] = (__bf16)e0;
-      Pb[wave][(4 * g + i) * kPPitch + 16 + r] = (__bf16)e1;
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      mx[i] = m;
+      need |= m > m_run[i] + 8.0f;
+    }
+    if (__builtin_amdgcn_read_exec() & __ballot(need)) {
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float m_new = fmaxf(m_run[i], mx[i]);
+        alpha[i] = (m_run[i] == -INFINITY) ? 0.0f : exp2f(m_run[i] - m_new);
+        l_run[i] *= alpha[i];
+        m_run[i] = m_new;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) {
+        acc[dt][0] *= alpha[0]; acc[dt][1] *= alpha[1];
+        acc[dt][2] *= alpha[2]; acc[dt][3] *= alpha[3];
+      }
     }
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      acc[dt][0] *= alpha[0]; acc[dt][1] *= alpha[1];
-      acc[dt][2] *= alpha[2]; acc[dt][3] *= alpha[3];
+    for (int i = 0; i < 4; ++i) {
+      const bool live = m_run[i] != -INFINITY;
+      const float e0 = live ? exp2f(x0[i] - m_run[i]) : 0.0f;
+      const float e1 = live ? exp2f(x1[i] - m_run[i]) : 0.0f;
+      l_run[i] += e0 + e1;
+      Pb[wave][(4 * g + i) * kPPitch + r] = (__bf16)e0;
+      Pb[wave][(4 * g + i) * kPPitch + 16 + r] = (__bf16)e1;
     }
     // P (A operand): lane (r, g) needs P[head r][keys 8g .. 8g+7], written above by
     // other lanes of this wave
@@ -407,26 +440,37 @@ __global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_sp
 
 // merge the slices of one (query, head) in slice order, with the sink
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a, int n_splits, int keys_per_split) {
-  const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[4];
+  const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const SetInfo si = set_info(a, n);
   const int n_set = si.n_ent + si.n_w;
   const int S = (n_set + keys_per_split - 1) / keys_per_split;
   PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, n_splits, a.H);
+  const size_t base0 = (size_t)n * n_splits * a.H + h;          // + s * H
   const float sig = a.sink[h] * (float)kLog2e;
-  float M = sig;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pp.m[((size_t)n * n_splits + s) * a.H + h]);
-  float den = exp2f(sig - M);
-  for (int s = 0; s < S; ++s) {
-    const size_t base = ((size_t)n * n_splits + s) * a.H + h;
-    den += pp.l[base] * exp2f(pp.m[base] - M);
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pp.m[base0 + (size_t)s * a.H]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), sig);
+  __syncthreads();
+  for (int s = tid; s < S; s += 256) s_w[s] = exp2f(pp.m[base0 + (size_t)s * a.H] - M);
+  __syncthreads();
+  if (wave == 0) {                     // fixed-order denominator
+    float l = 0.f;
+    for (int s = lane; s < S; s += 64) l += pp.l[base0 + (size_t)s * a.H] * s_w[s];
+    l = wave_sum(l);
+    if (lane == 0) s_red[0] = l;
   }
+  __syncthreads();
+  const float den = exp2f(sig - M) + s_red[0];
   const float inv = 1.0f / den;
   for (int d = tid; d < kD; d += 256) {
     float acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const size_t base = ((size_t)n * n_splits + s) * a.H + h;
-      acc += pp.o[base * kD + d] * exp2f(pp.m[base] - M);
-    }
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) acc += pp.o[(base0 + (size_t)s * a.H) * kD + d] * s_w[s];
     reinterpret_cast<__bf16*>(a.o)[((int64_t)n * a.H + h) * kD + d] = (__bf16)(acc * inv);
   }
   if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
@@ -443,7 +487,11 @@ void split_plan(int Nq, int mode, int k, int n_win, int64_t max_visible, int pre
   int64_t s = want < chunks / 4 ? want : chunks / 4;
   if (prefill) s = 1;
   if (s < 1) s = 1;
+  const int64_t max_chunks_per_split = kMaxSplitKeys / kChunk;   // CSA index lists live in LDS
+  if (mode == HCA_MODE_CSA && (chunks + s - 1) / s > max_chunks_per_split)
+    s = (chunks + max_chunks_per_split - 1) / max_chunks_per_split;
   int64_t per = (chunks + s - 1) / s;
+  if ((chunks + per - 1) / per > kMaxSplits) per = (chunks + kMaxSplits - 1) / kMaxSplits;
   *kps = (int)(per * kChunk);
   *n_splits = (int)((max_set + *kps - 1) / *kps);
 }

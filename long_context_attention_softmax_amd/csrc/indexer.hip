@@ -337,7 +337,10 @@ __device__ int find_digit(const uint32_t* hist, int nbins, uint32_t* need, uint3
 
 __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
   __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_ck[kChunk1];
+  __shared__ int32_t s_cj[kChunk1];
   __shared__ uint32_t s_wave[256 / 64 + 1];
+  __shared__ uint32_t s_n, s_base;
   __shared__ int s_found;
   __shared__ uint32_t s_need;
   const int n = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
@@ -347,6 +350,7 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   if (V <= K || j0 >= V) return;
   const uint32_t* gh = a.hist + (int64_t)n * kBins;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
+  if (tid == 0) s_n = 0;
   __syncthreads();
   uint32_t need = (uint32_t)K;
   const uint32_t d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
@@ -358,16 +362,26 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
     const uint32_t dg = key >> 21;
     gt += dg > d1;
     if (dg == d1) {
-      const uint32_t p = atomicAdd(&ws.cand_count[n], 1u);
-      if (p < (uint32_t)kCandCap2) {
-        ws.cand_key[(int64_t)n * kCandCap2 + p] = key;
-        ws.cand_idx[(int64_t)n * kCandCap2 + p] = (int32_t)j;
-      }
+      const uint32_t p = atomicAdd(&s_n, 1u);           // LDS: at most kChunk1 per chunk
+      s_ck[p] = key;
+      s_cj[p] = (int32_t)j;
     }
   }
   uint32_t tot;
-  block_exclusive_scan<256>(gt, s_wave, &tot);
-  if (tid == 0) ws.chunk_gt[(int64_t)n * ws.nch + c] = tot;
+  block_exclusive_scan<256>(gt, s_wave, &tot);         // also orders the appends above
+  if (tid == 0) {
+    ws.chunk_gt[(int64_t)n * ws.nch + c] = tot;
+    s_base = s_n ? atomicAdd(&ws.cand_count[n], s_n) : 0;
+  }
+  __syncthreads();
+  const uint32_t cnt = s_n, base = s_base;
+  for (uint32_t i = tid; i < cnt; i += 256) {
+    const uint32_t p = base + i;
+    if (p < (uint32_t)kCandCap2) {
+      ws.cand_key[(int64_t)n * kCandCap2 + p] = s_ck[i];
+      ws.cand_idx[(int64_t)n * kCandCap2 + p] = s_cj[i];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(IndexerArgs a, SelectWs ws) {

@@ -20,43 +20,51 @@ namespace {
 constexpr int kPoolThreads = 256;
 constexpr int kMaxM = 256, kMaxD = 1024, kMaxDI = 256;
 
-// 8 consecutive raw elements [8g, 8g+8) of row `row` as fp64 (BF16 or f32 storage)
-__device__ __forceinline__ void load8(const char* base, int64_t pitch, int64_t row, int g, int is_f32,
-                                      double out[8]) {
-  const char* p = base + row * pitch;
-  if (is_f32) {
-    const float4* q = reinterpret_cast<const float4*>(p) + 2 * g;
-    float4 a = q[0], b = q[1];
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  } else {
-    uint4 u = reinterpret_cast<const uint4*>(p)[g];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = (double)bf16_to_f32((uint16_t)w[i]);
-      out[2 * i + 1] = (double)bf16_to_f32((uint16_t)(w[i] >> 16));
-    }
-  }
+// Raw storage of 8 consecutive elements [8g, 8g+8) of a row: one uint4 (BF16) or
+// two (f32); decoded to fp64 on use.
+template <bool F32> struct Raw8 { uint4 v[F32 ? 2 : 1]; };
+
+template <bool F32>
+__device__ __forceinline__ Raw8<F32> load8(const char* base, int64_t pitch, int64_t row, int g) {
+  Raw8<F32> r;
+  const uint4* q = reinterpret_cast<const uint4*>(base + row * pitch) + (F32 ? 2 * g : g);
+  r.v[0] = q[0];
+  if (F32) r.v[F32 ? 1 : 0] = q[1];
+  return r;
 }
 
-// Partial weighted sums of one wave over the tokens i = wave, wave+4, ... of the block,
-// four tokens in flight at a time; lane handles 8-element groups g = lane, lane+64, ...
+template <bool F32>
+__device__ __forceinline__ double elem(const Raw8<F32>& r, int e) {
+  if (F32) {
+    const uint4 u = r.v[e >> 2];
+    const uint32_t w = (e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w;
+    return (double)__uint_as_float(w);
+  }
+  const uint4 u = r.v[0];
+  const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+  return (double)bf16_to_f32((uint16_t)(w >> (16 * (e & 1))));
+}
+
+constexpr int kTokU = 16;     // tokens of one wave in flight
+
+// Partial weighted sums of one wave over the tokens i = wave, wave+4, ... of the block;
+// lane handles 8-element groups g = lane, lane+64, ...
+template <bool F32>
 __device__ __forceinline__ void pool_partial(const char* base, int64_t pitch, int64_t r0, int m, int ngroups,
-                                             int is_f32, const double* alpha, double* part, int wave, int lane) {
+                                             const double* alpha, double* part, int wave, int lane) {
   for (int g = lane; g < ngroups; g += 64) {
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i0 = wave; i0 < m; i0 += 16) {
-      double x[4][8];
+    for (int i0 = wave; i0 < m; i0 += 4 * kTokU) {
+      Raw8<F32> x[kTokU];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i0 + 4 * j < m) load8(base, pitch, r0 + i0 + 4 * j, g, is_f32, x[j]);
+      for (int j = 0; j < kTokU; ++j)
+        if (i0 + 4 * j < m) x[j] = load8<F32>(base, pitch, r0 + i0 + 4 * j, g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kTokU; ++j)
         if (i0 + 4 * j < m) {
           const double al = alpha[i0 + 4 * j];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += al * x[j][e];
+          for (int e = 0; e < 8; ++e) acc[e] += al * elem<F32>(x[j], e);
         }
     }
 #pragma unroll
@@ -64,6 +72,7 @@ __device__ __forceinline__ void pool_partial(const char* base, int64_t pitch, in
   }
 }
 
+template <bool F32>
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   __shared__ double s_z[kMaxM];
   __shared__ double s_c[kMaxD];
@@ -82,28 +91,31 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   const char* raw_idx = static_cast<const char*>(a.raw_idx);
   const int ng = a.D / 8, ngi = a.d_I / 8;
 
-  // gate logits z_i = g . x_i + b_i : wave w takes tokens w, w+4, ...; four at a time
-  for (int i0 = wave; i0 < a.m; i0 += 16) {
-    double acc[4] = {0, 0, 0, 0};
+  // gate logits z_i = g . x_i + b_i : wave w takes tokens w, w+4, ...; kTokU in flight
+  for (int i0 = wave; i0 < a.m; i0 += 4 * kTokU) {
+    double acc[kTokU];
+#pragma unroll
+    for (int j = 0; j < kTokU; ++j) acc[j] = 0.0;
     for (int g = lane; g < ng; g += 64) {
       const float4* gw4 = reinterpret_cast<const float4*>(a.gate_w) + 2 * g;
       const float4 ga = gw4[0], gb = gw4[1];
       const double gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-      double x[4][8];
+      Raw8<F32> x[kTokU];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i0 + 4 * j < a.m) load8(raw, a.raw_pitch, r0 + i0 + 4 * j, g, a.raw_is_f32, x[j]);
+      for (int j = 0; j < kTokU; ++j)
+        if (i0 + 4 * j < a.m) x[j] = load8<F32>(raw, a.raw_pitch, r0 + i0 + 4 * j, g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kTokU; ++j)
         if (i0 + 4 * j < a.m) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j] += gw[e] * x[j][e];
+          for (int e = 0; e < 8; ++e) acc[j] += gw[e] * elem<F32>(x[j], e);
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTokU; ++j) {
+      if (i0 + 4 * j >= a.m) break;                      // uniform over the wave
       const double z = wave_sum(acc[j]);
-      if (lane == 0 && i0 + 4 * j < a.m) s_z[i0 + 4 * j] = z + (double)a.gate_b[i0 + 4 * j];
+      if (lane == 0) s_z[i0 + 4 * j] = z + (double)a.gate_b[i0 + 4 * j];
     }
   }
   __syncthreads();
@@ -119,9 +131,9 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   }
   __syncthreads();
   // weighted sums: per-wave partials over interleaved tokens, merged in wave order
-  pool_partial(raw, a.raw_pitch, r0, a.m, ng, a.raw_is_f32, s_z, s_part[wave], wave, lane);
+  pool_partial<F32>(raw, a.raw_pitch, r0, a.m, ng, s_z, s_part[wave], wave, lane);
   if (a.idx_fmt >= 0)
-    pool_partial(raw_idx, a.raw_idx_pitch, r0, a.m, ngi, a.raw_is_f32, s_z, s_party[wave], wave, lane);
+    pool_partial<F32>(raw_idx, a.raw_idx_pitch, r0, a.m, ngi, s_z, s_party[wave], wave, lane);
   __syncthreads();
   for (int d = tid; d < a.D; d += kPoolThreads)
     s_c[d] = ((s_part[0][d] + s_part[1][d]) + s_part[2][d]) + s_part[3][d];
@@ -198,7 +210,10 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
   if (a.n_blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3(a.n_blocks), dim3(kPoolThreads), 0, s, a);
+  if (a.raw_is_f32)
+    hipLaunchKernelGGL(pool_kernel<true>, dim3(a.n_blocks), dim3(kPoolThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(pool_kernel<false>, dim3(a.n_blocks), dim3(kPoolThreads), 0, s, a);
   return hipGetLastError();
 }
 
