@@ -137,15 +137,38 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
 }
 
 // ============================================================ BF16 MFMA path
+//
+// One workgroup of 8 waves walks a contiguous run of 64-key chunks.  Wave w
+// owns head group hg = w % 4 (heads 16hg .. 16hg+15) and dim half dh = w / 4
+// (dims 256dh .. 256dh+255): QK^T is summed over its dims and the two halves
+// exchange partial logits through LDS (every logit is then S_dh0 + S_dh1, the
+// same in both waves), so both hold identical probabilities and each accumulates
+// P.V for its own 256 output dims.  The compressed entries of chunk c+1 are loaded
+// into registers while chunk c is computed, then widened to BF16 into the LDS
+// tile; window tokens (at most two chunks per query) are staged directly.
+//
+// Decode (few queries): the chunks of all queries form one list that is cut into
+// equal runs, one per workgroup, so ragged lengths balance.  A query whose chunks
+// all fall in one run is finished there; otherwise each run leaves a partial
+// (max, sum, unnormalized o) in the workspace and a combine kernel merges them in
+// run order with the sink.  Prefill (many queries): one workgroup per query.
 constexpr int kD = 512, kDr = 64, kDn = 448;
-constexpr int kChunk = 32;                 // keys staged per step
-constexpr int kKsPitch = kD + 8;           // bf16 elements per LDS key row (pad vs bank conflicts)
-constexpr int kPPitch = kChunk + 8;
-constexpr int kMaxSplitKeys = 1024;        // keys of one slice (index list preloaded in LDS)
-constexpr int kMaxSplits = 4096;
+constexpr int KC = 64;                     // keys per chunk
+constexpr int kKsPitch = kD + 8;           // bf16 per LDS key row (1040 B: rows 4 banks apart)
+constexpr int kPtPitch = 16 + 4;           // bf16 per LDS row of P^T (16 heads)
+constexpr int kThreads = 512;              // 8 waves
+constexpr int kIdxWin = 2048;              // index-list positions held in LDS
+constexpr int kMaxDecodeQ = 256;           // queries of one flattened (decode) launch
+#ifndef HCA_ATTN_GRID
+#define HCA_ATTN_GRID 256                  // workgroups of a decode launch
+#endif
+#ifndef HCA_ATTN_MIN_CHUNKS
+#define HCA_ATTN_MIN_CHUNKS 1              // fewest chunks per decode workgroup
+#endif
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -166,26 +189,6 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double inv_turn, float* c, 
   *c = __builtin_amdgcn_cosf(f);
 }
 
-struct PartialPtrs {
-  float* m;     // [Nq, S, H]  running max, log2 units
-  float* l;     // [Nq, S, H]
-  float* o;     // [Nq, S, H, D]
-};
-
-__device__ __forceinline__ PartialPtrs partial_ptrs(void* ws, int Nq, int S, int H) {
-  PartialPtrs p;
-  char* b = static_cast<char*>(ws);
-  size_t ml = ((size_t)Nq * S * H * 4 + 255) / 256 * 256;
-  p.m = reinterpret_cast<float*>(b);
-  p.l = reinterpret_cast<float*>(b + ml);
-  p.o = reinterpret_cast<float*>(b + 2 * ml);
-  return p;
-}
-
-// Staging of set positions [p0, p0 + 32) of a query into Ks as BF16 rows.
-// Task (kk, seg): key kk of the chunk, dims [64 seg, 64 seg + 64).  Every branch
-// keeps its data in named registers and writes LDS itself (no aggregates that
-// would be placed in scratch memory).
 template <bool HI>
 __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc) {
   v2bf v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI);
@@ -194,273 +197,531 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc) {
   return u;
 }
 
-// 16 FP8 codes -> 16 BF16 values times the power-of-two scale (exact)
-__device__ __forceinline__ void cvt16(uint4 x, float sc, uint4* dst) {
-  dst[0] = make_uint4(cvt2<false>(x.x, sc), cvt2<true>(x.x, sc), cvt2<false>(x.y, sc), cvt2<true>(x.y, sc));
-  dst[1] = make_uint4(cvt2<false>(x.z, sc), cvt2<true>(x.z, sc), cvt2<false>(x.w, sc), cvt2<true>(x.w, sc));
+// 8 FP8 codes -> 8 BF16 values times the power-of-two scale (exact)
+__device__ __forceinline__ u4 cvt8(u2 x, float sc) {
+  return (u4){cvt2<false>(x[0], sc), cvt2<true>(x[0], sc), cvt2<false>(x[1], sc), cvt2<true>(x[1], sc)};
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
+// What one query attends to, as the chunk walk needs it.
+struct QInfo {
+  int64_t row0;     // first cache row of the sequence
+  int64_t u0;       // first window position
+  int64_t t;        // query position
+  int64_t V;        // visible compressed entries
+  int n_ent;        // compressed entries in the set (a prefix of the index list for CSA)
+  int n_set;        // n_ent + window tokens
+  int b;            // sequence
+  int pad;
+};
 
-// rotate the 32 pairs (i, 32 + i) of a 64-element BF16 RoPE slice held as 8 uint4
-// at position u; writes the rotated slice to dst[0..7]
-__device__ __forceinline__ void rope64(const uint4 (&x)[8], int64_t u, const double* s_inv, uint4* dst) {
-  uint32_t outw[32];
-#pragma unroll
-  for (int i2 = 0; i2 < 16; ++i2) {          // pairs 2*i2 and 2*i2+1 share a word
-    float c0, s0, c1, s1;
-    rope_cs(u, s_inv[2 * i2], &c0, &s0);
-    rope_cs(u, s_inv[2 * i2 + 1], &c1, &s1);
-    const uint32_t lo = word(x[i2 >> 2], i2 & 3), hi = word(x[4 + (i2 >> 2)], i2 & 3);
-    const float a0 = bf16_to_f32((uint16_t)lo), a1 = bf16_to_f32((uint16_t)(lo >> 16));
-    const float b0 = bf16_to_f32((uint16_t)hi), b1 = bf16_to_f32((uint16_t)(hi >> 16));
-    outw[i2] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-    outw[16 + i2] = pack_bf16x2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
-  }
-#pragma unroll
-  for (int v = 0; v < 8; ++v) dst[v] = make_uint4(outw[4 * v], outw[4 * v + 1], outw[4 * v + 2], outw[4 * v + 3]);
-}
-
-__device__ __forceinline__ void stage_task(const AttnArgs& a, const SetInfo& si, int b, int p0, int p_beg,
-                                           int p_end, const int32_t* s_idx, int task, __bf16* Ks,
-                                           uint8_t* kvalid, const double* s_inv) {
-  const int kk = task >> 3, seg = task & 7;
-  const int p = p0 + kk;
-  uint4* dst = reinterpret_cast<uint4*>(Ks + kk * kKsPitch + seg * 64);
-  bool ok = p < p_end;
-  int64_t row = 0;
-  if (ok && p < si.n_ent) {
-    const int64_t j = (a.mode == HCA_MODE_CSA) ? (int64_t)s_idx[p - p_beg] : p;
-    ok = j >= 0 && j < si.V;
-    row = si.row0 + j;
-  }
-  if (seg == 0) kvalid[kk] = ok;
-  if (!ok) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) dst[v] = z;
-  } else if (p < si.n_ent && seg < 7) {            // entry: FP8 nope dims
-    const uint4* src = reinterpret_cast<const uint4*>(a.c_nope + row * a.c_nope_pitch + seg * 64);
-    const uint4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
-    const float sc = a.c_scale[row];
-    cvt16(x0, sc, dst + 0);
-    cvt16(x1, sc, dst + 2);
-    cvt16(x2, sc, dst + 4);
-    cvt16(x3, sc, dst + 6);
-  } else if (p < si.n_ent) {                       // entry: BF16 RoPE dims (already rotated)
-    const uint4* src = reinterpret_cast<const uint4*>(a.c_rope + row * a.c_rope_pitch);
-    uint4 x[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) x[v] = src[v];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) dst[v] = x[v];
-  } else {                                         // window token, raw BF16
-    const int64_t u = si.u0 + (p - si.n_ent);
-    const int64_t wrow = (int64_t)b * a.win_cap + u % a.win_cap;
-    const uint4* src = reinterpret_cast<const uint4*>(a.win + wrow * a.win_pitch + seg * 128);
-    uint4 x[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) x[v] = src[v];
-    if (seg == 7) {
-      rope64(x, u, s_inv, dst);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 8; ++v) dst[v] = x[v];
-    }
-  }
-}
-
-template <int NW>   // waves per workgroup = H / 16
-__global__ void __launch_bounds__(64 * NW) attn_bf16_kernel(AttnArgs a, int n_splits, int keys_per_split) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kChunk * kKsPitch];
-  __shared__ __attribute__((aligned(16))) __bf16 Pb[NW][16 * kPPitch];
-  __shared__ double s_inv[32];
-  __shared__ uint8_t s_kval[kChunk];
-  __shared__ int32_t s_idx[kMaxSplitKeys];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, n = blockIdx.y;
+__device__ __forceinline__ QInfo query_info(const AttnArgs& a, int n) {
+  QInfo qi;
   const SetInfo si = set_info(a, n);
-  const int n_set = si.n_ent + si.n_w;
-  const int p_beg = split * keys_per_split;
-  if (p_beg >= n_set) return;                        // uniform: this split is empty
-  const int p_end = min(n_set, p_beg + keys_per_split);
-  const int b = a.seq_id[n];
-  const int64_t t = a.q_pos[n];
-  if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr) / kTwoPi;   // turns per position
-  if (a.mode == HCA_MODE_CSA) {
-    const int p_ent_end = min(p_end, si.n_ent);
-    for (int p = p_beg + tid; p < p_ent_end; p += 64 * NW) s_idx[p - p_beg] = a.idx[(int64_t)n * a.k + p];
-  }
-  __syncthreads();
-  constexpr int TPT = (kChunk * 8) / (64 * NW);      // staging tasks per thread
+  qi.row0 = si.row0;
+  qi.u0 = si.u0;
+  qi.t = a.q_pos[n];
+  qi.V = si.V;
+  qi.n_ent = si.n_ent;
+  qi.n_set = si.n_ent + si.n_w;
+  qi.b = a.seq_id[n];
+  qi.pad = 0;
+  return qi;
+}
 
-  // Q operands: lane (r, g) of wave w holds head 16w + r, dims 32s + 8g .. +7
-  const int head = 16 * wave + r;
-  const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)n * a.H + head) * kD;
-  v8bf qa[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) qa[s] = *reinterpret_cast<const v8bf*>(qrow + 32 * s + 8 * g);
-  {
-    // rotate the RoPE pairs (448 + i, 480 + i), i = 8g + e, held in k-steps 14 / 15
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float c, s;
-      rope_cs(t, s_inv[8 * g + e], &c, &s);
-      const float x0 = (float)qa[14][e], x1 = (float)qa[15][e];
-      qa[14][e] = (__bf16)(x0 * c - x1 * s);
-      qa[15][e] = (__bf16)(x0 * s + x1 * c);
-    }
-  }
-  const float qscale = a.tau * (float)kLog2e;        // logits in log2 units
+// Staging of one key by its 16 threads: thread q writes the 16-byte chunks
+// q, q+16, q+32, q+48 of the key's BF16 row (dims 8j .. 8j+7 for chunk j), so the
+// 16 lanes of each LDS write cover one contiguous 256-byte span.
+// An entry's chunk j < 56 comes from FP8 bytes 8j .. 8j+7 of its nope row, chunk
+// 56 + i from BF16 dims 8i .. 8i+7 of its (already rotated) RoPE slice.
+enum { kInvalid = 0, kEntry = 1, kWindow = 2 };
 
-  v4f acc[32];
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float l_run[4] = {0.f, 0.f, 0.f, 0.f};
+struct EntryRegs {
+  u2 f0, f1, f2;    // FP8 chunks q, q+16, q+32
+  u2 f3;            // FP8 chunk 48 + (q & 7)       (used by q < 8)
+  u4 r3;            // BF16 RoPE dims 8(q & 7) ..   (used by q >= 8)
+  float sc;
+  int kind;
+};
 
-  for (int p0 = p_beg; p0 < p_end; p0 += kChunk) {
-#pragma unroll
-    for (int q = 0; q < TPT; ++q) stage_task(a, si, b, p0, p_beg, p_end, s_idx, tid + q * 64 * NW, Ks, s_kval, s_inv);
-    __syncthreads();
-    // S = Q K^T for 32 keys: two 16-key tiles
-    v4f sc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      v4f c = {0.f, 0.f, 0.f, 0.f};
-      const __bf16* kr = Ks + (16 * kt + r) * kKsPitch + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        v8bf kb = *reinterpret_cast<const v8bf*>(kr + 32 * s);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, c, 0, 0, 0);
-      }
-      sc[kt] = c;
-    }
-    // online softmax for heads 4g + i (this lane's rows); key = p0 + 16kt + r.
-    // m_run is a reference maximum: probabilities are exp2(x - m_run), and O is
-    // rescaled only when a row's maximum exceeds its reference by more than 2^8
-    // (wave-uniform branch); the final normalization makes the choice exact.
-    float x0[4], x1[4], mx[4];
-    bool need = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x0[i] = s_kval[r] ? sc[0][i] * qscale : -INFINITY;
-      x1[i] = s_kval[16 + r] ? sc[1][i] * qscale : -INFINITY;
-      float m = fmaxf(x0[i], x1[i]);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      mx[i] = m;
-      need |= m > m_run[i] + 8.0f;
-    }
-    if (__builtin_amdgcn_read_exec() & __ballot(need)) {
-      float alpha[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float m_new = fmaxf(m_run[i], mx[i]);
-        alpha[i] = (m_run[i] == -INFINITY) ? 0.0f : exp2f(m_run[i] - m_new);
-        l_run[i] *= alpha[i];
-        m_run[i] = m_new;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        acc[dt][0] *= alpha[0]; acc[dt][1] *= alpha[1];
-        acc[dt][2] *= alpha[2]; acc[dt][3] *= alpha[3];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool live = m_run[i] != -INFINITY;
-      const float e0 = live ? exp2f(x0[i] - m_run[i]) : 0.0f;
-      const float e1 = live ? exp2f(x1[i] - m_run[i]) : 0.0f;
-      l_run[i] += e0 + e1;
-      Pb[wave][(4 * g + i) * kPPitch + r] = (__bf16)e0;
-      Pb[wave][(4 * g + i) * kPPitch + 16 + r] = (__bf16)e1;
-    }
-    // P (A operand): lane (r, g) needs P[head r][keys 8g .. 8g+7], written above by
-    // other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const v8bf pa = *reinterpret_cast<const v8bf*>(&Pb[wave][r * kPPitch + 8 * g]);
-    // O += P V: V^T operand via transposed LDS reads of the row-major key tile
-    const int lr = r >> 2, lc = 4 * (r & 3);
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const __bf16* base0 = Ks + (8 * g + lr) * kKsPitch + 16 * dt + lc;
-      const __bf16* base1 = base0 + 4 * kKsPitch;
-      v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)base0);
-      v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)base1);
-      v8bf vb;
-      __builtin_memcpy(&vb, &t0, 8);
-      __builtin_memcpy(reinterpret_cast<char*>(&vb) + 8, &t1, 8);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
-    }
-    __syncthreads();
+__device__ __forceinline__ int key_kind(const QInfo& qi, int p, int jrow, bool csa) {
+  if (p < qi.n_ent) {
+    const int64_t j = csa ? (int64_t)jrow : (int64_t)p;
+    return (j >= 0 && j < qi.V) ? kEntry : kInvalid;
   }
-  // full row sums
+  return p < qi.n_set ? kWindow : kInvalid;
+}
+
+// Loads of one key's share, issued without any branch so that they stay in flight
+// while the previous chunk is computed: a key that is not a valid entry reads
+// row 0 of its sequence (the caller guarantees V >= 1) and is masked by `kind`.
+__device__ __forceinline__ EntryRegs entry_load(const AttnArgs& a, const QInfo& qi, int p, int jrow, int q,
+                                                bool csa) {
+  EntryRegs e;
+  e.kind = key_kind(qi, p, jrow, csa);
+  const int64_t j = e.kind == kEntry ? (csa ? (int64_t)jrow : (int64_t)p) : 0;
+  const int64_t row = qi.row0 + j;
+  const char* nope = a.c_nope + row * a.c_nope_pitch + 8 * q;
+  e.f0 = *reinterpret_cast<const u2*>(nope);
+  e.f1 = *reinterpret_cast<const u2*>(nope + 128);
+  e.f2 = *reinterpret_cast<const u2*>(nope + 256);
+  e.f3 = *reinterpret_cast<const u2*>(nope + 384 - 8 * (q & 8));
+  e.r3 = *reinterpret_cast<const u4*>(a.c_rope + row * a.c_rope_pitch + 16 * (q & 7));
+  e.sc = a.c_scale[row];
+  return e;
+}
+
+// rotate 8 BF16 dims of a window token's RoPE slice: `own` holds pair indices
+// i0 .. i0+7, `mate` the other member of each pair; first = own is the first half
+__device__ __forceinline__ u4 rope8(u4 own, u4 mate, int i0, bool first, int64_t u, const double* s_inv) {
+  u4 out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float l = l_run[i];
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
-    l_run[i] = l;
+  for (int w = 0; w < 4; ++w) {
+    float c0, s0, c1, s1;
+    rope_cs(u, s_inv[i0 + 2 * w], &c0, &s0);
+    rope_cs(u, s_inv[i0 + 2 * w + 1], &c1, &s1);
+    const float o0 = bf16_to_f32((uint16_t)own[w]), o1 = bf16_to_f32((uint16_t)(own[w] >> 16));
+    const float m0 = bf16_to_f32((uint16_t)mate[w]), m1 = bf16_to_f32((uint16_t)(mate[w] >> 16));
+    // first half: x0 c - x1 s with x0 = own; second half: x0 s + x1 c with x1 = own
+    out[w] = first ? pack_bf16x2(o0 * c0 - m0 * s0, o1 * c1 - m1 * s1)
+                   : pack_bf16x2(m0 * s0 + o0 * c0, m1 * s1 + o1 * c1);
   }
-  const int hrow0 = 16 * wave + 4 * g;             // this lane's 4 head rows
-  if (n_splits == 1) {
-    // finalize with the sink
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = hrow0 + i;
-      const float sig = a.sink[h] * (float)kLog2e;
-      const float M = fmaxf(sig, m_run[i]);
-      const float sc_o = exp2f(m_run[i] - M);
-      const float den = exp2f(sig - M) + l_run[i] * sc_o;
-      const float f = sc_o / den;
-      __bf16* o = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) o[16 * dt + r] = (__bf16)(acc[dt][i] * f);
-      if (a.lse && r == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
+  return out;
+}
+
+// write one key's 4 chunks (this thread's share) into the LDS row
+__device__ __forceinline__ void key_commit(const AttnArgs& a, const QInfo& qi, int p, const EntryRegs& e, int q,
+                                           u4* rowp, const double* s_inv) {
+  if (e.kind == kEntry) {
+    rowp[q] = cvt8(e.f0, e.sc);
+    rowp[q + 16] = cvt8(e.f1, e.sc);
+    rowp[q + 32] = cvt8(e.f2, e.sc);
+    rowp[q + 48] = q < 8 ? cvt8(e.f3, e.sc) : e.r3;
+  } else if (e.kind == kWindow) {
+    const int64_t u = qi.u0 + (p - qi.n_ent);
+    const u4* src = reinterpret_cast<const u4*>(a.win + ((int64_t)qi.b * a.win_cap + u % a.win_cap) * a.win_pitch);
+    const u4 x0 = src[q], x1 = src[q + 16], x2 = src[q + 32], x3 = src[q + 48];
+    rowp[q] = x0;
+    rowp[q + 16] = x1;
+    rowp[q + 32] = x2;
+    if (q < 8) {
+      rowp[q + 48] = x3;
+    } else {
+      // chunk 56 + m (m < 4: first halves, pairs 8m .. 8m+7) pairs with chunk 60 + m
+      const int m = q - 8;
+      const bool first = m < 4;
+      const u4 mate = src[first ? q + 52 : q + 44];
+      rowp[q + 48] = rope8(x3, mate, 8 * (m & 3), first, u, s_inv);
     }
   } else {
-    PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, n_splits, a.H);
+    const u4 z = {0u, 0u, 0u, 0u};
+    rowp[q] = z; rowp[q + 16] = z; rowp[q + 32] = z; rowp[q + 48] = z;
+  }
+}
+
+struct PartialPtrs {
+  int* pref;    // [Nq + 1] chunk prefix, then [Nq + 1] = chunks per workgroup
+  float* m;     // [slots, H]  running max, log2 units
+  float* l;     // [slots, H]
+  float* o;     // [slots, H, D]
+};
+
+__host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+__host__ __device__ inline PartialPtrs partial_ptrs(void* ws, int Nq, int H) {
+  PartialPtrs p;
+  char* b = static_cast<char*>(ws);
+  const size_t slots = (size_t)HCA_ATTN_GRID + Nq;
+  const size_t hdr = round256((size_t)(Nq + 2) * 4);
+  const size_t ml = round256(slots * H * 4);
+  p.pref = reinterpret_cast<int*>(b);
+  p.m = reinterpret_cast<float*>(b + hdr);
+  p.l = reinterpret_cast<float*>(b + hdr + ml);
+  p.o = reinterpret_cast<float*>(b + hdr + 2 * ml);
+  return p;
+}
+
+__device__ __forceinline__ int find_query(const int* pref, int nq, int c) {
+  // the query whose chunk range [pref[n], pref[n+1]) holds chunk c
+  int lo = 0, hi = nq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_query) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[KC * kKsPitch];
+  __shared__ __attribute__((aligned(16))) float4 s_sx[8][4][64];
+  __shared__ __attribute__((aligned(16))) __bf16 Pt[8][KC * kPtPitch];
+  __shared__ int32_t s_idx[kIdxWin];
+  __shared__ QInfo s_qi[kMaxDecodeQ];
+  __shared__ int s_pref[kMaxDecodeQ + 1];
+  __shared__ int s_wsum[8];
+  __shared__ double s_inv[32];
+  __shared__ uint8_t s_kval[KC];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int NHG = a.H / 16;
+  const int hg = wave & 3, dh = wave >> 2;
+  const bool active = hg < NHG;
+  const bool csa = a.mode == HCA_MODE_CSA;
+
+  if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr) / kTwoPi;   // turns per position
+  // ---- the chunk list and this workgroup's run [c0, c1)
+  int nq_local, qbase, c0, c1;
+  PartialPtrs pp{};
+  if (per_query) {
+    qbase = blockIdx.x;
+    nq_local = 1;
+    if (tid == 0) {
+      const QInfo qi = query_info(a, qbase);
+      s_qi[0] = qi;
+      s_pref[0] = 0;
+      s_pref[1] = (qi.n_set + KC - 1) / KC;
+    }
+    __syncthreads();
+    c0 = 0;
+    c1 = s_pref[1];
+  } else {
+    qbase = 0;
+    nq_local = a.Nq;
+    int cnt = 0;
+    if (tid < a.Nq) {
+      const QInfo qi = query_info(a, tid);
+      s_qi[tid] = qi;
+      cnt = (qi.n_set + KC - 1) / KC;
+    }
+    int x = cnt;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = hrow0 + i;
-      const size_t base = ((size_t)n * n_splits + split) * a.H + h;
-      if (r == 0) { pp.m[base] = m_run[i]; pp.l[base] = l_run[i]; }
-      float* o = pp.o + base * kD;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    if (tid < a.Nq) s_pref[tid + 1] = base + x;
+    if (tid == 0) s_pref[0] = 0;
+    __syncthreads();
+    const int total = s_pref[a.Nq];
+    int per = (total + gridDim.x - 1) / gridDim.x;
+    if (per < HCA_ATTN_MIN_CHUNKS) per = HCA_ATTN_MIN_CHUNKS;
+    pp = partial_ptrs(a.workspace, a.Nq, a.H);
+    if (blockIdx.x == 0) {
+      for (int i = tid; i <= a.Nq; i += kThreads) pp.pref[i] = s_pref[i];
+      if (tid == 0) pp.pref[a.Nq + 1] = per;
+    }
+    c0 = blockIdx.x * per;
+    c1 = min(c0 + per, total);
+  }
+  if (c0 >= c1) {
+    if (per_query && active) {              // empty set: the sink alone, o = 0
+      const int n = qbase;
+      const int hrow0 = 16 * hg + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) o[16 * dt + r] = acc[dt][i];
+      for (int i = 0; i < 4; ++i) {
+        const int h = hrow0 + i;
+        __bf16* o = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD + 256 * dh;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) o[16 * dt + r] = (__bf16)0.0f;
+        if (a.lse && r == 0 && dh == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
+      }
+    }
+    return;                                 // uniform over the workgroup
+  }
+
+  // index-list window: positions of chunks [cw, cw + kIdxWin / KC) of this run
+  auto fill_idx = [&](int cw) {
+    for (int e = tid; e < kIdxWin; e += kThreads) {
+      const int cc = cw + e / KC;
+      int v = -1;
+      if (cc < c1) {
+        const int nl = per_query ? 0 : find_query(s_pref, nq_local, cc);
+        const int p = (cc - s_pref[nl]) * KC + (e % KC);
+        if (p < s_qi[nl].n_ent) v = a.idx[(int64_t)(qbase + nl) * a.k + p];
+      }
+      s_idx[e] = v;
+    }
+  };
+
+  // staging: this thread's share q of keys kk0 and kk0 + 32
+  const int q16 = tid & 15, kk0 = tid >> 4, kk1 = kk0 + 32;
+  u4* const row0p = reinterpret_cast<u4*>(Ks + kk0 * kKsPitch);
+  u4* const row1p = reinterpret_cast<u4*>(Ks + kk1 * kKsPitch);
+  EntryRegs e0, e1;
+  int idx_win = c0;
+  int ns = per_query ? 0 : find_query(s_pref, nq_local, c0);   // query of the staged chunk
+  int p_st = (c0 - s_pref[ns]) * KC;                              // its first set position
+#define HCA_ISSUE()                                                                            \
+  do {                                                                                         \
+    const QInfo& qs_ = s_qi[ns];                                                               \
+    const int ib_ = (c_st - idx_win) * KC;                                                     \
+    const int j0_ = csa ? s_idx[ib_ + kk0] : 0, j1_ = csa ? s_idx[ib_ + kk1] : 0;              \
+    if (p_st < qs_.n_ent) {                        /* uniform: the chunk holds entries */      \
+      e0 = entry_load(a, qs_, p_st + kk0, j0_, q16, csa);                                      \
+      e1 = entry_load(a, qs_, p_st + kk1, j1_, q16, csa);                                      \
+    } else {                                                                                   \
+      e0.kind = key_kind(qs_, p_st + kk0, j0_, csa);                                           \
+      e1.kind = key_kind(qs_, p_st + kk1, j1_, csa);                                           \
+    }                                                                                          \
+  } while (0)
+#define HCA_COMMIT()                                                                           \
+  do {                                                                                         \
+    const QInfo& qs_ = s_qi[ns];                                                               \
+    key_commit(a, qs_, p_st + kk0, e0, q16, row0p, s_inv);                                     \
+    key_commit(a, qs_, p_st + kk1, e1, q16, row1p, s_inv);                                     \
+    if (q16 == 0) { s_kval[kk0] = e0.kind != kInvalid; s_kval[kk1] = e1.kind != kInvalid; }    \
+    __builtin_amdgcn_s_waitcnt(0x0F70);            /* vmcnt(0): no load of this chunk lingers */ \
+  } while (0)
+
+  if (csa) {
+    fill_idx(c0);
+  }
+  __syncthreads();                                   // s_inv, s_idx
+  int c_st = c0;
+  HCA_ISSUE();
+  HCA_COMMIT();
+
+  // ---- per-query state
+  int nl = ns;
+  v8bf qa[8];
+  v4f acc[16];
+  float m_run[4], l_run[4];
+  const float qscale = a.tau * (float)kLog2e;        // logits in log2 units
+  auto load_q = [&](int nloc) {
+    const int n = qbase + nloc;
+    const int head = 16 * hg + r;
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)n * a.H + head) * kD + 256 * dh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[s] = *reinterpret_cast<const v8bf*>(qrow + 32 * s + 8 * g);
+    if (dh == 1) {
+      // rotate the RoPE pairs (448 + i, 480 + i), i = 8g + e, held in k-steps 6 / 7
+      const int64_t t = s_qi[nloc].t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float c, s;
+        rope_cs(t, s_inv[8 * g + e], &c, &s);
+        const float x0 = (float)qa[6][e], x1 = (float)qa[7][e];
+        qa[6][e] = (__bf16)(x0 * c - x1 * s);
+        qa[7][e] = (__bf16)(x0 * s + x1 * c);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+    // the query is needed at once; waiting here keeps the staging loads that
+    // follow from being waited for at the first QK product
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+  };
+  __syncthreads();                                   // first tile
+  if (active) load_q(nl);
+
+  // per-lane LDS read bases: QK rows 16kt + r at dims 256dh + 8g (+32s);
+  // transposed reads rows 8g + lr (+32ks, +4) at dims 256dh + lc (+16dt)
+  const int lr = r >> 2, lc = 4 * (r & 3);
+  const __bf16* kq_base = Ks + r * kKsPitch + 256 * dh + 8 * g;
+  const __bf16* kv_base = Ks + (8 * g + lr) * kKsPitch + 256 * dh + lc;
+  __bf16* const pt = Pt[wave];
+
+  for (int c = c0; c < c1; ++c) {
+    const bool more = c + 1 < c1;
+    if (more) {
+      c_st = c + 1;
+      while (s_pref[ns + 1] <= c_st) ++ns;           // uniform
+      p_st = (c_st - s_pref[ns]) * KC;
+      if (csa && c_st - idx_win >= kIdxWin / KC) {   // next window of the index list
+        __syncthreads();
+        idx_win = c_st;
+        fill_idx(idx_win);
+        __syncthreads();
+      }
+      HCA_ISSUE();
+    }
+    v4f sc[4];
+    if (active) {
+      // ---- partial logits over this wave's 256 dims: 4 key tiles of 16
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        v4f cacc = {0.f, 0.f, 0.f, 0.f};
+        const __bf16* kr = kq_base + 16 * kt * kKsPitch;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const v8bf kb = *reinterpret_cast<const v8bf*>(kr + 32 * s);
+          cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, cacc, 0, 0, 0);
+        }
+        sc[kt] = cacc;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s_sx[wave][kt][lane] = make_float4(sc[kt][0], sc[kt][1], sc[kt][2], sc[kt][3]);
+    }
+    __syncthreads();
+    if (active) {
+      // full logits S = S_dh0 + S_dh1 (the same sum in both waves), in log2 units;
+      // lane (r, g) holds key 16kt + r of head rows 4g + i
+      float x[4][4];
+      bool need = false;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float4 o4 = s_sx[wave ^ 4][kt][lane];
+        const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+        const bool kv = s_kval[16 * kt + r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float S = dh == 0 ? sc[kt][i] + ov[i] : ov[i] + sc[kt][i];
+          x[kt][i] = kv ? S * qscale : -INFINITY;
+          need |= x[kt][i] > m_run[i] + 8.0f;
+        }
+      }
+      // m_run is a reference maximum per head row: probabilities are
+      // exp2(x - m_run) and o is rescaled only when a logit exceeds the reference
+      // by more than 2^8 (wave-uniform branch); the final normalization makes the
+      // choice of reference exact.
+      if (__builtin_amdgcn_read_exec() & __ballot(need)) {
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float mx = fmaxf(fmaxf(x[0][i], x[1][i]), fmaxf(x[2][i], x[3][i]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          const float m_new = fmaxf(m_run[i], mx);
+          alpha[i] = (m_run[i] == -INFINITY) ? 0.0f : exp2f(m_run[i] - m_new);
+          l_run[i] *= alpha[i];
+          m_run[i] = m_new;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+          acc[dt][0] *= alpha[0]; acc[dt][1] *= alpha[1];
+          acc[dt][2] *= alpha[2]; acc[dt][3] *= alpha[3];
+        }
+      }
+      // P^T in LDS: row = key, this lane's 4 heads in one 8-byte write
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float ev[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ev[i] = (m_run[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[kt][i] - m_run[i]);
+          l_run[i] += ev[i];
+        }
+        *reinterpret_cast<u2*>(pt + (16 * kt + r) * kPtPitch + 4 * g) =
+            (u2){pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3])};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // O += P V over 2 k-steps of 32 keys; both operands by transposed LDS reads
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const __bf16* pb = pt + (32 * ks + 8 * g + lr) * kPtPitch + lc;
+        v4s p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)pb);
+        v4s p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(pb + 4 * kPtPitch));
+        v8bf pa;
+        __builtin_memcpy(&pa, &p0, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&pa) + 8, &p1, 8);
+        const __bf16* vbase = kv_base + 32 * ks * kKsPitch;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+          const __bf16* b0 = vbase + 16 * dt;
+          v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)b0);
+          v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(b0 + 4 * kKsPitch));
+          v8bf vb;
+          __builtin_memcpy(&vb, &t0, 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&vb) + 8, &t1, 8);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+    // ---- end of this query's chunks in the run: finish it
+    const bool last_of_query = !more || s_pref[nl + 1] == c + 1;
+    if (last_of_query) {
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float l = l_run[i];
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+          l_run[i] = l;
+        }
+        const int n = qbase + nl;
+        const int hrow0 = 16 * hg + 4 * g;
+        const bool direct = per_query || (s_pref[nl] >= c0 && s_pref[nl + 1] <= c1);
+        if (direct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = hrow0 + i;
+            const float sig = a.sink[h] * (float)kLog2e;
+            const float M = fmaxf(sig, m_run[i]);
+            const float sc_o = exp2f(m_run[i] - M);
+            const float den = exp2f(sig - M) + l_run[i] * sc_o;
+            const float f = sc_o / den;
+            __bf16* o = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD + 256 * dh;
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt) o[16 * dt + r] = (__bf16)(acc[dt][i] * f);
+            if (a.lse && r == 0 && dh == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
+          }
+        } else {
+          const size_t slot = (size_t)blockIdx.x + n;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = hrow0 + i;
+            const size_t base = slot * a.H + h;
+            if (r == 0 && dh == 0) { pp.m[base] = m_run[i]; pp.l[base] = l_run[i]; }
+            float* o = pp.o + base * kD + 256 * dh;
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt) o[16 * dt + r] = acc[dt][i];
+          }
+        }
+      }
+      if (more) {
+        nl = ns;                                     // the staged chunk's query is next
+        if (active) load_q(nl);
+      }
+    }
+    if (more) {
+      __syncthreads();                     // every wave is done with Ks, Pt, s_sx
+      HCA_COMMIT();
+      __syncthreads();
     }
   }
 }
 
-// merge the slices of one (query, head) in slice order, with the sink
-__global__ void __launch_bounds__(256) combine_kernel(AttnArgs a, int n_splits, int keys_per_split) {
-  __shared__ float s_w[kMaxSplits];
+#undef HCA_ISSUE
+#undef HCA_COMMIT
+
+// merge the runs of one (query, head) in run order, with the sink
+__global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
+  __shared__ float s_w[HCA_ATTN_GRID];
   __shared__ float s_red[4];
   const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const SetInfo si = set_info(a, n);
-  const int n_set = si.n_ent + si.n_w;
-  const int S = (n_set + keys_per_split - 1) / keys_per_split;
-  PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, n_splits, a.H);
-  const size_t base0 = (size_t)n * n_splits * a.H + h;          // + s * H
+  PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H);
+  const int cb = pp.pref[n], ce = pp.pref[n + 1], per = pp.pref[a.Nq + 1];
   const float sig = a.sink[h] * (float)kLog2e;
+  __bf16* out = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD;
+  if (cb == ce) {                          // empty set: the sink alone, o = 0
+    for (int d = tid; d < kD; d += 256) out[d] = (__bf16)0.0f;
+    if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
+    return;
+  }
+  const int w0 = cb / per, w1 = (ce - 1) / per;
+  if (w0 == w1) return;                    // finished by its single run
+  const int S = w1 - w0 + 1;
+  auto slot = [&](int s) { return ((size_t)(w0 + s) + n) * a.H + h; };
   float mx = -INFINITY;
-  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pp.m[base0 + (size_t)s * a.H]);
+  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pp.m[slot(s)]);
   mx = wave_max(mx);
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), sig);
   __syncthreads();
-  for (int s = tid; s < S; s += 256) s_w[s] = exp2f(pp.m[base0 + (size_t)s * a.H] - M);
+  for (int s = tid; s < S; s += 256) s_w[s] = exp2f(pp.m[slot(s)] - M);
   __syncthreads();
-  if (wave == 0) {                     // fixed-order denominator
+  if (wave == 0) {                         // fixed-order denominator
     float l = 0.f;
-    for (int s = lane; s < S; s += 64) l += pp.l[base0 + (size_t)s * a.H] * s_w[s];
+    for (int s = lane; s < S; s += 64) l += pp.l[slot(s)] * s_w[s];
     l = wave_sum(l);
     if (lane == 0) s_red[0] = l;
   }
@@ -468,44 +729,30 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a, int n_splits, 
   const float den = exp2f(sig - M) + s_red[0];
   const float inv = 1.0f / den;
   for (int d = tid; d < kD; d += 256) {
-    float acc = 0.f;
+    float accv = 0.f;
 #pragma unroll 8
-    for (int s = 0; s < S; ++s) acc += pp.o[(base0 + (size_t)s * a.H) * kD + d] * s_w[s];
-    reinterpret_cast<__bf16*>(a.o)[((int64_t)n * a.H + h) * kD + d] = (__bf16)(acc * inv);
+    for (int s = 0; s < S; ++s) accv += pp.o[slot(s) * kD + d] * s_w[s];
+    out[d] = (__bf16)(accv * inv);
   }
   if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
 }
 
-void split_plan(int Nq, int mode, int k, int n_win, int64_t max_visible, int prefill,
-                int* n_splits, int* kps) {
-  int64_t max_set = (mode == HCA_MODE_CSA ? (int64_t)k : max_visible) + n_win;
-  if (max_set < 1) max_set = 1;
-  const int64_t chunks = (max_set + kChunk - 1) / kChunk;
-  // aim at >= 512 workgroups, at least 4 chunks per slice
-  const int64_t nq = Nq > 0 ? Nq : 1;
-  int64_t want = (512 + nq - 1) / nq;
-  int64_t s = want < chunks / 4 ? want : chunks / 4;
-  if (prefill) s = 1;
-  if (s < 1) s = 1;
-  const int64_t max_chunks_per_split = kMaxSplitKeys / kChunk;   // CSA index lists live in LDS
-  if (mode == HCA_MODE_CSA && (chunks + s - 1) / s > max_chunks_per_split)
-    s = (chunks + max_chunks_per_split - 1) / max_chunks_per_split;
-  int64_t per = (chunks + s - 1) / s;
-  if ((chunks + per - 1) / per > kMaxSplits) per = (chunks + kMaxSplits - 1) / kMaxSplits;
-  *kps = (int)(per * kChunk);
-  *n_splits = (int)((max_set + *kps - 1) / *kps);
+// Decode layout: few queries spread over one flattened chunk list (chunk counts
+// must stay far from int overflow); otherwise one workgroup per query.
+bool decode_layout(int Nq, int prefill, int mode, int k, int n_win, int64_t max_visible) {
+  const int64_t n_ent = mode == HCA_MODE_CSA ? (k < max_visible ? (int64_t)k : max_visible) : max_visible;
+  const int64_t chunks = (n_ent + n_win + KC - 1) / KC;
+  return !prefill && Nq <= kMaxDecodeQ && (int64_t)Nq * chunks < (1LL << 30);
 }
 
 }  // namespace
 
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
                                  int64_t max_visible, int io_f32, int prefill) {
-  if (io_f32) return 0;
-  int S, kps;
-  split_plan(Nq, mode, k, n_win, max_visible, prefill, &S, &kps);
-  if (S == 1) return 0;
-  size_t ml = ((size_t)Nq * S * H * 4 + 255) / 256 * 256;
-  return 2 * ml + (size_t)Nq * S * H * D * 4;
+  (void)D;
+  if (io_f32 || !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
+  const size_t slots = (size_t)HCA_ATTN_GRID + Nq;
+  return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + slots * H * kD * 4;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -516,19 +763,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.prof_end) hipEventRecord(a.prof_end, s);
     return hipGetLastError();
   }
-  int S, kps;
-  split_plan(a.Nq, a.mode, a.k, a.n_win, a.max_visible, a.prefill, &S, &kps);
-  const int nw = a.H / 16;
-  dim3 grid(S, a.Nq);
+  const bool dec = decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible);
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
-  switch (nw) {
-    case 1: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, a, S, kps); break;
-    case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, a, S, kps); break;
-    case 3: hipLaunchKernelGGL(attn_bf16_kernel<3>, grid, dim3(192), 0, s, a, S, kps); break;
-    default: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a, S, kps); break;
-  }
+  hipLaunchKernelGGL(attn_mqa_kernel, dim3(dec ? HCA_ATTN_GRID : a.Nq), dim3(kThreads), 0, s, a, dec ? 0 : 1);
   if (a.prof_end) hipEventRecord(a.prof_end, s);
-  if (S > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a, S, kps);
+  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
