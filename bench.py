@@ -82,6 +82,30 @@ def prefill_indexer_flops(prefix, T, H_I=64, d_I=128):
     return pairs * H_I * d_I * 2, pairs
 
 
+# ------------------------------------------------ committed counter evidence
+def committed_traffic(summary="profiles/hbm_counters.ragged_pair_32.md"):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has changed
+    since those counters were taken (or no summary exists)."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, summary)).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        k, _, v = line.strip().partition(": ")
+        if k in ("kernel_source", "kernel_source_sha256", "traffic_bytes_per_launch"):
+            fields[k] = v.strip()
+    try:
+        src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 # ---------------------------------------------------------------- GPU timing
 class Timed:
     def __init__(self, name, layer_sets, prefill=False):
@@ -159,6 +183,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true", help="time the primary workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
     ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -171,6 +197,16 @@ def main():
     import synth
     from synth.configs import config_by_name
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 4}), flush=True)
+        return
 
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
@@ -202,7 +238,7 @@ def main():
             roofline={"bound": "hbm", "kernel": "score_quant_kernel<FP8> (CSA indexer scoring)",
                       "achieved": round(ckeys / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                       "unit": "GB/s", "frac": round(ckeys / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "traffic": None, "algorithmic_bytes_per_launch": ckeys,
+                      "traffic": committed_traffic(), "algorithmic_bytes_per_launch": ckeys,
                       "avg_launch_ms": round(kern_avg, 5)}))
         log(f"[bench] ragged pair: {ms:.4f} ms/step, scoring kernel {kern_avg:.4f} ms")
         del sets
