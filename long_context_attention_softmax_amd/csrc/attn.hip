@@ -545,15 +545,26 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
     if (active) {
       // ---- partial logits over this wave's 256 dims: 4 key tiles of 16
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        v4f cacc = {0.f, 0.f, 0.f, 0.f};
-        const __bf16* kr = kq_base + 16 * kt * kKsPitch;
+      for (int kt = 0; kt < 4; ++kt) sc[kt] = (v4f){0.f, 0.f, 0.f, 0.f};
+      // the reads of k-step s+1 are in flight while k-step s multiplies
+      v8bf kb0[4], kb1[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const v8bf kb = *reinterpret_cast<const v8bf*>(kr + 32 * s);
-          cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, cacc, 0, 0, 0);
+      for (int kt = 0; kt < 4; ++kt) kb0[kt] = *reinterpret_cast<const v8bf*>(kq_base + 16 * kt * kKsPitch);
+#pragma unroll
+      for (int s = 0; s < 8; s += 2) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          kb1[kt] = *reinterpret_cast<const v8bf*>(kq_base + 16 * kt * kKsPitch + 32 * (s + 1));
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb0[kt], sc[kt], 0, 0, 0);
+        if (s + 2 < 8) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            kb0[kt] = *reinterpret_cast<const v8bf*>(kq_base + 16 * kt * kKsPitch + 32 * (s + 2));
         }
-        sc[kt] = cacc;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s + 1], kb1[kt], sc[kt], 0, 0, 0);
       }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s_sx[wave][kt][lane] = make_float4(sc[kt][0], sc[kt][1], sc[kt][2], sc[kt][3]);
@@ -633,6 +644,15 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
           __builtin_memcpy(reinterpret_cast<char*>(&vb) + 8, &t1, 8);
           acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
         }
+        // P^T and the first two V^T tiles, then each product with the reads of the
+        // tile two ahead in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+        for (int dt = 0; dt < 14; ++dt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
       }
     }
     // ---- end of this query's chunks in the run: finish it

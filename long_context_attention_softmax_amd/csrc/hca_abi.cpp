@@ -108,7 +108,7 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
     REQUIRE((int64_t)d->H_I * d->d_I <= 16384, HCA_E_UNSUPPORTED, "F32 indexer needs H_I*d_I <= 16384");
   } else {
     REQUIRE(d->d_I == 128, HCA_E_UNSUPPORTED, "quantized indexer needs d_I = 128 (got %d)", d->d_I);
-    REQUIRE(d->H_I % 16 == 0 && d->H_I <= 64, HCA_E_UNSUPPORTED, "quantized indexer needs H_I in {16,32,48,64}");
+    REQUIRE(d->H_I == 32 || d->H_I == 64, HCA_E_UNSUPPORTED, "quantized indexer needs H_I in {32, 64}");
     REQUIRE(d->max_visible <= 2048LL * 4096, HCA_E_UNSUPPORTED, "quantized indexer supports at most 2^23 visible entries");
   }
   *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt);

@@ -15,10 +15,13 @@
 // scaled FP4 MFMA, exact under the same condition.  (The FP8 MFMA is not used: it
 // sums groups of eight products in a narrower window and can drop low-order bits.)
 // The head sum follows one fixed order - binary32, un-fused:
-//     S_g = (((+0 + t_{h0}) + t_{h1}) + ...) over h = 16T + 4g + i (T asc, i asc)
-//     I   = (S_0 + S_1) + (S_2 + S_3),      t_h = fl(w_h * max(d_h, +0))
-// which is exactly the order the 16x16 MFMA output layout produces: lane (n, g)
-// holds heads 16T + 4g + i of entry n, and two butterfly adds combine the groups.
+//     S_u = (((+0 + t_{h0}) + t_{h1}) + ...) over h = 32T + 8(i / 4) + 4u + (i % 4)
+//           (T ascending, then i = 0..15), for the two halves u = 0, 1
+//     I   = S_0 + S_1,      t_h = fl(w_h * max(d_h, +0))
+// which is exactly the order the 32x32 MFMA output layout produces: lane (j, u)
+// holds heads 32T + 8(i / 4) + 4u + (i % 4) of entry j in register i, and one
+// butterfly add combines the halves.  (32x32 products run at twice the rate of
+// 16x16 ones on this hardware.)
 //
 // Selection: exact radix select on the orderable 32-bit key of each score, lower
 // index first among equal scores, output in ascending index order.
@@ -125,71 +128,82 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 }
 
 // -------------------------------------------------------- quantized operands
-constexpr int kTilesPerWave = 8;                         // 8 x 16 entries per wave
-constexpr int kEntriesPerWG2 = 4 * 16 * kTilesPerWave;   // 512
+constexpr int kTilesPerWave = 4;                         // 4 x 32 entries per wave
+constexpr int kEntriesPerWG2 = 4 * 32 * kTilesPerWave;   // 512
 
-// One workgroup scores 512 consecutive entries of one query; each wave owns 128
-// entries (eight 16-entry MFMA tiles) and issues all their key loads before the
-// first MFMA.  Rows of the MFMA are indexer heads, columns entries.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Lane (j, u) = (lane % 32, lane / 32) of a 32-entry tile.  FP8: it holds bytes
+// [64u, 64u + 64) of entry j's key and, per k-step s of the BF16 32x32x16 product,
+// dims 64u + 8s .. 64u + 8s + 7; the query rows use the same dims.  MXFP4: it holds
+// the 32-element blocks u and 2 + u (k-steps 0 and 1 of the scaled 32x32x64
+// product).  Every head dot is the exact sum over all 128 dims either way.
 template <int FMT>
 __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
   __shared__ uint32_t s_hist[kBins];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g = lane >> 4;
+  const int jl = lane & 31, u = lane >> 5;
   const int n = blockIdx.y;
   const int64_t V = visible(a, n);
   const int64_t ebase = (int64_t)blockIdx.x * kEntriesPerWG2;
   if (ebase >= V) return;                               // uniform over the workgroup
   const int64_t row0 = a.cache_row_start[a.seq_id[n]];
-  const int64_t wbase = ebase + wave * 16 * kTilesPerWave;
+  const int64_t wbase = ebase + wave * 32 * kTilesPerWave;
 
-  // key loads for all tiles of this wave first (lane (r, g): entry r, bytes of group g)
-  uint4 kr0[kTilesPerWave], kr1[kTilesPerWave];
-  int ks[kTilesPerWave];
+  // key loads for all tiles of this wave first
+  uint4 kr[kTilesPerWave][4];
+  int ks[kTilesPerWave][2];
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t j = wbase + 16 * t + r;
-    kr0[t] = make_uint4(0, 0, 0, 0);
-    kr1[t] = make_uint4(0, 0, 0, 0);
-    ks[t] = 127;
+    const int64_t j = wbase + 32 * t + jl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kr[t][q] = make_uint4(0, 0, 0, 0);
+    ks[t][0] = ks[t][1] = 127;
     if (j < V) {
+      const char* key = a.keys + (row0 + j) * a.key_pitch;
       if (FMT == HCA_FP8_E4M3) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 32 * g);
-        kr0[t] = p[0];
-        kr1[t] = p[1];
+        const uint4* p = reinterpret_cast<const uint4*>(key + 64 * u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kr[t][q] = p[q];
       } else {
-        kr0[t] = *reinterpret_cast<const uint4*>(a.keys + (row0 + j) * a.key_pitch + 16 * g);
-        ks[t] = a.key_scales[(row0 + j) * a.key_scale_pitch + g];
+        kr[t][0] = *reinterpret_cast<const uint4*>(key + 16 * u);
+        kr[t][1] = *reinterpret_cast<const uint4*>(key + 32 + 16 * u);
+        const uint8_t* kscl = a.key_scales + (row0 + j) * a.key_scale_pitch;
+        ks[t][0] = kscl[u];
+        ks[t][1] = kscl[2 + u];
       }
     }
   }
   for (int i = tid; i < kBins; i += kScoreThreads) s_hist[i] = 0;
 
-  const int HT = a.H_I / 16;                            // head tiles (<= 4)
-  v8bf qa[4][4];
-  v8i qf4[4];
-  int qs[4];
-  float wv[4][4];
+  const int HT = a.H_I / 32;                            // head tiles (<= 2)
+  v8bf qa[2][8];
+  v8i qf4[2][2];
+  int qs[2][2];
+  float wv[2][16];
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
+  for (int T = 0; T < 2; ++T) {
     if (T < HT) {
-      const int64_t qr = (int64_t)n * a.H_I + 16 * T + r;
+      const int64_t qr = (int64_t)n * a.H_I + 32 * T + jl;
       if (FMT == HCA_FP8_E4M3) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 32 * g);
-        uint4 u0 = p[0], u1 = p[1];
-        qa[T][0] = fp8x8_to_bf16(u0.x, u0.y);
-        qa[T][1] = fp8x8_to_bf16(u0.z, u0.w);
-        qa[T][2] = fp8x8_to_bf16(u1.x, u1.y);
-        qa[T][3] = fp8x8_to_bf16(u1.z, u1.w);
+        const uint4* p = reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 64 * u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = p[q];
+          qa[T][2 * q] = fp8x8_to_bf16(v.x, v.y);
+          qa[T][2 * q + 1] = fp8x8_to_bf16(v.z, v.w);
+        }
       } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 16 * g);
-        v8i v = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        qf4[T] = v;
-        qs[T] = a.q_scales[qr * a.q_scale_pitch + g];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const uint4 v = *reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 32 * s2 + 16 * u);
+          qf4[T][s2] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          qs[T][s2] = a.q_scales[qr * a.q_scale_pitch + 2 * s2 + u];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[T][i] = a.w[(int64_t)n * a.H_I + 16 * T + 4 * g + i];
+      for (int i = 0; i < 16; ++i) wv[T][i] = a.w[(int64_t)n * a.H_I + 32 * T + 8 * (i >> 2) + 4 * u + (i & 3)];
     }
   }
   __syncthreads();
@@ -197,46 +211,52 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
   float* sc = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t j = wbase + 16 * t + r;
-    v4f acc[4];
+    const int64_t j = wbase + 32 * t + jl;
+    v16f acc[2];
     if (FMT == HCA_FP8_E4M3) {
-      v8bf kb[4] = {fp8x8_to_bf16(kr0[t].x, kr0[t].y), fp8x8_to_bf16(kr0[t].z, kr0[t].w),
-                    fp8x8_to_bf16(kr1[t].x, kr1[t].y), fp8x8_to_bf16(kr1[t].z, kr1[t].w)};
+      v8bf kb[8];
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
+      for (int q = 0; q < 4; ++q) {
+        kb[2 * q] = fp8x8_to_bf16(kr[t][q].x, kr[t][q].y);
+        kb[2 * q + 1] = fp8x8_to_bf16(kr[t][q].z, kr[t][q].w);
+      }
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
         if (T < HT) {
-          v4f c = {0.f, 0.f, 0.f, 0.f};
+          v16f c = {};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s2], kb[s2], c, 0, 0, 0);
+          for (int s2 = 0; s2 < 8; ++s2) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[T][s2], kb[s2], c, 0, 0, 0);
           acc[T] = c;
         }
       }
     } else {
-      v8i kv = {(int)kr0[t].x, (int)kr0[t].y, (int)kr0[t].z, (int)kr0[t].w, 0, 0, 0, 0};
+      const v8i kv0 = {(int)kr[t][0].x, (int)kr[t][0].y, (int)kr[t][0].z, (int)kr[t][0].w, 0, 0, 0, 0};
+      const v8i kv1 = {(int)kr[t][1].x, (int)kr[t][1].y, (int)kr[t][1].z, (int)kr[t][1].w, 0, 0, 0, 0};
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
+      for (int T = 0; T < 2; ++T) {
         if (T < HT) {
-          v4f c = {0.f, 0.f, 0.f, 0.f};
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf4[T], kv, c, 4, 4, 0, qs[T], 0, ks[t]);
+          v16f c = {};
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][0], kv0, c, 4, 4, 0, qs[T][0], 0, ks[t][0]);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][1], kv1, c, 4, 4, 0, qs[T][1], 0, ks[t][1]);
+          acc[T] = c;
         }
       }
     }
-    // canonical head sum
+    // canonical head sum: this lane's 16 heads per tile, tiles in order, then halves
     float S = 0.0f;
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
+    for (int T = 0; T < 2; ++T) {
       if (T < HT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 16; ++i) {
           const float d = acc[T][i];
           const float term = wv[T][i] * (d > 0.0f ? d : 0.0f);
           S = S + term;
         }
       }
     }
-    S = S + __shfl_xor(S, 16, 64);
     S = S + __shfl_xor(S, 32, 64);
-    if (g == 0 && j < V) {
+    if (u == 0 && j < V) {
       sc[j] = S;
       atomicAdd(&s_hist[float_key(S) >> 21], 1u);
     }

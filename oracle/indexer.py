@@ -17,9 +17,9 @@ exact binary32 number (products of the element grids are exact and the sums stay
 within 24 bits), so d is computed exactly here and checked to be so.  The head
 sum is then defined in binary32, un-fused, in one canonical order:
     term_h = fl32(w_h * max(d_h, +0))
-    S_g    = (((+0 + term_{h0}) + term_{h1}) + ...) over h = 16T + 4g + i,
-             T ascending, then i = 0..3 ascending           (g = 0..3)
-    I      = (S_0 + S_1) + (S_2 + S_3)
+    S_u    = (((+0 + term_{h0}) + term_{h1}) + ...) over h = 32T + 8(i//4) + 4u + i%4,
+             T ascending, then i = 0..15 ascending          (u = 0, 1)
+    I      = S_0 + S_1
 f32 operands (the tiny workload): everything in fp64, sequential over dims, then
 over heads ascending, un-fused.
 """
@@ -64,22 +64,21 @@ def mxfp4_grain(scales: np.ndarray) -> np.ndarray:
 
 def score_canonical_f32(d: np.ndarray, w: np.ndarray) -> np.ndarray:
     """I[j] (float32) from exact head dots d [H_I, V] and weights w [H_I], in the
-    canonical order above.  H_I must be a multiple of 16."""
+    canonical order above.  H_I must be a multiple of 32."""
     H_I, V = d.shape
-    assert H_I % 16 == 0
+    assert H_I % 32 == 0
     w32 = np.asarray(w, np.float32)
     relu = np.where(d > 0, d, 0.0).astype(np.float32)
     S = []
-    for g in range(4):
+    for u in range(2):
         acc = np.zeros(V, np.float32)
-        for T in range(H_I // 16):
-            for i in range(4):
-                h = 16 * T + 4 * g + i
+        for T in range(H_I // 32):
+            for i in range(16):
+                h = 32 * T + 8 * (i // 4) + 4 * u + i % 4
                 term = np.multiply(w32[h], relu[h], dtype=np.float32)
                 acc = np.add(acc, term, dtype=np.float32)
         S.append(acc)
-    return np.add(np.add(S[0], S[1], dtype=np.float32), np.add(S[2], S[3], dtype=np.float32),
-                  dtype=np.float32)
+    return np.add(S[0], S[1], dtype=np.float32)
 
 
 def score_f64(q: np.ndarray, k: np.ndarray, w: np.ndarray) -> np.ndarray:

@@ -141,6 +141,7 @@ def run_layer(lay, g, queries=None, pooled=None):
     out_o = np.zeros((len(qs), g.H, g.D))
     out_lse = np.zeros((len(qs), g.H))
     out_idx = np.full((len(qs), g.topk), -1, np.int64) if lay.mode == "csa" else None
+    out_sel = np.zeros((len(qs), g.topk)) if lay.mode == "csa" else None
     gaps = []
     for n, qi in enumerate(qs):
         t, b = int(lay.q_pos[qi]), int(lay.seq_id[qi])
@@ -149,6 +150,7 @@ def run_layer(lay, g, queries=None, pooled=None):
             I = scores_for_query(cache, lay, g, qi, t, b)
             sel = topk.select(I, g.topk)
             out_idx[n] = sel
+            out_sel[n, sel >= 0] = I[sel[sel >= 0]]
             gaps.append(topk.kth_gap(I, g.topk))
             js = sel[sel >= 0]
         else:
@@ -158,4 +160,5 @@ def run_layer(lay, g, queries=None, pooled=None):
         keys = np.concatenate([ent, win], axis=0)
         qh = attend.query_hat(query_values(lay, qi), t, g.D_r, g.rope_base)
         out_o[n], out_lse[n] = attend.attend(qh, keys, lay.sink, g.tau)
-    return dict(pooled=pooled, idx=out_idx, o=out_o, lse=out_lse, queries=qs, kth_gaps=gaps)
+    return dict(pooled=pooled, idx=out_idx, sel_scores=out_sel, o=out_o, lse=out_lse, queries=qs,
+                kth_gaps=gaps)

@@ -99,6 +99,16 @@ def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, che
         for n in range(len(qs)):
             assert np.array_equal(got_idx[n], ref["idx"][n]), \
                 f"top-k set differs for query {qs[n]} (t={lay.q_pos[qs[n]]})"
+        if check_scores:
+            # the scores behind the selection: bit-exact on the quantized paths
+            # (exact dots, one canonical head sum), fp64 on the f32 path
+            got_sc = to_np(score)[qs].astype(np.float64)
+            want = ref["sel_scores"]
+            if dev.f32:
+                np.testing.assert_allclose(got_sc, want, rtol=1e-12, atol=0)
+            else:
+                assert np.array_equal(got_sc, want), \
+                    f"selected scores differ: max |diff| {np.abs(got_sc - want).max():.3e}"
     got_o = to_np(o)[qs]
     got_o = got_o.astype(np.float64) if dev.f32 else bf16_values(got_o)
     err = row_rel_err(got_o, ref["o"])

@@ -106,6 +106,7 @@ def test_indexer_validation_and_workspace():
     assert call("hca_indexer_topk", d) == -6
     assert call("hca_indexer_topk", idx_desc(d_I=64)) == -5
     assert call("hca_indexer_topk", idx_desc(H_I=20)) == -5
+    assert call("hca_indexer_topk", idx_desc(H_I=48)) == -5          # 32x32 head tiles
     assert call("hca_indexer_topk", idx_desc(k=0)) == -2
     d = idx_desc()
     d.keys.fmt = A.MXFP4

@@ -92,3 +92,37 @@ def test_repeat_runs_bit_identical(gpu):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a, b)
+
+
+def _tied_layer(seed, B, L):
+    """CSA decode layer whose head weights are all zero: every visible entry scores
+    +0, so the top-k is decided by the lower-index rule alone."""
+    w = synth.csa_decode(seed=seed, B=B, L=L)
+    lay = w.layers[0]
+    lay.w = np.zeros_like(lay.w)
+    return lay, w.g
+
+
+def test_select_all_tied_within_candidate_list(gpu):
+    # V = 4096 per query: every key equals the k-th key; the tie set fits the list
+    lay, g = _tied_layer(15, 2, 16384)
+    _print("select: all scores tied, V=4096")
+    ref, dev, _ = run_and_compare(lay, g)
+    assert np.array_equal(to_np(dev.idx), np.tile(np.arange(g.topk, dtype=np.int32), (2, 1)))
+
+
+def test_select_all_tied_beyond_candidate_list(gpu):
+    # V = 16384 > the candidate capacity: resolved from the scores themselves
+    lay, g = _tied_layer(16, 1, 65536)
+    _print("select: all scores tied, V=16384")
+    ref, dev, _ = run_and_compare(lay, g)
+    assert np.array_equal(to_np(dev.idx)[0], np.arange(g.topk, dtype=np.int32))
+
+
+def test_select_large_k(gpu):
+    # k above the fused select's limit takes the three-phase path
+    from dataclasses import replace
+    g = replace(synth.FULL_GEOMETRY, topk=3000)
+    w = synth.csa_decode(seed=17, B=2, L=32768, g=g)
+    _print("select: k=3000, V=8192")
+    run_and_compare(w.layers[0], g)
