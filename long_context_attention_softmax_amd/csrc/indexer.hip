@@ -128,8 +128,15 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 }
 
 // -------------------------------------------------------- quantized operands
-constexpr int kTilesPerWave = 4;                         // 4 x 32 entries per wave
-constexpr int kEntriesPerWG2 = 4 * 32 * kTilesPerWave;   // 512
+#ifndef HCA_SCORE_TPW
+#define HCA_SCORE_TPW 8
+#endif
+#ifndef HCA_SCORE_RING
+#define HCA_SCORE_RING 2
+#endif
+constexpr int kTilesPerWave = HCA_SCORE_TPW;             // 32-entry tiles per wave
+constexpr int kRing = HCA_SCORE_RING;                    // tiles in flight per wave
+constexpr int kEntriesPerWG2 = 4 * 32 * kTilesPerWave;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -151,35 +158,36 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
   const int64_t row0 = a.cache_row_start[a.seq_id[n]];
   const int64_t wbase = ebase + wave * 32 * kTilesPerWave;
 
-  // key loads for all tiles of this wave first
-  uint4 kr[kTilesPerWave][4];
-  int ks[kTilesPerWave][2];
+  // keys stream through a ring of kRing tiles per wave: tile t + kRing is loaded
+  // as soon as tile t has been widened, so kRing - 1 tiles stay in flight while
+  // one is multiplied
+  uint4 kr[kRing][4];
+  int ks[kRing][2];
+  // Lanes past the last visible entry load the last one instead (branch-free, so
+  // the load counters stay exact); a column of the product depends on its own
+  // key only, and those columns are never stored.
+  auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2]) {
+    const int64_t j = min(wbase + 32 * t + jl, V - 1);
+    const char* key = a.keys + (row0 + j) * a.key_pitch;
+    if (FMT == HCA_FP8_E4M3) {
+      const uint4* p = reinterpret_cast<const uint4*>(key + 64 * u);
 #pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t j = wbase + 32 * t + jl;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kr[t][q] = make_uint4(0, 0, 0, 0);
-    ks[t][0] = ks[t][1] = 127;
-    if (j < V) {
-      const char* key = a.keys + (row0 + j) * a.key_pitch;
-      if (FMT == HCA_FP8_E4M3) {
-        const uint4* p = reinterpret_cast<const uint4*>(key + 64 * u);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kr[t][q] = p[q];
-      } else {
-        kr[t][0] = *reinterpret_cast<const uint4*>(key + 16 * u);
-        kr[t][1] = *reinterpret_cast<const uint4*>(key + 32 + 16 * u);
-        const uint8_t* kscl = a.key_scales + (row0 + j) * a.key_scale_pitch;
-        ks[t][0] = kscl[u];
-        ks[t][1] = kscl[2 + u];
-      }
+      for (int q = 0; q < 4; ++q) dst[q] = p[q];
+    } else {
+      dst[0] = *reinterpret_cast<const uint4*>(key + 16 * u);
+      dst[1] = *reinterpret_cast<const uint4*>(key + 32 + 16 * u);
+      const uint8_t* kscl = a.key_scales + (row0 + j) * a.key_scale_pitch;
+      dsc[0] = kscl[u];
+      dsc[1] = kscl[2 + u];
     }
-  }
+  };
   for (int i = tid; i < kBins; i += kScoreThreads) s_hist[i] = 0;
 
+  // Query rows and weights are all requested first (raw), then the first kRing
+  // key tiles in tile order (the scheduling barriers keep that order), so that
+  // waiting for the query or for tile t never waits for a later tile.
   const int HT = a.H_I / 32;                            // head tiles (<= 2)
-  v8bf qa[2][8];
-  v8i qf4[2][2];
+  uint4 qraw[2][4];
   int qs[2][2];
   float wv[2][16];
 #pragma unroll
@@ -189,21 +197,40 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
       if (FMT == HCA_FP8_E4M3) {
         const uint4* p = reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 64 * u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = p[q];
-          qa[T][2 * q] = fp8x8_to_bf16(v.x, v.y);
-          qa[T][2 * q + 1] = fp8x8_to_bf16(v.z, v.w);
-        }
+        for (int q = 0; q < 4; ++q) qraw[T][q] = p[q];
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const uint4 v = *reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 32 * s2 + 16 * u);
-          qf4[T][s2] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          qraw[T][s2] = *reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 32 * s2 + 16 * u);
           qs[T][s2] = a.q_scales[qr * a.q_scale_pitch + 2 * s2 + u];
         }
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) wv[T][i] = a.w[(int64_t)n * a.H_I + 32 * T + 8 * (i >> 2) + 4 * u + (i & 3)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < kRing; ++t) {
+    if (t < kTilesPerWave) load_tile(t, kr[t], ks[t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v8bf qa[2][8];
+  v8i qf4[2][2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    if (T < HT) {
+      if (FMT == HCA_FP8_E4M3) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          qa[T][2 * q] = fp8x8_to_bf16(qraw[T][q].x, qraw[T][q].y);
+          qa[T][2 * q + 1] = fp8x8_to_bf16(qraw[T][q].z, qraw[T][q].w);
+        }
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          qf4[T][s2] = (v8i){(int)qraw[T][s2].x, (int)qraw[T][s2].y, (int)qraw[T][s2].z, (int)qraw[T][s2].w, 0, 0, 0, 0};
+      }
     }
   }
   __syncthreads();
@@ -212,14 +239,18 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
     const int64_t j = wbase + 32 * t + jl;
+    const int slot = t % kRing;
     v16f acc[2];
     if (FMT == HCA_FP8_E4M3) {
       v8bf kb[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        kb[2 * q] = fp8x8_to_bf16(kr[t][q].x, kr[t][q].y);
-        kb[2 * q + 1] = fp8x8_to_bf16(kr[t][q].z, kr[t][q].w);
+        kb[2 * q] = fp8x8_to_bf16(kr[slot][q].x, kr[slot][q].y);
+        kb[2 * q + 1] = fp8x8_to_bf16(kr[slot][q].z, kr[slot][q].w);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + kRing < kTilesPerWave) load_tile(t + kRing, kr[slot], ks[slot]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         if (T < HT) {
@@ -230,14 +261,18 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
         }
       }
     } else {
-      const v8i kv0 = {(int)kr[t][0].x, (int)kr[t][0].y, (int)kr[t][0].z, (int)kr[t][0].w, 0, 0, 0, 0};
-      const v8i kv1 = {(int)kr[t][1].x, (int)kr[t][1].y, (int)kr[t][1].z, (int)kr[t][1].w, 0, 0, 0, 0};
+      const v8i kv0 = {(int)kr[slot][0].x, (int)kr[slot][0].y, (int)kr[slot][0].z, (int)kr[slot][0].w, 0, 0, 0, 0};
+      const v8i kv1 = {(int)kr[slot][1].x, (int)kr[slot][1].y, (int)kr[slot][1].z, (int)kr[slot][1].w, 0, 0, 0, 0};
+      const int ks0 = ks[slot][0], ks1 = ks[slot][1];
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + kRing < kTilesPerWave) load_tile(t + kRing, kr[slot], ks[slot]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         if (T < HT) {
           v16f c = {};
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][0], kv0, c, 4, 4, 0, qs[T][0], 0, ks[t][0]);
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][1], kv1, c, 4, 4, 0, qs[T][1], 0, ks[t][1]);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][0], kv0, c, 4, 4, 0, qs[T][0], 0, ks0);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][1], kv1, c, 4, 4, 0, qs[T][1], 0, ks1);
           acc[T] = c;
         }
       }
