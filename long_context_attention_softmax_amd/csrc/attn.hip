@@ -37,11 +37,10 @@ struct SetInfo {
   int n_w;           // window tokens
 };
 
-__device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
+// everything but the first cache row, from the query position alone
+__device__ __forceinline__ SetInfo set_info_pos(const AttnArgs& a, int64_t t) {
   SetInfo si;
-  const int b = a.seq_id[n];
-  const int64_t t = a.q_pos[n];
-  si.row0 = a.cache_row_start[b];
+  si.row0 = 0;
   int64_t V = (t + 1) / a.m;
   if (V > a.max_visible) V = a.max_visible;
   si.V = V;
@@ -51,6 +50,12 @@ __device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
   si.u0 = t - a.n_win + 1 > 0 ? t - a.n_win + 1 : 0;
   si.n_w = (int)(t - si.u0 + 1);
   if (a.n_win == 0) si.n_w = 0;
+  return si;
+}
+
+__device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
+  SetInfo si = set_info_pos(a, a.q_pos[n]);
+  si.row0 = a.cache_row_start[a.seq_id[n]];
   return si;
 }
 
@@ -214,6 +219,22 @@ struct QInfo {
   int pad;
 };
 
+// the query record without its first cache row (row0 = 0), for sequence b
+__device__ __forceinline__ QInfo query_info_pos(const AttnArgs& a, int n, int b) {
+  QInfo qi;
+  const int64_t t = a.q_pos[n];
+  const SetInfo si = set_info_pos(a, t);
+  qi.row0 = 0;
+  qi.u0 = si.u0;
+  qi.t = t;
+  qi.V = si.V;
+  qi.n_ent = si.n_ent;
+  qi.n_set = si.n_ent + si.n_w;
+  qi.b = b;
+  qi.pad = 0;
+  return qi;
+}
+
 __device__ __forceinline__ QInfo query_info(const AttnArgs& a, int n) {
   QInfo qi;
   const SetInfo si = set_info(a, n);
@@ -368,7 +389,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
   const bool active = hg < NHG;
   const bool csa = a.mode == HCA_MODE_CSA;
 
-  if (tid < 32) s_inv[tid] = pow(a.rope_base, -2.0 * tid / kDr) / kTwoPi;   // turns per position
+  if (tid < 32) s_inv[tid] = a.inv_turn[tid];       // turns per position
   // ---- the chunk list and this workgroup's run [c0, c1)
   int nq_local, qbase, c0, c1;
   PartialPtrs pp{};
@@ -387,9 +408,14 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
   } else {
     qbase = 0;
     nq_local = a.Nq;
+    // the chunk counts need only the positions; the dependent cache-row load is
+    // in flight during the scan and stored with the rest of the query record
     int cnt = 0;
+    int64_t row0 = 0;
     if (tid < a.Nq) {
-      const QInfo qi = query_info(a, tid);
+      const int b = a.seq_id[tid];
+      row0 = a.cache_row_start[b];
+      QInfo qi = query_info_pos(a, tid, b);
       s_qi[tid] = qi;
       cnt = (qi.n_set + KC - 1) / KC;
     }
@@ -416,6 +442,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
     }
     c0 = blockIdx.x * per;
     c1 = min(c0 + per, total);
+    if (tid < a.Nq) s_qi[tid].row0 = row0;
   }
   if (c0 >= c1) {
     if (per_query && active) {              // empty set: the sink alone, o = 0
@@ -480,10 +507,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
   if (csa) {
     fill_idx(c0);
   }
-  __syncthreads();                                   // s_inv, s_idx
-  int c_st = c0;
-  HCA_ISSUE();
-  HCA_COMMIT();
+  __syncthreads();                                   // s_inv, s_idx, s_qi
 
   // ---- per-query state
   int nl = ns;
@@ -491,12 +515,16 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
   v4f acc[16];
   float m_run[4], l_run[4];
   const float qscale = a.tau * (float)kLog2e;        // logits in log2 units
-  auto load_q = [&](int nloc) {
+  // the query's rows are requested early (in flight with key loads) and rotated
+  // and made current once they have arrived
+  auto q_issue = [&](int nloc) {
     const int n = qbase + nloc;
     const int head = 16 * hg + r;
     const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)n * a.H + head) * kD + 256 * dh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qa[s] = *reinterpret_cast<const v8bf*>(qrow + 32 * s + 8 * g);
+  };
+  auto q_finish = [&](int nloc) {
     if (dh == 1) {
       // rotate the RoPE pairs (448 + i, 480 + i), i = 8g + e, held in k-steps 6 / 7
       const int64_t t = s_qi[nloc].t;
@@ -513,12 +541,13 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
     for (int dt = 0; dt < 16; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
-    // the query is needed at once; waiting here keeps the staging loads that
-    // follow from being waited for at the first QK product
-    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
   };
+  int c_st = c0;
+  HCA_ISSUE();
+  if (active) q_issue(nl);                           // in flight with the first chunk's keys
+  HCA_COMMIT();                                      // (waits for both)
+  if (active) q_finish(nl);
   __syncthreads();                                   // first tile
-  if (active) load_q(nl);
 
   // per-lane LDS read bases: QK rows 16kt + r at dims 256dh + 8g (+32s);
   // transposed reads rows 8g + lr (+32ks, +4) at dims 256dh + lc (+16dt)
@@ -569,6 +598,8 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s_sx[wave][kt][lane] = make_float4(sc[kt][0], sc[kt][1], sc[kt][2], sc[kt][3]);
     }
+    const bool last_of_query = !more || s_pref[nl + 1] == c + 1;
+    if (more && last_of_query && active) q_issue(ns);  // the next query's rows, in flight from here
     __syncthreads();
     if (active) {
       // full logits S = S_dh0 + S_dh1 (the same sum in both waves), in log2 units;
@@ -656,7 +687,6 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
       }
     }
     // ---- end of this query's chunks in the run: finish it
-    const bool last_of_query = !more || s_pref[nl + 1] == c + 1;
     if (last_of_query) {
       if (active) {
 #pragma unroll
@@ -696,14 +726,14 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
           }
         }
       }
-      if (more) {
-        nl = ns;                                     // the staged chunk's query is next
-        if (active) load_q(nl);
-      }
     }
     if (more) {
       __syncthreads();                     // every wave is done with Ks, Pt, s_sx
-      HCA_COMMIT();
+      HCA_COMMIT();                        // (also waits for the next query's rows)
+      if (last_of_query) {
+        nl = ns;                           // the staged chunk's query is next
+        if (active) q_finish(nl);
+      }
       __syncthreads();
     }
   }
@@ -778,15 +808,15 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Nq == 0) return hipSuccess;
   if (a.io_f32) {
-    if (a.prof_begin) hipEventRecord(a.prof_begin, s);
+    if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
-    if (a.prof_end) hipEventRecord(a.prof_end, s);
+    if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
     return hipGetLastError();
   }
   const bool dec = decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible);
-  if (a.prof_begin) hipEventRecord(a.prof_begin, s);
+  if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
   hipLaunchKernelGGL(attn_mqa_kernel, dim3(dec ? HCA_ATTN_GRID : a.Nq), dim3(kThreads), 0, s, a, dec ? 0 : 1);
-  if (a.prof_end) hipEventRecord(a.prof_end, s);
+  if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
   if (dec) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // C ABI of the hybrid compressed-attention library: host-side argument checks,
 // workspace sizing and kernel dispatch.  Every check runs before anything is
 // launched, so argument errors never touch the device.
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -203,6 +204,8 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   a.Nq = d->Nq; a.H = d->H; a.D = d->D; a.D_r = d->D_r; a.mode = d->mode; a.m = d->m;
   a.k = d->mode == HCA_MODE_CSA ? d->k : 0; a.n_win = d->n_win; a.win_cap = d->win_cap;
   a.io_f32 = d->io_fmt == HCA_F32; a.tau = d->tau; a.rope_base = d->rope_base;
+  // RoPE frequencies of the 32 pairs in turns per position, formed once here in fp64
+  for (int i = 0; i < 32; ++i) a.inv_turn[i] = std::pow(d->rope_base, -2.0 * i / 64.0) / (2.0 * M_PI);
   a.max_visible = d->max_visible; a.q = d->q; a.cache_fmt = d->cache.fmt;
   a.c_f32 = static_cast<const char*>(d->cache.f32); a.c_f32_pitch = d->cache.f32_pitch;
   a.c_nope = static_cast<const char*>(d->cache.nope); a.c_nope_pitch = d->cache.nope_pitch;

@@ -59,6 +59,7 @@ struct AttnArgs {
   void* workspace;
   int prefill;
   hipEvent_t prof_begin, prof_end;    // optional, around the attention kernel
+  double inv_turn[32];                // BF16 path: rope_base^(-2i/64) / (2 pi), turns per position
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
