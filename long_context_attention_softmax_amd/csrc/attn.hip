@@ -343,7 +343,7 @@ struct PartialPtrs {
   int* pref;    // [Nq + 1] chunk prefix, then [Nq + 1] = chunks per workgroup
   float* m;     // [slots, H]  running max, log2 units
   float* l;     // [slots, H]
-  float* o;     // [slots, H, D]
+  __bf16* o;    // [slots, H, D]  o / l of the run (0 where l = 0)
 };
 
 __host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -357,7 +357,7 @@ __host__ __device__ inline PartialPtrs partial_ptrs(void* ws, int Nq, int H) {
   p.pref = reinterpret_cast<int*>(b);
   p.m = reinterpret_cast<float*>(b + hdr);
   p.l = reinterpret_cast<float*>(b + hdr + ml);
-  p.o = reinterpret_cast<float*>(b + hdr + 2 * ml);
+  p.o = reinterpret_cast<__bf16*>(b + hdr + 2 * ml);
   return p;
 }
 
@@ -720,9 +720,10 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
             const int h = hrow0 + i;
             const size_t base = slot * a.H + h;
             if (r == 0 && dh == 0) { pp.m[base] = m_run[i]; pp.l[base] = l_run[i]; }
-            float* o = pp.o + base * kD + 256 * dh;
+            const float f = l_run[i] > 0.0f ? 1.0f / l_run[i] : 0.0f;
+            __bf16* o = pp.o + base * kD + 256 * dh;
 #pragma unroll
-            for (int dt = 0; dt < 16; ++dt) o[16 * dt + r] = acc[dt][i];
+            for (int dt = 0; dt < 16; ++dt) o[16 * dt + r] = (__bf16)(acc[dt][i] * f);
           }
         }
       }
@@ -742,10 +743,12 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
 #undef HCA_ISSUE
 #undef HCA_COMMIT
 
-// merge the runs of one (query, head) in run order, with the sink
+// merge the runs of one (query, head) in run order, with the sink: run s holds
+// (m_s, l_s, o_s / l_s), so o = sum_s w_s (o_s / l_s) / (e^(sigma - M) + sum_s w_s)
+// with w_s = 2^(m_s - M) l_s
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   __shared__ float s_w[HCA_ATTN_GRID];
-  __shared__ float s_red[4];
+  __shared__ float s_red[8];
   const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H);
   const int cb = pp.pref[n], ce = pp.pref[n + 1], per = pp.pref[a.Nq + 1];
@@ -758,32 +761,32 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   }
   const int w0 = cb / per, w1 = (ce - 1) / per;
   if (w0 == w1) return;                    // finished by its single run
-  const int S = w1 - w0 + 1;
-  auto slot = [&](int s) { return ((size_t)(w0 + s) + n) * a.H + h; };
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pp.m[slot(s)]);
-  mx = wave_max(mx);
+  const int S = w1 - w0 + 1;               // <= the number of workgroups (one thread each)
+  const size_t slot0 = ((size_t)w0 + n) * a.H + h, sstride = (size_t)a.H;
+  float m = -INFINITY, l = 0.0f;
+  if (tid < S) { m = pp.m[slot0 + tid * sstride]; l = pp.l[slot0 + tid * sstride]; }
+  const float mx = wave_max(m);
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), sig);
+  const float w = tid < S ? exp2f(m - M) * l : 0.0f;
+  if (tid < S) s_w[tid] = w;
+  const float ws = wave_sum(w);            // fixed-order denominator
+  if (lane == 0) s_red[4 + wave] = ws;
   __syncthreads();
-  for (int s = tid; s < S; s += 256) s_w[s] = exp2f(pp.m[slot(s)] - M);
-  __syncthreads();
-  if (wave == 0) {                         // fixed-order denominator
-    float l = 0.f;
-    for (int s = lane; s < S; s += 64) l += pp.l[slot(s)] * s_w[s];
-    l = wave_sum(l);
-    if (lane == 0) s_red[0] = l;
-  }
-  __syncthreads();
-  const float den = exp2f(sig - M) + s_red[0];
+  const float den = exp2f(sig - M) + ((s_red[4] + s_red[5]) + (s_red[6] + s_red[7]));
   const float inv = 1.0f / den;
-  for (int d = tid; d < kD; d += 256) {
-    float accv = 0.f;
+  // thread t: dims 2t, 2t + 1 of every run's row
+  const uint32_t* po = reinterpret_cast<const uint32_t*>(pp.o + slot0 * kD) + tid;
+  const size_t ostride = sstride * kD / 2;
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll 8
-    for (int s = 0; s < S; ++s) accv += pp.o[slot(s) * kD + d] * s_w[s];
-    out[d] = (__bf16)(accv * inv);
+  for (int s = 0; s < S; ++s) {
+    const uint32_t v = po[s * ostride];
+    a0 += bf16_to_f32((uint16_t)v) * s_w[s];
+    a1 += bf16_to_f32((uint16_t)(v >> 16)) * s_w[s];
   }
+  reinterpret_cast<uint32_t*>(out)[tid] = pack_bf16x2(a0 * inv, a1 * inv);
   if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
 }
 
@@ -802,7 +805,7 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
   (void)D;
   if (io_f32 || !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
   const size_t slots = (size_t)HCA_ATTN_GRID + Nq;
-  return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + slots * H * kD * 4;
+  return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + slots * H * kD * 2;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
