@@ -390,6 +390,19 @@ __device__ int find_digit(const uint32_t* hist, int nbins, uint32_t* need, uint3
   return d;
 }
 
+// 16 consecutive scores of a 4096-entry chunk per thread (4 aligned 16-byte loads;
+// the score rows are padded to a multiple of 64, so no load passes the row)
+constexpr int kPerThread1 = kChunk1 / 256;
+__device__ __forceinline__ void load_chunk_keys(const float* sc, int64_t jt, int64_t j1, uint32_t (&key)[kPerThread1]) {
+#pragma unroll
+  for (int v = 0; v < kPerThread1 / 4; ++v) {
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jt + 4 * v < j1) f = *reinterpret_cast<const float4*>(sc + jt + 4 * v);
+    key[4 * v] = float_key(f.x); key[4 * v + 1] = float_key(f.y);
+    key[4 * v + 2] = float_key(f.z); key[4 * v + 3] = float_key(f.w);
+  }
+}
+
 __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ uint32_t s_ck[kChunk1];
@@ -403,23 +416,29 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   const int64_t K = V < a.k ? V : a.k;
   const int64_t j0 = (int64_t)c * kChunk1;
   if (V <= K || j0 >= V) return;
+  // the scores do not depend on the threshold digit: request them first
+  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
+  const int64_t jt = j0 + (int64_t)kPerThread1 * tid;
+  uint32_t key[kPerThread1];
+  load_chunk_keys(sc, jt, j1, key);
   const uint32_t* gh = a.hist + (int64_t)n * kBins;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
   if (tid == 0) s_n = 0;
   __syncthreads();
   uint32_t need = (uint32_t)K;
   const uint32_t d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
-  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
-  const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
   uint32_t gt = 0;
-  for (int64_t j = j0 + tid; j < j1; j += 256) {
-    const uint32_t key = float_key(sc[j]);
-    const uint32_t dg = key >> 21;
-    gt += dg > d1;
-    if (dg == d1) {
-      const uint32_t p = atomicAdd(&s_n, 1u);           // LDS: at most kChunk1 per chunk
-      s_ck[p] = key;
-      s_cj[p] = (int32_t)j;
+#pragma unroll
+  for (int e = 0; e < kPerThread1; ++e) {
+    if (jt + e < j1) {
+      const uint32_t dg = key[e] >> 21;
+      gt += dg > d1;
+      if (dg == d1) {
+        const uint32_t p = atomicAdd(&s_n, 1u);           // LDS: at most kChunk1 per chunk
+        s_ck[p] = key[e];
+        s_cj[p] = (int32_t)(jt + e);
+      }
     }
   }
   uint32_t tot;
@@ -457,6 +476,9 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
   }
   const int nch = (int)((V + kChunk1 - 1) / kChunk1);
   const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  uint32_t gtc[2];                                      // chunks 2t, 2t + 1: keys above digit d1
+#pragma unroll
+  for (int e = 0; e < 2; ++e) gtc[e] = 2 * tid + e < nch ? ws.chunk_gt[(int64_t)n * ws.nch + 2 * tid + e] : 0;
   const uint32_t* gh = a.hist + (int64_t)n * kBins;
   for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = gh[i];
   for (int i = tid; i < nch; i += kSelectThreads) { s_selc[i] = 0; s_eqc[i] = 0; }
@@ -513,15 +535,30 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t off = 0, eqb = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-      ws.out_off[(int64_t)n * ws.nch + ch] = off;
-      ws.eq_before[(int64_t)n * ws.nch + ch] = eqb;
-      const uint32_t eq_keep = eqb >= take_eq ? 0 : (s_eqc[ch] < take_eq - eqb ? s_eqc[ch] : take_eq - eqb);
-      off += ws.chunk_gt[(int64_t)n * ws.nch + ch] + s_selc[ch] + eq_keep;
-      eqb += s_eqc[ch];
+  // output offsets in chunk order: a chunk keeps its keys above digit d1, its
+  // candidates above T and the equal keys that earlier chunks left to take
+  // (thread t: chunks 2t, 2t + 1; two block scans)
+  uint32_t eqc[2], keep[2], eqb[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) eqc[e] = 2 * tid + e < nch ? s_eqc[2 * tid + e] : 0;
+  uint32_t tot;
+  eqb[0] = block_exclusive_scan<kSelectThreads>(eqc[0] + eqc[1], s_wave, &tot);
+  eqb[1] = eqb[0] + eqc[0];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t left = eqb[e] >= take_eq ? 0 : take_eq - eqb[e];
+    keep[e] = 2 * tid + e < nch ? gtc[e] + s_selc[2 * tid + e] + (eqc[e] < left ? eqc[e] : left) : 0;
+  }
+  const uint32_t off0 = block_exclusive_scan<kSelectThreads>(keep[0] + keep[1], s_wave, &tot);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int ch = 2 * tid + e;
+    if (ch < nch) {
+      ws.out_off[(int64_t)n * ws.nch + ch] = e ? off0 + keep[0] : off0;
+      ws.eq_before[(int64_t)n * ws.nch + ch] = eqb[e];
     }
+  }
+  if (tid == 0) {
     ws.state[2 * n] = T;
     ws.state[2 * n + 1] = take_eq;
   }
@@ -549,35 +586,35 @@ __global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectW
     return;
   }
   if (j0 >= V) return;
-  const uint32_t T = ws.state[2 * n], take_eq = ws.state[2 * n + 1];
-  uint32_t pos_base = ws.out_off[(int64_t)n * ws.nch + c];
-  uint32_t eqb = ws.eq_before[(int64_t)n * ws.nch + c];
+  // the scores first (independent of the threshold), then the chunk's offsets
   const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
-  uint32_t run_sel = 0;
-  for (int64_t base = j0; base < j1; base += 4 * 256) {
-    const int64_t jt = base + 4 * (int64_t)tid;
-    uint32_t kk[4];
-    uint32_t ngt = 0, neq = 0;
+  const int64_t jt = j0 + (int64_t)kPerThread1 * tid;
+  uint32_t key[kPerThread1];
+  load_chunk_keys(sc, jt, j1, key);
+  const uint32_t T = ws.state[2 * n], take_eq = ws.state[2 * n + 1];
+  const uint32_t pos_base = ws.out_off[(int64_t)n * ws.nch + c];
+  const uint32_t eqb = ws.eq_before[(int64_t)n * ws.nch + c];
+  uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kk[e] = 0;
-      if (jt + e < j1) {
-        kk[e] = float_key(sc[jt + e]);
-        ngt += kk[e] > T;
-        neq += kk[e] == T;
-      }
+  for (int e = 0; e < kPerThread1; ++e) {
+    if (jt + e < j1) {
+      ngt += key[e] > T;
+      neq += key[e] == T;
     }
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan<256>(ngt | (neq << 16), s_wave, &tot);
-    uint32_t gt_before = pre & 0xFFFF;
-    uint32_t eq_before = eqb + (pre >> 16);
+  }
+  // counts of this thread's predecessors in the chunk (16 bits each suffice: <= 4096)
+  uint32_t tot;
+  const uint32_t pre = block_exclusive_scan<256>(ngt | (neq << 16), s_wave, &tot);
+  uint32_t gt_before = pre & 0xFFFF;
+  uint32_t eq_before = eqb + (pre >> 16);
+  const uint32_t eq_taken0 = eqb < take_eq ? eqb : take_eq;     // equal keys taken before the chunk
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (jt + e >= j1) break;
-      const bool is_gt = kk[e] > T, is_eq = kk[e] == T;
-      const uint32_t eq_sel_before = (eq_before < take_eq ? eq_before : take_eq) - (eqb < take_eq ? eqb : take_eq);
+  for (int e = 0; e < kPerThread1; ++e) {
+    if (jt + e < j1) {
+      const bool is_gt = key[e] > T, is_eq = key[e] == T;
       if (is_gt || (is_eq && eq_before < take_eq)) {
-        const uint32_t pos = pos_base + run_sel + gt_before + eq_sel_before;
+        const uint32_t eq_sel_before = (eq_before < take_eq ? eq_before : take_eq) - eq_taken0;
+        const uint32_t pos = pos_base + gt_before + eq_sel_before;
         if (pos < (uint32_t)K) {
           out[pos] = (int32_t)(jt + e);
           if (so) so[(int64_t)n * a.k + pos] = sc[jt + e];
@@ -586,11 +623,6 @@ __global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectW
       gt_before += is_gt;
       eq_before += is_eq;
     }
-    // selected in this tile: all above T plus the kept equal keys
-    const uint32_t tile_eq_end = eqb + (tot >> 16);
-    const uint32_t kept_eq = (tile_eq_end < take_eq ? tile_eq_end : take_eq) - (eqb < take_eq ? eqb : take_eq);
-    run_sel += (tot & 0xFFFF) + kept_eq;
-    eqb = tile_eq_end;
   }
 }
 
