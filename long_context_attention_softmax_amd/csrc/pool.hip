@@ -81,6 +81,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   __shared__ double s_party[4][kMaxDI];
   __shared__ double s_red[kPoolThreads / 64];
   __shared__ double s_bamax[kMaxDI / 32];
+  __shared__ double s_rc[kMaxD / 2], s_rs[kMaxD / 2];   // RoPE cos / sin at the entry's position
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = blockIdx.x;
@@ -119,7 +120,9 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
     }
   }
   __syncthreads();
-  // softmax over the block (wave 0)
+  // softmax over the block (wave 0); meanwhile the other waves form the rotation
+  // of the entry's RoPE slice (half-split pairs i, half + i) at its last position
+  const int half = a.D_r / 2, D_n = a.D - a.D_r;
   if (wave == 0) {
     double mx = -INFINITY;
     for (int i = lane; i < a.m; i += 64) mx = fmax(mx, s_z[i]);
@@ -128,6 +131,14 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
     for (int i = lane; i < a.m; i += 64) { double e = exp(s_z[i] - mx); s_z[i] = e; sum += e; }
     sum = wave_sum(sum);
     for (int i = lane; i < a.m; i += 64) s_z[i] = s_z[i] / sum;
+  } else {
+    for (int i = tid - 64; i < half; i += kPoolThreads - 64) {
+      const double inv = pow(a.rope_base, -2.0 * (double)i / (double)a.D_r);
+      double sn, cs;
+      sincos((double)p_last * inv, &sn, &cs);
+      s_rc[i] = cs;
+      s_rs[i] = sn;
+    }
   }
   __syncthreads();
   // weighted sums: per-wave partials over interleaved tokens, merged in wave order
@@ -142,11 +153,8 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
       s_y[d] = ((s_party[0][d] + s_party[1][d]) + s_party[2][d]) + s_party[3][d];
   __syncthreads();
   // half-split RoPE of the entry's slice at the block's last position
-  const int half = a.D_r / 2, D_n = a.D - a.D_r;
   for (int i = tid; i < half; i += kPoolThreads) {
-    double inv = pow(a.rope_base, -2.0 * (double)i / (double)a.D_r);
-    double sn, cs;
-    sincos((double)p_last * inv, &sn, &cs);
+    const double cs = s_rc[i], sn = s_rs[i];
     double x0 = s_c[D_n + i], x1 = s_c[D_n + half + i];
     s_c[D_n + i] = x0 * cs - x1 * sn;
     s_c[D_n + half + i] = x0 * sn + x1 * cs;
