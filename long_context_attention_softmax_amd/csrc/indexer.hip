@@ -145,10 +145,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // dims 64u + 8s .. 64u + 8s + 7; the query rows use the same dims.  MXFP4: it holds
 // the 32-element blocks u and 2 + u (k-steps 0 and 1 of the scaled 32x32x64
 // product).  Every head dot is the exact sum over all 128 dims either way.
+#ifndef HCA_SCORE_WAVES
+#define HCA_SCORE_WAVES 2                                // waves per SIMD the registers allow
+#endif
 template <int FMT>
-__global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs a) {
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(HCA_SCORE_WAVES)))
+score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
   __shared__ uint32_t s_hist[kBins];
+  __shared__ v8bf s_qa[2][8][64];                        // FP8 path: widened query operands, per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, u = lane >> 5;
   const int n = blockIdx.y;
@@ -195,9 +200,11 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
     if (T < HT) {
       const int64_t qr = (int64_t)n * a.H_I + 32 * T + jl;
       if (FMT == HCA_FP8_E4M3) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 64 * u);
+        if (wave == 0) {                                 // widened once, into LDS, for all waves
+          const uint4* p = reinterpret_cast<const uint4*>(a.q + qr * a.q_pitch + 64 * u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) qraw[T][q] = p[q];
+          for (int q = 0; q < 4; ++q) qraw[T][q] = p[q];
+        }
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -215,16 +222,17 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
     if (t < kTilesPerWave) load_tile(t, kr[t], ks[t]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  v8bf qa[2][8];
   v8i qf4[2][2];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     if (T < HT) {
       if (FMT == HCA_FP8_E4M3) {
+        if (wave == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          qa[T][2 * q] = fp8x8_to_bf16(qraw[T][q].x, qraw[T][q].y);
-          qa[T][2 * q + 1] = fp8x8_to_bf16(qraw[T][q].z, qraw[T][q].w);
+          for (int q = 0; q < 4; ++q) {
+            s_qa[T][2 * q][lane] = fp8x8_to_bf16(qraw[T][q].x, qraw[T][q].y);
+            s_qa[T][2 * q + 1][lane] = fp8x8_to_bf16(qraw[T][q].z, qraw[T][q].w);
+          }
         }
       } else {
 #pragma unroll
@@ -256,7 +264,7 @@ __global__ void __launch_bounds__(kScoreThreads) score_quant_kernel(IndexerArgs 
         if (T < HT) {
           v16f c = {};
 #pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[T][s2], kb[s2], c, 0, 0, 0);
+          for (int s2 = 0; s2 < 8; ++s2) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s_qa[T][s2][lane], kb[s2], c, 0, 0, 0);
           acc[T] = c;
         }
       }
