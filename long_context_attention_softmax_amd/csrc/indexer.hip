@@ -129,14 +129,19 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 
 // -------------------------------------------------------- quantized operands
 #ifndef HCA_SCORE_TPW
-#define HCA_SCORE_TPW 8
+#define HCA_SCORE_TPW 8                                   // FP8 keys (decode: few queries)
+#endif
+#ifndef HCA_SCORE_TPW4
+#define HCA_SCORE_TPW4 32                                 // MXFP4 keys (prefill: many queries)
 #endif
 #ifndef HCA_SCORE_RING
 #define HCA_SCORE_RING 2
 #endif
-constexpr int kTilesPerWave = HCA_SCORE_TPW;             // 32-entry tiles per wave
+// 32-entry tiles per wave: fewer, larger workgroups amortize the per-workgroup
+// query/weight loads and histogram traffic when there are thousands of queries
+template <int FMT> constexpr int tiles_per_wave() { return FMT == HCA_MXFP4 ? HCA_SCORE_TPW4 : HCA_SCORE_TPW; }
+template <int FMT> constexpr int entries_per_wg() { return 4 * 32 * tiles_per_wave<FMT>(); }
 constexpr int kRing = HCA_SCORE_RING;                    // tiles in flight per wave
-constexpr int kEntriesPerWG2 = 4 * 32 * kTilesPerWave;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -146,9 +151,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // the 32-element blocks u and 2 + u (k-steps 0 and 1 of the scaled 32x32x64
 // product).  Every head dot is the exact sum over all 128 dims either way.
 #ifndef HCA_SCORE_WAVES
-#define HCA_SCORE_WAVES 2                                // waves per SIMD the registers allow
+#define HCA_SCORE_WAVES 3                                // waves per SIMD the registers allow
 #endif
-template <int FMT>
+// Workgroup order.  Chunk-major (XQ = false): the chunks of one query run together,
+// so concurrent workgroups stream one contiguous key range (queries of different
+// sequences touch different ranges).  XCD-major (XQ = true): linear workgroup L runs
+// on XCD L mod 8; XCD x takes queries x, x + 8, ... and walks the entry chunks in
+// order with its queries fastest, so a chunk of a shared key cache is read from
+// memory once per XCD and then served by that XCD's L2 to all of its queries.
+#ifndef HCA_SCORE_XCD_MAJOR
+#define HCA_SCORE_XCD_MAJOR 1
+#endif
+template <int FMT, bool XQ>
 __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(HCA_SCORE_WAVES)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
@@ -156,9 +170,21 @@ score_quant_kernel(IndexerArgs a) {
   __shared__ v8bf s_qa[2][8][64];                        // FP8 path: widened query operands, per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, u = lane >> 5;
-  const int n = blockIdx.y;
+  int n;
+  int64_t chunk;
+  if (XQ) {
+    const int64_t L = blockIdx.x, r = L >> 3;
+    const int64_t nper = ((int64_t)a.Nq + 7) >> 3;
+    n = (int)(8 * (r % nper) + (L & 7));
+    chunk = r / nper;
+    if (n >= a.Nq) return;                              // uniform over the workgroup
+  } else {
+    n = blockIdx.y;
+    chunk = blockIdx.x;
+  }
   const int64_t V = visible(a, n);
-  const int64_t ebase = (int64_t)blockIdx.x * kEntriesPerWG2;
+  constexpr int kTilesPerWave = tiles_per_wave<FMT>();
+  const int64_t ebase = chunk * entries_per_wg<FMT>();
   if (ebase >= V) return;                               // uniform over the workgroup
   const int64_t row0 = a.cache_row_start[a.seq_id[n]];
   const int64_t wbase = ebase + wave * 32 * kTilesPerWave;
@@ -292,8 +318,12 @@ score_quant_kernel(IndexerArgs a) {
       if (T < HT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+          // max(d, +0) of a finite dot; with MXFP4 keys (ALU-bound) as one integer
+          // max of its bits (a negative float, -0 included, is a negative integer),
+          // which needs no NaN canonicalization; both give the same bits
           const float d = acc[T][i];
-          const float term = wv[T][i] * (d > 0.0f ? d : 0.0f);
+          const float r = FMT == HCA_MXFP4 ? __int_as_float(max(__float_as_int(d), 0)) : (d > 0.0f ? d : 0.0f);
+          const float term = wv[T][i] * r;
           S = S + term;
         }
       }
@@ -700,13 +730,17 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
-  const int64_t chunks = (a.max_visible + kEntriesPerWG2 - 1) / kEntriesPerWG2;
+  const int64_t epw = a.fmt == HCA_MXFP4 ? entries_per_wg<HCA_MXFP4>() : entries_per_wg<HCA_FP8_E4M3>();
+  const int64_t chunks = (a.max_visible + epw - 1) / epw;
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
     if (a.fmt == HCA_FP8_E4M3)
-      hipLaunchKernelGGL(score_quant_kernel<HCA_FP8_E4M3>, dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
+      hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false>), dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
+    else if (HCA_SCORE_XCD_MAJOR)
+      hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true>), dim3((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8))),
+                         dim3(kScoreThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(score_quant_kernel<HCA_MXFP4>, dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
+      hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false>), dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
   dim3 cgrid((unsigned)L.nch, a.Nq);
