@@ -162,7 +162,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #ifndef HCA_SCORE_XCD_MAJOR
 #define HCA_SCORE_XCD_MAJOR 1
 #endif
-template <int FMT, bool XQ>
+template <int FMT, bool XQ, int HT>
 __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(HCA_SCORE_WAVES)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
@@ -217,7 +217,7 @@ score_quant_kernel(IndexerArgs a) {
   // Query rows and weights are all requested first (raw), then the first kRing
   // key tiles in tile order (the scheduling barriers keep that order), so that
   // waiting for the query or for tile t never waits for a later tile.
-  const int HT = a.H_I / 32;                            // head tiles (<= 2)
+  // HT = H_I / 32 head tiles (1 or 2), a template argument so the tile loop has no branches
   uint4 qraw[2][4];
   int qs[2][2];
   float wv[2][16];
@@ -734,13 +734,18 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   const int64_t chunks = (a.max_visible + epw - 1) / epw;
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
-    if (a.fmt == HCA_FP8_E4M3)
-      hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false>), dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
-    else if (HCA_SCORE_XCD_MAJOR)
-      hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true>), dim3((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8))),
-                         dim3(kScoreThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false>), dim3((unsigned)chunks, a.Nq), dim3(kScoreThreads), 0, s, a);
+    const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
+    const bool h2 = a.H_I == 64;
+    if (a.fmt == HCA_FP8_E4M3) {
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 2>), g2, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 1>), g2, dim3(kScoreThreads), 0, s, a);
+    } else if (HCA_SCORE_XCD_MAJOR) {
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 2>), gx, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 1>), gx, dim3(kScoreThreads), 0, s, a);
+    } else {
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2>), g2, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1>), g2, dim3(kScoreThreads), 0, s, a);
+    }
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
   dim3 cgrid((unsigned)L.nch, a.Nq);
