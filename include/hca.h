@@ -174,6 +174,9 @@ typedef struct hca_kv_compress_desc {
  * scores in the same order (f32, or f64 for F32 operands).
  * max_visible must bound V for every query.  q and keys share `fmt`; `q` has
  * Nq*H_I rows (row n*H_I + h).  w is [Nq, H_I] f32 with w >= 0.
+ * Quantized keys: max_visible <= 2^23, and max_visible times the key (and, for
+ * MXFP4, key-scale) pitch must stay below 2^32 bytes; otherwise
+ * HCA_E_UNSUPPORTED.
  */
 typedef struct hca_indexer_topk_desc {
   uint32_t struct_size;

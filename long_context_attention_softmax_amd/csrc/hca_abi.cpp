@@ -128,6 +128,11 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
   if (fmt == HCA_MXFP4)
     REQUIRE(d->q.scales && d->keys.scales && d->q.scale_pitch >= 4 && d->keys.scale_pitch >= 4, HCA_E_NULL,
             "MXFP4 q/keys need scale planes");
+  if (fmt != HCA_F32) {   // the scoring kernel addresses a sequence's key rows with 32-bit offsets
+    REQUIRE(d->keys.pitch * d->max_visible < (1LL << 32) &&
+            (fmt != HCA_MXFP4 || d->keys.scale_pitch * d->max_visible < (1LL << 32)),
+            HCA_E_UNSUPPORTED, "max_visible x key pitch must be < 2^32 bytes");
+  }
   REQUIRE(aligned(d->w, 4) && aligned(d->idx, 4) && aligned(d->cache_row_start, 8) && aligned(d->q_pos, 8) &&
           aligned(d->seq_id, 4), HCA_E_ALIGN, "w/idx/cache_row_start/q_pos/seq_id misaligned");
   REQUIRE(d->workspace && d->workspace_bytes >= *ws, HCA_E_WORKSPACE, "workspace needs %zu bytes, got %zu",

@@ -197,9 +197,15 @@ score_quant_kernel(IndexerArgs a) {
   // Lanes past the last visible entry load the last one instead (branch-free, so
   // the load counters stay exact); a column of the product depends on its own
   // key only, and those columns are never stored.
+  // Rows are addressed by 32-bit byte offsets from the sequence's first row
+  // (entries < 2^23 and max_visible x pitch < 2^32, checked by the caller), so a
+  // tile costs one full-rate 24-bit multiply per plane.
+  const char* const kseq = a.keys + row0 * a.key_pitch;
+  const uint8_t* const sseq = FMT == HCA_MXFP4 ? a.key_scales + row0 * a.key_scale_pitch : nullptr;
+  const uint32_t j0 = (uint32_t)(wbase + jl), jmax = (uint32_t)(V - 1);
   auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2]) {
-    const int64_t j = min(wbase + 32 * t + jl, V - 1);
-    const char* key = a.keys + (row0 + j) * a.key_pitch;
+    const uint32_t j = min(j0 + 32u * (uint32_t)t, jmax);
+    const char* key = kseq + (size_t)__umul24(j, (uint32_t)a.key_pitch);
     if (FMT == HCA_FP8_E4M3) {
       const uint4* p = reinterpret_cast<const uint4*>(key + 64 * u);
 #pragma unroll
@@ -207,7 +213,7 @@ score_quant_kernel(IndexerArgs a) {
     } else {
       dst[0] = *reinterpret_cast<const uint4*>(key + 16 * u);
       dst[1] = *reinterpret_cast<const uint4*>(key + 32 + 16 * u);
-      const uint8_t* kscl = a.key_scales + (row0 + j) * a.key_scale_pitch;
+      const uint8_t* kscl = sseq + (size_t)__umul24(j, (uint32_t)a.key_scale_pitch);
       dsc[0] = kscl[u];
       dsc[1] = kscl[2 + u];
     }
@@ -331,7 +337,10 @@ score_quant_kernel(IndexerArgs a) {
     S = S + __shfl_xor(S, 32, 64);
     if (u == 0 && j < V) {
       sc[j] = S;
-      atomicAdd(&s_hist[float_key(S) >> 21], 1u);
+      // first digit of float_key(S): S is never -0 (each half-sum starts from +0,
+      // and a sum is -0 only if both addends are), so the sign flip needs no case
+      const uint32_t b = __float_as_uint(S);
+      atomicAdd(&s_hist[(b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 21], 1u);
     }
   }
   __syncthreads();

@@ -122,6 +122,10 @@ def test_indexer_validation_and_workspace():
     d.q.data = FAKE + 8
     d.workspace, d.workspace_bytes = FAKE, 1 << 30
     assert call("hca_indexer_topk", d) == -3
+    d = idx_desc(max_visible=1 << 23)
+    d.keys.pitch = 1024                     # 2^23 rows x 1 KiB: past the 32-bit row offsets
+    assert call("hca_indexer_topk", d) == -5
+    assert b"2^32" in A.lib.hca_last_error()
     assert call("hca_indexer_topk", idx_desc(Nq=0)) == 0
 
 
