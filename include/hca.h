@@ -102,6 +102,7 @@ typedef struct hca_kv_planes {
  *   fmt HCA_F32:      data [rows, d_I] float
  *   fmt HCA_FP8_E4M3: data [rows, d_I] E4M3 codes, per-tensor scale 1
  *   fmt HCA_MXFP4:    data [rows, d_I/2] packed E2M1, scales [rows, d_I/32] E8M0
+ *                     (indexer keys: scale rows 4-byte aligned, else HCA_E_ALIGN)
  */
 typedef struct hca_idx_planes {
   int32_t fmt;

@@ -125,9 +125,12 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
     REQUIRE(aligned(d->q.data, 4) && aligned(d->keys.data, 4) && d->q.pitch % 4 == 0 && d->keys.pitch % 4 == 0,
             HCA_E_ALIGN, "f32 q/keys need 4-byte aligned rows");
   }
-  if (fmt == HCA_MXFP4)
+  if (fmt == HCA_MXFP4) {
     REQUIRE(d->q.scales && d->keys.scales && d->q.scale_pitch >= 4 && d->keys.scale_pitch >= 4, HCA_E_NULL,
             "MXFP4 q/keys need scale planes");
+    REQUIRE(aligned(d->keys.scales, 4) && d->keys.scale_pitch % 4 == 0, HCA_E_ALIGN,
+            "MXFP4 key scale rows must be 4-byte aligned");
+  }
   if (fmt != HCA_F32) {   // the scoring kernel addresses a sequence's key rows with 32-bit offsets
     REQUIRE(d->keys.pitch * d->max_visible < (1LL << 32) &&
             (fmt != HCA_MXFP4 || d->keys.scale_pitch * d->max_visible < (1LL << 32)),

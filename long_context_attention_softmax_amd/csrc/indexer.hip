@@ -151,7 +151,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // the 32-element blocks u and 2 + u (k-steps 0 and 1 of the scaled 32x32x64
 // product).  Every head dot is the exact sum over all 128 dims either way.
 #ifndef HCA_SCORE_WAVES
-#define HCA_SCORE_WAVES 3                                // waves per SIMD the registers allow
+#define HCA_SCORE_WAVES 4                                // MXFP4: waves per SIMD the registers allow
 #endif
 // Workgroup order.  Chunk-major (XQ = false): the chunks of one query run together,
 // so concurrent workgroups stream one contiguous key range (queries of different
@@ -163,7 +163,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #define HCA_SCORE_XCD_MAJOR 1
 #endif
 template <int FMT, bool XQ, int HT>
-__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(HCA_SCORE_WAVES)))
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
   __shared__ uint32_t s_hist[kBins];
@@ -203,19 +203,22 @@ score_quant_kernel(IndexerArgs a) {
   const char* const kseq = a.keys + row0 * a.key_pitch;
   const uint8_t* const sseq = FMT == HCA_MXFP4 ? a.key_scales + row0 * a.key_scale_pitch : nullptr;
   const uint32_t j0 = (uint32_t)(wbase + jl), jmax = (uint32_t)(V - 1);
+  const uint32_t lane_off = FMT == HCA_FP8_E4M3 ? 64u * u : 16u * u;
+  // MXFP4: the entry's four E8M0 block scales are one aligned 32-bit word; shifted
+  // by 8u, its bytes 0 and 2 are this lane's blocks u and 2 + u, which the scaled
+  // product selects with op_sel
   auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2]) {
     const uint32_t j = min(j0 + 32u * (uint32_t)t, jmax);
-    const char* key = kseq + (size_t)__umul24(j, (uint32_t)a.key_pitch);
+    const char* key = kseq + (uint32_t)((uint32_t)__umul24(j, (uint32_t)a.key_pitch) + lane_off);
     if (FMT == HCA_FP8_E4M3) {
-      const uint4* p = reinterpret_cast<const uint4*>(key + 64 * u);
+      const uint4* p = reinterpret_cast<const uint4*>(key);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = p[q];
     } else {
-      dst[0] = *reinterpret_cast<const uint4*>(key + 16 * u);
-      dst[1] = *reinterpret_cast<const uint4*>(key + 32 + 16 * u);
-      const uint8_t* kscl = sseq + (size_t)__umul24(j, (uint32_t)a.key_scale_pitch);
-      dsc[0] = kscl[u];
-      dsc[1] = kscl[2 + u];
+      dst[0] = *reinterpret_cast<const uint4*>(key);
+      dst[1] = *reinterpret_cast<const uint4*>(key + 32);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(sseq + (uint32_t)__umul24(j, (uint32_t)a.key_scale_pitch));
+      dsc[0] = (int)(w >> (8 * u));
     }
   };
   for (int i = tid; i < kBins; i += kScoreThreads) s_hist[i] = 0;
@@ -278,7 +281,7 @@ score_quant_kernel(IndexerArgs a) {
   float* sc = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t j = wbase + 32 * t + jl;
+    const uint32_t j = j0 + 32u * (uint32_t)t;
     const int slot = t % kRing;
     v16f acc[2];
     if (FMT == HCA_FP8_E4M3) {
@@ -303,7 +306,7 @@ score_quant_kernel(IndexerArgs a) {
     } else {
       const v8i kv0 = {(int)kr[slot][0].x, (int)kr[slot][0].y, (int)kr[slot][0].z, (int)kr[slot][0].w, 0, 0, 0, 0};
       const v8i kv1 = {(int)kr[slot][1].x, (int)kr[slot][1].y, (int)kr[slot][1].z, (int)kr[slot][1].w, 0, 0, 0, 0};
-      const int ks0 = ks[slot][0], ks1 = ks[slot][1];
+      const int ksw = ks[slot][0];
       __builtin_amdgcn_sched_barrier(0);
       if (t + kRing < kTilesPerWave) load_tile(t + kRing, kr[slot], ks[slot]);
       __builtin_amdgcn_sched_barrier(0);
@@ -311,8 +314,8 @@ score_quant_kernel(IndexerArgs a) {
       for (int T = 0; T < 2; ++T) {
         if (T < HT) {
           v16f c = {};
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][0], kv0, c, 4, 4, 0, qs[T][0], 0, ks0);
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][1], kv1, c, 4, 4, 0, qs[T][1], 0, ks1);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][0], kv0, c, 4, 4, 0, qs[T][0], 0, ksw);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf4[T][1], kv1, c, 4, 4, 0, qs[T][1], 2, ksw);
           acc[T] = c;
         }
       }
@@ -335,8 +338,8 @@ score_quant_kernel(IndexerArgs a) {
       }
     }
     S = S + __shfl_xor(S, 32, 64);
-    if (u == 0 && j < V) {
-      sc[j] = S;
+    if (u == 0 && j < (uint32_t)V) {
+      *reinterpret_cast<float*>(reinterpret_cast<char*>(sc) + (uint32_t)(4u * j)) = S;   // scalar base + 32-bit offset
       // first digit of float_key(S): S is never -0 (each half-sum starts from +0,
       // and a sum is -0 only if both addends are), so the sign flip needs no case
       const uint32_t b = __float_as_uint(S);
