@@ -165,10 +165,10 @@ typedef struct hca_kv_compress_desc {
  *   d_h   = q[n, h] . key[j]                        (exact)
  *   I_j   = sum_h w[n, h] * max(d_h, 0)
  * Quantized operands (FP8 or MXFP4, same format for q and keys; d_I = 128,
- * H_I = 32 or 64): d_h is exact in binary32, and I_j is summed in binary32,
- * un-fused, as S_0 + S_1 where S_u adds, from +0, the terms
- * fl(w_h * max(d_h, +0)) of heads h = 32T + 8(i / 4) + 4u + (i % 4) in order
- * T = 0, 1, then i = 0..15.  F32 operands: dots and the head sum in fp64,
+ * H_I = 32 or 64): d_h is exact in binary32, and I_j = fl(S_0 + S_1) where S_u
+ * starts at +0 and takes, for heads h = 32T + 8(i / 4) + 4u + (i % 4) in order
+ * T = 0, 1, then i = 0..15, S_u = fl(w_h * max(d_h, +0) + S_u) (binary32, one
+ * rounding per head: a fused multiply-add).  F32 operands: dots and the head sum in fp64,
  * sequential, un-fused (V <= 4096 per query).
  * Output: idx[n, 0..k) = the min(k, V) entries with the largest I (equal scores:
  * lower j first), in ascending j, padded with -1; `score` (optional) gets their

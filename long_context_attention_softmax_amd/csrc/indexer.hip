@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 #define HCA_SCORE_TPW 8                                   // FP8 keys (decode: few queries)
 #endif
 #ifndef HCA_SCORE_TPW4
-#define HCA_SCORE_TPW4 32                                 // MXFP4 keys (prefill: many queries)
+#define HCA_SCORE_TPW4 64                                 // MXFP4 keys (prefill: many queries)
 #endif
 #ifndef HCA_SCORE_RING
 #define HCA_SCORE_RING 2
@@ -320,7 +320,8 @@ score_quant_kernel(IndexerArgs a) {
         }
       }
     }
-    // canonical head sum: this lane's 16 heads per tile, tiles in order, then halves
+    // canonical head sum: this lane's 16 heads per tile, tiles in order, each head
+    // one fused multiply-add into the running sum (one rounding), then the halves
     float S = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
@@ -332,8 +333,7 @@ score_quant_kernel(IndexerArgs a) {
           // which needs no NaN canonicalization; both give the same bits
           const float d = acc[T][i];
           const float r = FMT == HCA_MXFP4 ? __int_as_float(max(__float_as_int(d), 0)) : (d > 0.0f ? d : 0.0f);
-          const float term = wv[T][i] * r;
-          S = S + term;
+          S = __builtin_fmaf(wv[T][i], r, S);
         }
       }
     }
@@ -341,7 +341,7 @@ score_quant_kernel(IndexerArgs a) {
     if (u == 0 && j < (uint32_t)V) {
       *reinterpret_cast<float*>(reinterpret_cast<char*>(sc) + (uint32_t)(4u * j)) = S;   // scalar base + 32-bit offset
       // first digit of float_key(S): S is never -0 (each half-sum starts from +0,
-      // and a sum is -0 only if both addends are), so the sign flip needs no case
+      // and a rounded sum is -0 only if both addends are), so the sign flip needs no case
       const uint32_t b = __float_as_uint(S);
       atomicAdd(&s_hist[(b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 21], 1u);
     }

@@ -15,11 +15,11 @@ with per-(query, head) weights w >= 0.
 Quantized operands (FP8 with per-tensor scale 1, or MXFP4): every head dot is an
 exact binary32 number (products of the element grids are exact and the sums stay
 within 24 bits), so d is computed exactly here and checked to be so.  The head
-sum is then defined in binary32, un-fused, in one canonical order:
-    term_h = fl32(w_h * max(d_h, +0))
-    S_u    = (((+0 + term_{h0}) + term_{h1}) + ...) over h = 32T + 8(i//4) + 4u + i%4,
-             T ascending, then i = 0..15 ascending          (u = 0, 1)
-    I      = S_0 + S_1
+sum is then defined in binary32, one rounding per head (a fused multiply-add into
+the running sum), in one canonical order:
+    S_u <- fl32(w_h * max(d_h, +0) + S_u), from S_u = +0,
+           over h = 32T + 8(i//4) + 4u + i%4, T ascending, then i = 0..15   (u = 0, 1)
+    I    = fl32(S_0 + S_1)
 f32 operands (the tiny workload): everything in fp64, sequential over dims, then
 over heads ascending, un-fused.
 """
@@ -62,6 +62,30 @@ def mxfp4_grain(scales: np.ndarray) -> np.ndarray:
     return np.exp2(s - 127.0) * 0.5
 
 
+def fma_f32(a, b, c) -> np.ndarray:
+    """fl32(a * b + c) with a single rounding (round to nearest even), elementwise,
+    for binary32 a, b, c.  a * b is exact in binary64 (24 + 24 significand bits);
+    the binary64 sum s = fl64(a*b + c) and its error e (a*b + c = s + e exactly,
+    Knuth's TwoSum) then decide the result: s rounds to binary32 like the exact sum
+    unless s lies exactly halfway between two binary32 neighbours and e != 0, when
+    the exact sum is on the side of e."""
+    p = np.asarray(a, np.float32).astype(np.float64) * np.asarray(b, np.float32).astype(np.float64)
+    c64 = np.asarray(c, np.float32).astype(np.float64)
+    p, c64 = np.broadcast_arrays(p, c64)
+    s = p + c64
+    bv = s - p
+    e = (p - (s - bv)) + (c64 - bv)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    up = np.nextafter(r, np.float32(np.inf))
+    dn = np.nextafter(r, np.float32(-np.inf))
+    hi = np.where(r64 > s, r, up)                 # the binary32 neighbours bracketing s
+    lo = np.where(r64 < s, r, dn)
+    tie = (r64 != s) & (s - lo.astype(np.float64) == hi.astype(np.float64) - s)
+    out = np.where(tie & (e > 0), hi, np.where(tie & (e < 0), lo, r))
+    return out.astype(np.float32)
+
+
 def score_canonical_f32(d: np.ndarray, w: np.ndarray) -> np.ndarray:
     """I[j] (float32) from exact head dots d [H_I, V] and weights w [H_I], in the
     canonical order above.  H_I must be a multiple of 32."""
@@ -75,8 +99,7 @@ def score_canonical_f32(d: np.ndarray, w: np.ndarray) -> np.ndarray:
         for T in range(H_I // 32):
             for i in range(16):
                 h = 32 * T + 8 * (i // 4) + 4 * u + i % 4
-                term = np.multiply(w32[h], relu[h], dtype=np.float32)
-                acc = np.add(acc, term, dtype=np.float32)
+                acc = fma_f32(w32[h], relu[h], acc)
         S.append(acc)
     return np.add(S[0], S[1], dtype=np.float32)
 

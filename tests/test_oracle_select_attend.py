@@ -99,6 +99,58 @@ def test_canonical_sum_one_hot_and_negative():
     assert np.all(got == 0) and not np.any(np.signbit(got))
 
 
+def _round_f32(x: Fraction) -> Fraction:
+    """The binary32 value nearest to x (ties to even), by exact rational arithmetic."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    x = abs(x)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    if Fraction(2) ** e > x:
+        e -= 1                                   # now 2^e <= x < 2^(e+1)
+    e = max(e, -126)                             # subnormals share the smallest step
+    step = Fraction(2) ** (e - 23)
+    q = x / step
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * step
+
+
+def test_fma_f32_against_exact_rounding():
+    rng = np.random.default_rng(9)
+    a = rng.random(400).astype(np.float32) * np.float32(2.0) ** rng.integers(-30, 5, 400).astype(np.float32)
+    b = (rng.standard_normal(400) * 2.0 ** rng.integers(-30, 5, 400)).astype(np.float32)
+    c = (rng.standard_normal(400) * 2.0 ** rng.integers(-30, 5, 400)).astype(np.float32)
+    # a double-rounding trap: c + a*b = 1 + 2^-23 + 2^-24 - 2^-60 rounds to 1 + 2^-24
+    # in binary64, exactly halfway; the single rounding must go down to 1 + 2^-23
+    a[0], b[0], c[0] = np.float32(1 + 2.0 ** -18), np.float32(2.0 ** -24 * (1 - 2.0 ** -18)), np.float32(1 + 2.0 ** -23)
+    got = indexer.fma_f32(a, b, c)
+    assert float(got[0]) == 1 + 2.0 ** -23
+    assert float(np.float32(np.float64(a[0]) * np.float64(b[0]) + np.float64(c[0]))) != 1 + 2.0 ** -23
+    for i in range(400):
+        want = _round_f32(Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i])))
+        assert Fraction(float(got[i])) == want, i
+
+
+def test_canonical_sum_order_by_hand():
+    # heads enter S_0 / S_1 in the 32x32 output-layout order, one rounding per head
+    rng = np.random.default_rng(10)
+    d = (rng.standard_normal((64, 7)) * 4).astype(np.float32)
+    w = rng.random(64).astype(np.float32)
+    got = indexer.score_canonical_f32(d.astype(np.float64), w)
+    for j in range(7):
+        S = [Fraction(0), Fraction(0)]
+        for u in range(2):
+            for T in range(2):
+                for i in range(16):
+                    h = 32 * T + 8 * (i // 4) + 4 * u + i % 4
+                    r = max(Fraction(float(d[h, j])), Fraction(0))
+                    S[u] = _round_f32(Fraction(float(w[h])) * r + S[u])
+        assert Fraction(float(got[j])) == _round_f32(S[0] + S[1])
+
+
 # ------------------------------------------------------------------- top-k
 def test_topk_against_stable_sort():
     rng = np.random.default_rng(7)
