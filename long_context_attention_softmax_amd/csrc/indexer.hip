@@ -14,10 +14,11 @@
 // value of any dot whose partial sums are binary32 numbers; MXFP4 operands use the
 // scaled FP4 MFMA, exact under the same condition.  (The FP8 MFMA is not used: it
 // sums groups of eight products in a narrower window and can drop low-order bits.)
-// The head sum follows one fixed order - binary32, un-fused:
-//     S_u = (((+0 + t_{h0}) + t_{h1}) + ...) over h = 32T + 8(i / 4) + 4u + (i % 4)
-//           (T ascending, then i = 0..15), for the two halves u = 0, 1
-//     I   = S_0 + S_1,      t_h = fl(w_h * max(d_h, +0))
+// The head sum follows one fixed order in binary32, each head one fused
+// multiply-add (a single rounding):
+//     S_u <- fl(w_h * max(d_h, +0) + S_u), from S_u = +0, over
+//            h = 32T + 8(i / 4) + 4u + (i % 4) (T ascending, then i = 0..15),
+//            for the two halves u = 0, 1;      I = fl(S_0 + S_1)
 // which is exactly the order the 32x32 MFMA output layout produces: lane (j, u)
 // holds heads 32T + 8(i / 4) + 4u + (i % 4) of entry j in register i, and one
 // butterfly add combines the halves.  (32x32 products run at twice the rate of
@@ -55,6 +56,37 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   r[0] = a0[0]; r[1] = a0[1]; r[2] = a1[0]; r[3] = a1[1];
   r[4] = a2[0]; r[5] = a2[1]; r[6] = a3[0]; r[7] = a3[1];
   return r;
+}
+
+// Exclusive scan over the threads of a workgroup of NT threads (order = thread id).
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = lane < NWV ? s_wave[lane] : 0;
+    uint32_t u = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t y = __shfl_up(u, o, 64);
+      if (lane >= o) u += y;
+    }
+    if (lane < NWV) s_wave[lane] = u - t;
+    if (lane == NWV - 1) s_wave[NWV] = u;
+  }
+  __syncthreads();
+  uint32_t res = s_wave[wave] + x - v;
+  *total = s_wave[NWV];
+  __syncthreads();
+  return res;
 }
 
 // ----------------------------------------------------------- f32 operands (fp64)
@@ -145,6 +177,43 @@ constexpr int kRing = HCA_SCORE_RING;                    // tiles in flight per 
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// One float per lane into a buffer of `bytes` bytes at `base`: a lane whose byte
+// offset is at or past the end writes nothing (the buffer range check drops it).
+// All lanes execute the store, so a score store needs no branch, and the memory
+// counter waits of the key ring stay exact (a store under a branch would make
+// the compiler assume the path without it and wait for one load too many).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t score_range(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_ranged(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+constexpr uint32_t kNoStore = 0x80000000u;              // past any score row
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// Canonical head sum of one tile: this lane's 16 heads per head tile, head tiles in
+// order, each head one fused multiply-add into the running sum (one rounding), then
+// the two halves of the wave (lanes j and j + 32) added.
+template <int FMT, int HT>
+__device__ __forceinline__ float head_sum(const v16f (&acc)[2], const float (&wv)[2][16]) {
+  float S = 0.0f;
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    if (T < HT) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // max(d, +0) of a finite dot; with MXFP4 keys (ALU-bound) as one integer
+        // max of its bits (a negative float, -0 included, is a negative integer),
+        // which needs no NaN canonicalization; both give the same bits
+        const float d = acc[T][i];
+        const float r = FMT == HCA_MXFP4 ? __int_as_float(max(__float_as_int(d), 0)) : (d > 0.0f ? d : 0.0f);
+        S = __builtin_fmaf(wv[T][i], r, S);
+      }
+    }
+  }
+  return S + __shfl_xor(S, 32, 64);
+}
+
 // Lane (j, u) = (lane % 32, lane / 32) of a 32-entry tile.  FP8: it holds bytes
 // [64u, 64u + 64) of entry j's key and, per k-step s of the BF16 32x32x16 product,
 // dims 64u + 8s .. 64u + 8s + 7; the query rows use the same dims.  MXFP4: it holds
@@ -166,8 +235,11 @@ template <int FMT, bool XQ, int HT>
 __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
+  constexpr bool kStage = FMT == HCA_FP8_E4M3;          // scores staged in LDS, one write per wave
+  static_assert(!kStage || (32 * tiles_per_wave<FMT>()) % 256 == 0, "staged scores: whole 16-byte groups per lane");
   __shared__ uint32_t s_hist[kBins];
   __shared__ v8bf s_qa[2][8][64];                        // FP8 path: widened query operands, per lane
+  __shared__ __attribute__((aligned(16))) float s_st[kStage ? kScoreThreads / 64 : 1][kStage ? 32 * tiles_per_wave<FMT>() : 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, u = lane >> 5;
   int n;
@@ -278,7 +350,10 @@ score_quant_kernel(IndexerArgs a) {
   }
   __syncthreads();
 
-  float* sc = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
+  // MXFP4: the query's V scores, one store per tile; FP8 (staged): the whole padded
+  // row (a multiple of 64 floats), so a 16-byte group is either in the row or past it
+  float* const sc_row = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
+  const __amdgpu_buffer_rsrc_t srange = score_range(sc_row, kStage ? 4u * (uint32_t)a.score_pitch : 4u * (uint32_t)V);
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
     const uint32_t j = j0 + 32u * (uint32_t)t;
@@ -320,30 +395,30 @@ score_quant_kernel(IndexerArgs a) {
         }
       }
     }
-    // canonical head sum: this lane's 16 heads per tile, tiles in order, each head
-    // one fused multiply-add into the running sum (one rounding), then the halves
-    float S = 0.0f;
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      if (T < HT) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // max(d, +0) of a finite dot; with MXFP4 keys (ALU-bound) as one integer
-          // max of its bits (a negative float, -0 included, is a negative integer),
-          // which needs no NaN canonicalization; both give the same bits
-          const float d = acc[T][i];
-          const float r = FMT == HCA_MXFP4 ? __int_as_float(max(__float_as_int(d), 0)) : (d > 0.0f ? d : 0.0f);
-          S = __builtin_fmaf(wv[T][i], r, S);
-        }
-      }
+    const float S = head_sum<FMT, HT>(acc, wv);
+    if (kStage) {
+      if (u == 0) s_st[wave][32 * t + jl] = S;
+    } else {
+      store_ranged(srange, u == 0 ? 4u * j : kNoStore, S);      // j >= V: past the range
     }
-    S = S + __shfl_xor(S, 32, 64);
     if (u == 0 && j < (uint32_t)V) {
-      *reinterpret_cast<float*>(reinterpret_cast<char*>(sc) + (uint32_t)(4u * j)) = S;   // scalar base + 32-bit offset
       // first digit of float_key(S): S is never -0 (each half-sum starts from +0,
       // and a rounded sum is -0 only if both addends are), so the sign flip needs no case
       const uint32_t b = __float_as_uint(S);
       atomicAdd(&s_hist[(b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 21], 1u);
+    }
+  }
+  if (kStage) {
+    // the wave's 32 x tiles scores in entry order, 16 bytes per lane; entries past V
+    // land in the row's padding (never read), groups past the row are dropped
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int h = 0; h < 32 * kTilesPerWave / 256; ++h) {
+      const uint32_t f = 256u * h + 4u * lane;
+      const u4v v = *reinterpret_cast<const u4v*>(&s_st[wave][f]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, srange, (int)(4u * ((uint32_t)wbase + f)), 0, 0);
     }
   }
   __syncthreads();
@@ -382,37 +457,6 @@ struct SelectWs {
   uint32_t* state;        // [Nq, 2]: threshold key, number of equal keys kept
   int nch;
 };
-
-// Exclusive scan over the threads of a workgroup of NT threads (order = thread id).
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
-  constexpr int NWV = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < NWV ? s_wave[lane] : 0;
-    uint32_t u = t;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t y = __shfl_up(u, o, 64);
-      if (lane >= o) u += y;
-    }
-    if (lane < NWV) s_wave[lane] = u - t;
-    if (lane == NWV - 1) s_wave[NWV] = u;
-  }
-  __syncthreads();
-  uint32_t res = s_wave[wave] + x - v;
-  *total = s_wave[NWV];
-  __syncthreads();
-  return res;
-}
 
 // The digit holding the need-th largest key of a histogram (digits ordered by key);
 // *need becomes the rank still needed inside that digit.

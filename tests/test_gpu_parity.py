@@ -47,6 +47,22 @@ def test_csa_decode_ragged_tail(gpu):
     run_and_compare(lay, g)
 
 
+@pytest.mark.parametrize("B", [256, 257])
+def test_csa_decode_many_short_queries(gpu, B):
+    # many decode queries (up to 256 workgroup-scan positions, and one past), with
+    # lengths that give no entry, a partial tile, exactly one tile and ragged tails:
+    # scores staged per wave and written past V into the row padding only
+    rng = np.random.default_rng(40 + B)
+    L = (np.exp(rng.uniform(0.0, np.log(40000.0), B)) + 1).astype(np.int64)
+    L[:12] = [1, 2, 3, 4, 5, 8, 127, 128, 129, 2048, 2049, 4100]
+    g = synth.FULL_GEOMETRY
+    from synth.gen import _decode_layer
+    lay = _decode_layer(rng, g, "csa", L, 128, 1.0, "fp8")
+    _print(f"csa decode B={B} short ragged lengths (min {L.min()}, max {L.max()})")
+    ref, dev, err = run_and_compare(lay, g)
+    _print(f"  rel err {err:.2e}")
+
+
 def test_hca_decode_small(gpu):
     w = synth.hca_decode(seed=13, B=2, L=65536)
     _print("hca decode B=2 L=65536")
