@@ -136,7 +136,7 @@ def test_select_all_tied_beyond_candidate_list(gpu):
 
 
 def test_select_large_k(gpu):
-    # k above the fused select's limit takes the three-phase path
+    # k larger than V / 4 and than one chunk's 4096 entries: output offsets span chunks
     from dataclasses import replace
     g = replace(synth.FULL_GEOMETRY, topk=3000)
     w = synth.csa_decode(seed=17, B=2, L=32768, g=g)
