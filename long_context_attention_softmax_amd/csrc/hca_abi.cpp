@@ -289,6 +289,8 @@ int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
   hca::PoolArgs a{};
   a.m = d->m; a.D = d->D; a.D_r = d->D_r; a.d_I = d->raw_idx ? d->d_I : 0; a.n_blocks = d->n_blocks;
   a.rope_base = d->rope_base; a.raw_is_f32 = d->raw_fmt == HCA_F32;
+  if (d->D_r / 2 <= 64)
+    for (int i = 0; i < d->D_r / 2; ++i) a.rope_inv[i] = std::pow(d->rope_base, -2.0 * i / (double)d->D_r);
   a.raw = d->raw; a.raw_pitch = d->raw_pitch; a.raw_idx = d->raw_idx; a.raw_idx_pitch = d->raw_idx_pitch;
   a.block_row = d->block_row; a.block_pos = d->block_pos; a.out_row = d->out_row;
   a.gate_w = d->gate_w; a.gate_b = d->gate_b;

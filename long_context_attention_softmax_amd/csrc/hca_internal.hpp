@@ -24,6 +24,7 @@ struct PoolArgs {
   char* out_idx; int64_t idx_pitch;
   char* out_idx_scales; int64_t idx_scale_pitch;
   float* debug;
+  double rope_inv[64];                // rope_base^(-2i/D_r), i < D_r / 2, when D_r / 2 <= 64
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 

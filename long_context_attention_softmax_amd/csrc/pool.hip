@@ -46,6 +46,8 @@ __device__ __forceinline__ double elem(const Raw8<F32>& r, int e) {
 }
 
 constexpr int kTokU = 16;     // tokens of one wave in flight
+constexpr int kOne = 4;       // tokens of one wave kept in registers (blocks of m <= 16)
+constexpr int kPoolHostInv = (int)(sizeof(PoolArgs::rope_inv) / sizeof(double));   // RoPE frequencies from the host
 
 // Partial weighted sums of one wave over the tokens i = wave, wave+4, ... of the block;
 // lane handles 8-element groups g = lane, lane+64, ...
@@ -92,6 +94,24 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   const char* raw_idx = static_cast<const char*>(a.raw_idx);
   const int ng = a.D / 8, ngi = a.d_I / 8;
 
+  // Small BF16 blocks (m <= 4 kOne tokens, one 8-element group per lane) load each
+  // token row (and index-stream row) once: the rows loaded for the gate logits stay
+  // in registers for the weighted sums, which add the same terms in the same order
+  // as the general path.
+  const bool one_pass = !F32 && a.m <= 4 * kOne && ng <= 64 && ngi <= 64;   // uniform
+  Raw8<F32> xr[kOne], yr[kOne];
+  if (one_pass) {
+    if (a.idx_fmt >= 0 && lane < ngi) {
+#pragma unroll
+      for (int j = 0; j < kOne; ++j)
+        if (wave + 4 * j < a.m) yr[j] = load8<F32>(raw_idx, a.raw_idx_pitch, r0 + wave + 4 * j, lane);
+    }
+    if (lane < ng) {
+#pragma unroll
+      for (int j = 0; j < kOne; ++j)
+        if (wave + 4 * j < a.m) xr[j] = load8<F32>(raw, a.raw_pitch, r0 + wave + 4 * j, lane);
+    }
+  }
   // gate logits z_i = g . x_i + b_i : wave w takes tokens w, w+4, ...; kTokU in flight
   for (int i0 = wave; i0 < a.m; i0 += 4 * kTokU) {
     double acc[kTokU];
@@ -104,7 +124,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
       Raw8<F32> x[kTokU];
 #pragma unroll
       for (int j = 0; j < kTokU; ++j)
-        if (i0 + 4 * j < a.m) x[j] = load8<F32>(raw, a.raw_pitch, r0 + i0 + 4 * j, g);
+        if (i0 + 4 * j < a.m) x[j] = one_pass && j < kOne ? xr[j < kOne ? j : 0] : load8<F32>(raw, a.raw_pitch, r0 + i0 + 4 * j, g);
 #pragma unroll
       for (int j = 0; j < kTokU; ++j)
         if (i0 + 4 * j < a.m) {
@@ -133,7 +153,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
     for (int i = lane; i < a.m; i += 64) s_z[i] = s_z[i] / sum;
   } else {
     for (int i = tid - 64; i < half; i += kPoolThreads - 64) {
-      const double inv = pow(a.rope_base, -2.0 * (double)i / (double)a.D_r);
+      const double inv = half <= kPoolHostInv ? a.rope_inv[i] : pow(a.rope_base, -2.0 * (double)i / (double)a.D_r);
       double sn, cs;
       sincos((double)p_last * inv, &sn, &cs);
       s_rc[i] = cs;
@@ -142,9 +162,27 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolArgs a) {
   }
   __syncthreads();
   // weighted sums: per-wave partials over interleaved tokens, merged in wave order
-  pool_partial<F32>(raw, a.raw_pitch, r0, a.m, ng, s_z, s_part[wave], wave, lane);
-  if (a.idx_fmt >= 0)
-    pool_partial<F32>(raw_idx, a.raw_idx_pitch, r0, a.m, ngi, s_z, s_party[wave], wave, lane);
+  if (one_pass) {
+    auto partial = [&](const Raw8<F32> (&r)[kOne], int ngr, double* part) {
+      if (lane >= ngr) return;
+      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < kOne; ++j)
+        if (wave + 4 * j < a.m) {
+          const double al = s_z[wave + 4 * j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += al * elem<F32>(r[j], e);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[8 * lane + e] = acc[e];
+    };
+    partial(xr, ng, s_part[wave]);
+    if (a.idx_fmt >= 0) partial(yr, ngi, s_party[wave]);
+  } else {
+    pool_partial<F32>(raw, a.raw_pitch, r0, a.m, ng, s_z, s_part[wave], wave, lane);
+    if (a.idx_fmt >= 0)
+      pool_partial<F32>(raw_idx, a.raw_idx_pitch, r0, a.m, ngi, s_z, s_party[wave], wave, lane);
+  }
   __syncthreads();
   for (int d = tid; d < a.D; d += kPoolThreads)
     s_c[d] = ((s_part[0][d] + s_part[1][d]) + s_part[2][d]) + s_part[3][d];
