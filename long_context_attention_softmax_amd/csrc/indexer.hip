@@ -448,6 +448,7 @@ constexpr int kCandCap2 = 8192;
 constexpr int kMaxChunks = 2048;
 
 struct SelectWs {
+  uint32_t* d1;           // [Nq] first digit found once per query (many queries), else null
   uint32_t* cand_count;   // [Nq] (cleared with the histogram)
   uint32_t* cand_key;     // [Nq, kCandCap2]
   int32_t* cand_idx;      // [Nq, kCandCap2]
@@ -497,8 +498,30 @@ __device__ __forceinline__ void load_chunk_keys(const float* sc, int64_t jt, int
   }
 }
 
-__global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
+// With many queries, every chunk workgroup finding the first digit again (8 KB of
+// histogram and a 2048-bin scan each) costs more than one extra launch: one
+// workgroup per query finds it once.
+constexpr int kDigitMinQ = 256;
+__global__ void __launch_bounds__(256) select_digit_kernel(IndexerArgs a, SelectWs ws) {
   __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_wave[256 / 64 + 1];
+  __shared__ int s_found;
+  __shared__ uint32_t s_need;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int64_t V = visible(a, n);
+  const int64_t K = V < a.k ? V : a.k;
+  if (V <= K) return;                                    // uniform
+  const uint32_t* gh = a.hist + (int64_t)n * kBins;
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
+  __syncthreads();
+  uint32_t need = (uint32_t)K;
+  const uint32_t d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+  if (tid == 0) ws.d1[n] = d1;
+}
+
+template <bool PRE>                                      // PRE: the first digit was found per query
+__global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
+  __shared__ uint32_t s_hist[PRE ? 1 : kBins];
   __shared__ uint32_t s_ck[kChunk1];
   __shared__ int32_t s_cj[kChunk1];
   __shared__ uint32_t s_wave[256 / 64 + 1];
@@ -516,12 +539,19 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   const int64_t jt = j0 + (int64_t)kPerThread1 * tid;
   uint32_t key[kPerThread1];
   load_chunk_keys(sc, jt, j1, key);
-  const uint32_t* gh = a.hist + (int64_t)n * kBins;
-  for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
-  if (tid == 0) s_n = 0;
-  __syncthreads();
-  uint32_t need = (uint32_t)K;
-  const uint32_t d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+  uint32_t d1;
+  if constexpr (PRE) {
+    d1 = ws.d1[n];
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+  } else {
+    const uint32_t* gh = a.hist + (int64_t)n * kBins;
+    for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    uint32_t need = (uint32_t)K;
+    d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+  }
   uint32_t gt = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread1; ++e) {
@@ -724,7 +754,7 @@ __global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectW
 
 namespace {
 struct WsLayout {
-  size_t scores, hist, cand_key, cand_idx, chunk_gt, out_off, eq_before, state, total;
+  size_t scores, hist, cand_key, cand_idx, chunk_gt, out_off, eq_before, state, d1, total;
   int nch;
 };
 WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
@@ -744,6 +774,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
   L.out_off = o; o = up(o + (size_t)Nq * L.nch * 4);
   L.eq_before = o; o = up(o + (size_t)Nq * L.nch * 4);
   L.state = o; o = up(o + (size_t)Nq * 2 * 4);
+  L.d1 = o; o = up(o + (size_t)Nq * 4);
   L.total = o;
   return L;
 }
@@ -771,6 +802,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   char* wsb = static_cast<char*>(a.scores);
   a.hist = reinterpret_cast<uint32_t*>(wsb + L.hist);
   SelectWs sw;
+  sw.d1 = a.Nq >= kDigitMinQ ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
   sw.cand_key = reinterpret_cast<uint32_t*>(wsb + L.cand_key);
   sw.cand_idx = reinterpret_cast<int32_t*>(wsb + L.cand_idx);
@@ -805,7 +837,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
   dim3 cgrid((unsigned)L.nch, a.Nq);
-  hipLaunchKernelGGL(select_collect_kernel, cgrid, dim3(256), 0, s, a, sw);
+  if (sw.d1) {
+    hipLaunchKernelGGL(select_digit_kernel, dim3(a.Nq), dim3(256), 0, s, a, sw);
+    hipLaunchKernelGGL(select_collect_kernel<true>, cgrid, dim3(256), 0, s, a, sw);
+  } else {
+    hipLaunchKernelGGL(select_collect_kernel<false>, cgrid, dim3(256), 0, s, a, sw);
+  }
   hipLaunchKernelGGL(select_threshold_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a, sw);
   hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
   return hipGetLastError();
