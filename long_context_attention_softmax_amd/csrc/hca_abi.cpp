@@ -112,7 +112,7 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
     REQUIRE(d->H_I == 32 || d->H_I == 64, HCA_E_UNSUPPORTED, "quantized indexer needs H_I in {32, 64}");
     REQUIRE(d->max_visible <= 2048LL * 4096, HCA_E_UNSUPPORTED, "quantized indexer supports at most 2^23 visible entries");
   }
-  *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt);
+  *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt, d->k);
   if (d->Nq == 0) return HCA_OK;
   REQUIRE(d->q.data && d->keys.data && d->w && d->cache_row_start && d->seq_id && d->q_pos && d->idx,
           HCA_E_NULL, "q, keys, w, cache_row_start, seq_id, q_pos and idx are required");
@@ -260,7 +260,7 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
       REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
       REQUIRE(d->struct_size == sizeof(hca_indexer_topk_desc), HCA_E_VERSION, "struct_size mismatch");
       REQUIRE(d->Nq >= 0 && d->max_visible >= 0, HCA_E_SHAPE, "Nq and max_visible must be >= 0");
-      ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, d->q.fmt);
+      ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, d->q.fmt, d->k);
       rc = HCA_OK;
       break;
     }

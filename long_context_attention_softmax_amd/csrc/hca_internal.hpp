@@ -41,7 +41,7 @@ struct IndexerArgs {
   hipEvent_t prof_begin, prof_end;    // optional, around the scoring kernel
 };
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
-size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt);
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k);
 
 struct AttnArgs {
   int Nq, H, D, D_r, mode, m, k, n_win, win_cap, io_f32;

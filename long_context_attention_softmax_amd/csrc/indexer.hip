@@ -446,10 +446,18 @@ __global__ void __launch_bounds__(256) zero_kernel(uint4* p, int64_t n16) {
 constexpr int kChunk1 = 4096;
 constexpr int kCandCap2 = 8192;
 constexpr int kMaxChunks = 2048;
+// Many queries (>= kDigitMinQ) and k <= kMergedMaxK: collect also keeps the keys above
+// d1 (fewer than k per query) and the threshold phase writes the selection itself,
+// each selected entry placed by the rank of its index, so the scores are not read a
+// second time (no emit phase).
+constexpr int kMergedMaxK = 2048;
 
 struct SelectWs {
   uint32_t* d1;           // [Nq] first digit found once per query (many queries), else null
-  uint32_t* cand_count;   // [Nq] (cleared with the histogram)
+  uint32_t* cand_count;   // [Nq] (cleared with the histogram, as the next)
+  uint32_t* above_count;  // [Nq]  merged selection: keys above the first digit
+  uint32_t* above_key;    // [Nq, k]
+  int32_t* above_idx;     // [Nq, k]
   uint32_t* cand_key;     // [Nq, kCandCap2]
   int32_t* cand_idx;      // [Nq, kCandCap2]
   uint32_t* chunk_gt;     // [Nq, nch]
@@ -522,10 +530,10 @@ __global__ void __launch_bounds__(256) select_digit_kernel(IndexerArgs a, Select
 template <bool PRE>                                      // PRE: the first digit was found per query
 __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, SelectWs ws) {
   __shared__ uint32_t s_hist[PRE ? 1 : kBins];
-  __shared__ uint32_t s_ck[kChunk1];
-  __shared__ int32_t s_cj[kChunk1];
+  __shared__ uint32_t s_ck[kChunk1];                   // candidates from the front, keys above d1 from the back
+  __shared__ uint16_t s_cj[kChunk1];                   // their offsets in the chunk
   __shared__ uint32_t s_wave[256 / 64 + 1];
-  __shared__ uint32_t s_n, s_base;
+  __shared__ uint32_t s_n, s_base, s_na, s_abase;
   __shared__ int s_found;
   __shared__ uint32_t s_need;
   const int n = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
@@ -533,6 +541,7 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   const int64_t K = V < a.k ? V : a.k;
   const int64_t j0 = (int64_t)c * kChunk1;
   if (V <= K || j0 >= V) return;
+  const bool merged = ws.above_key != nullptr;          // uniform
   // the scores do not depend on the threshold digit: request them first
   const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
   const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
@@ -542,12 +551,12 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   uint32_t d1;
   if constexpr (PRE) {
     d1 = ws.d1[n];
-    if (tid == 0) s_n = 0;
+    if (tid == 0) { s_n = 0; s_na = 0; }
     __syncthreads();
   } else {
     const uint32_t* gh = a.hist + (int64_t)n * kBins;
     for (int i = tid; i < kBins; i += 256) s_hist[i] = gh[i];
-    if (tid == 0) s_n = 0;
+    if (tid == 0) { s_n = 0; s_na = 0; }
     __syncthreads();
     uint32_t need = (uint32_t)K;
     d1 = (uint32_t)find_digit<256>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
@@ -561,7 +570,11 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
       if (dg == d1) {
         const uint32_t p = atomicAdd(&s_n, 1u);           // LDS: at most kChunk1 per chunk
         s_ck[p] = key[e];
-        s_cj[p] = (int32_t)(jt + e);
+        s_cj[p] = (uint16_t)(jt + e - j0);
+      } else if (merged && dg > d1) {
+        const uint32_t p = kChunk1 - 1 - atomicAdd(&s_na, 1u);
+        s_ck[p] = key[e];
+        s_cj[p] = (uint16_t)(jt + e - j0);
       }
     }
   }
@@ -570,6 +583,7 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   if (tid == 0) {
     ws.chunk_gt[(int64_t)n * ws.nch + c] = tot;
     s_base = s_n ? atomicAdd(&ws.cand_count[n], s_n) : 0;
+    s_abase = s_na ? atomicAdd(&ws.above_count[n], s_na) : 0;
   }
   __syncthreads();
   const uint32_t cnt = s_n, base = s_base;
@@ -577,9 +591,65 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
     const uint32_t p = base + i;
     if (p < (uint32_t)kCandCap2) {
       ws.cand_key[(int64_t)n * kCandCap2 + p] = s_ck[i];
-      ws.cand_idx[(int64_t)n * kCandCap2 + p] = s_cj[i];
+      ws.cand_idx[(int64_t)n * kCandCap2 + p] = (int32_t)(j0 + s_cj[i]);
     }
   }
+  const uint32_t na = s_na, abase = s_abase;
+  for (uint32_t i = tid; i < na; i += 256) {
+    const uint32_t p = abase + i;                        // < k: fewer than k keys lie above d1
+    if (p < (uint32_t)a.k) {
+      ws.above_key[(int64_t)n * a.k + p] = s_ck[kChunk1 - 1 - i];
+      ws.above_idx[(int64_t)n * a.k + p] = (int32_t)(j0 + s_cj[kChunk1 - 1 - i]);
+    }
+  }
+}
+
+// Writes, in index order, the keys of one stretch above T and its keys equal to T
+// while fewer than take_eq equal keys precede them in the whole row (NT threads,
+// kPerThread1 consecutive keys each): pos_base = entries selected before the
+// stretch, eqb = keys equal to T before it.  Returns the stretch's count of keys
+// above T | keys equal to T << 16.
+template <int NT>
+__device__ uint32_t emit_ordered(const IndexerArgs& a, int n, const uint32_t (&key)[kPerThread1], int64_t jt,
+                                 int64_t j1, uint32_t T, uint32_t take_eq, uint32_t pos_base, uint32_t eqb,
+                                 int64_t K, const float* sc, uint32_t* s_wave) {
+  static_assert(NT * kPerThread1 < 65536, "16-bit counts per stretch");
+  int32_t* out = a.idx + (int64_t)n * a.k;
+  float* so = reinterpret_cast<float*>(a.score_out);
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread1; ++e) {
+    if (jt + e < j1) {
+      ngt += key[e] > T;
+      neq += key[e] == T;
+    }
+  }
+  uint32_t tot;
+  const uint32_t pre = block_exclusive_scan<NT>(ngt | (neq << 16), s_wave, &tot);
+  uint32_t gt_before = pre & 0xFFFF;
+  uint32_t eq_before = eqb + (pre >> 16);
+  const uint32_t eq_taken0 = eqb < take_eq ? eqb : take_eq;     // equal keys taken before the stretch
+#pragma unroll
+  for (int e = 0; e < kPerThread1; ++e) {
+    if (jt + e < j1) {
+      const bool is_gt = key[e] > T, is_eq = key[e] == T;
+      if (is_gt || (is_eq && eq_before < take_eq)) {
+        const uint32_t eq_sel_before = (eq_before < take_eq ? eq_before : take_eq) - eq_taken0;
+        const uint32_t pos = pos_base + gt_before + eq_sel_before;
+        if (pos < (uint32_t)K) {
+          out[pos] = (int32_t)(jt + e);
+          if (so) so[(int64_t)n * a.k + pos] = sc[jt + e];
+        }
+      }
+      gt_before += is_gt;
+      eq_before += is_eq;
+    }
+  }
+  return tot;
+}
+
+__device__ __forceinline__ float key_float(uint32_t k) {        // inverse of float_key (no -0 arises)
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(IndexerArgs a, SelectWs ws) {
@@ -590,16 +660,29 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
   __shared__ uint32_t s_eqc[kMaxChunks];
   __shared__ uint32_t s_wave[kSelectThreads / 64 + 1];
   __shared__ int s_found;
-  __shared__ uint32_t s_need;
+  __shared__ uint32_t s_need, s_ns;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sk[kMergedMaxK];      // merged: the selected entries
+  __shared__ __attribute__((aligned(16))) int32_t s_sj[kMergedMaxK + 32];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int64_t V = visible(a, n);
   const int64_t K = V < a.k ? V : a.k;
+  const bool merged = ws.above_key != nullptr;          // uniform: this kernel writes the selection
+  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+  int32_t* const out = a.idx + (int64_t)n * a.k;
+  float* const so = reinterpret_cast<float*>(a.score_out);
   if (V <= K) {
-    if (tid == 0) { ws.state[2 * n] = 0; ws.state[2 * n + 1] = 0xFFFFFFFFu; }
+    if (merged) {                                        // every visible entry, at its own position
+      for (int64_t p = tid; p < a.k; p += kSelectThreads) {
+        out[p] = p < V ? (int32_t)p : -1;
+        if (so) so[(int64_t)n * a.k + p] = p < V ? sc[p] : 0.0f;
+      }
+    } else if (tid == 0) {
+      ws.state[2 * n] = 0;
+      ws.state[2 * n + 1] = 0xFFFFFFFFu;
+    }
     return;
   }
   const int nch = (int)((V + kChunk1 - 1) / kChunk1);
-  const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
   uint32_t gtc[2];                                      // chunks 2t, 2t + 1: keys above digit d1
 #pragma unroll
   for (int e = 0; e < 2; ++e) gtc[e] = 2 * tid + e < nch ? ws.chunk_gt[(int64_t)n * ws.nch + 2 * tid + e] : 0;
@@ -619,6 +702,7 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
   }
   __syncthreads();
   uint32_t prefix = d1;
+  uint32_t n_eq = 0;                                     // candidates equal to T (in the list)
   for (int round = 0; round < 2; ++round) {
     const int shift = round == 0 ? 10 : 0;
     const int nbits = round == 0 ? 11 : 10;
@@ -638,9 +722,112 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
     }
     __syncthreads();
     const int dd = find_digit<kSelectThreads>(s_hist, nb, &need, s_wave, &s_found, &s_need);
+    if (round == 1) n_eq = s_hist[dd];
     prefix = (prefix << nbits) | (uint32_t)dd;
   }
   const uint32_t T = prefix, take_eq = need;
+  if (merged) {
+    __syncthreads();                                     // every thread has read n_eq before s_hist is reused
+    if (!in_lds) {
+      // the candidates overflowed their list: one ordered pass over the scores
+      uint32_t sel_before = 0, eq_seen = 0;
+      constexpr int64_t kStretch = (int64_t)kSelectThreads * kPerThread1;
+      for (int64_t b0 = 0; b0 < V; b0 += kStretch) {
+        const int64_t b1 = b0 + kStretch < V ? b0 + kStretch : V;
+        const int64_t bt = b0 + (int64_t)kPerThread1 * tid;
+        uint32_t kk[kPerThread1];
+        load_chunk_keys(sc, bt, b1, kk);
+        const uint32_t tt = emit_ordered<kSelectThreads>(a, n, kk, bt, b1, T, take_eq, sel_before, eq_seen, K, sc, s_wave);
+        const uint32_t gt = tt & 0xFFFF, eq = tt >> 16;
+        const uint32_t took = (eq_seen + eq < take_eq ? eq_seen + eq : take_eq) - (eq_seen < take_eq ? eq_seen : take_eq);
+        sel_before += gt + took;
+        eq_seen += eq;
+      }
+      return;
+    }
+    // equal keys: the take_eq lowest indices, i.e. the take_eq largest of 2^30 - 1 - j
+    // (three 10-bit digits)
+    uint32_t inv_min = 0;
+    if (take_eq < n_eq) {
+      uint32_t need_i = take_eq, pre = 0;
+      for (int round = 0; round < 3; ++round) {
+        const int shift = 20 - 10 * round;
+        for (int i = tid; i < 1024; i += kSelectThreads) s_hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < n1; i += kSelectThreads) {
+          if (s_ck[i] != T) continue;
+          const uint32_t inv = 0x3FFFFFFFu - (uint32_t)s_cj[i];
+          if ((inv >> (shift + 10)) == pre) atomicAdd(&s_hist[(inv >> shift) & 1023], 1u);
+        }
+        __syncthreads();
+        const int dd = find_digit<kSelectThreads>(s_hist, 1024, &need_i, s_wave, &s_found, &s_need);
+        pre = (pre << 10) | (uint32_t)dd;
+      }
+      inv_min = pre;
+    }
+    // the selected entries: every key above d1, the candidates above T and the equal
+    // keys taken (exactly K; the checks below only guard the LDS bounds); then each
+    // one's output position is the rank of its index
+    if (tid == 0) s_ns = 0;
+    __syncthreads();
+    const uint32_t na = min(ws.above_count[n], (uint32_t)a.k);
+    for (uint32_t i = tid; i < na; i += kSelectThreads) {
+      const uint32_t p = atomicAdd(&s_ns, 1u);
+      if (p < (uint32_t)kMergedMaxK) {
+        s_sk[p] = ws.above_key[(int64_t)n * a.k + i];
+        s_sj[p] = ws.above_idx[(int64_t)n * a.k + i];
+      }
+    }
+    for (uint32_t i = tid; i < n1; i += kSelectThreads) {
+      const uint32_t k2 = s_ck[i];
+      const int32_t j = s_cj[i];
+      if (k2 > T || (k2 == T && 0x3FFFFFFFu - (uint32_t)j >= inv_min)) {
+        const uint32_t p = atomicAdd(&s_ns, 1u);
+        if (p < (uint32_t)kMergedMaxK) {
+          s_sk[p] = k2;
+          s_sj[p] = j;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t ns = min(s_ns, (uint32_t)kMergedMaxK);   // == K <= kMergedMaxK
+    const uint32_t ns32 = (ns + 31) & ~31u;
+    if (tid < ns32 - ns) s_sj[ns + tid] = 0x7FFFFFFF;    // pads to a multiple of 32 (never below an index)
+    __syncthreads();
+    constexpr int kPer = kMergedMaxK / kSelectThreads;
+    int32_t mine[kPer];
+    uint32_t rank[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      mine[r] = tid + (uint32_t)kSelectThreads * r < ns ? s_sj[tid + kSelectThreads * r] : 0x7FFFFFFF;
+      rank[r] = 0;
+    }
+    // waves without an entry skip the pass; eight 16-byte reads in flight per step
+    const uint32_t wave_first = tid & ~63u;
+    if (wave_first < ns || (kPer > 1 && wave_first + kSelectThreads < ns)) {
+      const int4* c4 = reinterpret_cast<const int4*>(s_sj);
+      for (uint32_t f = 0; f < ns32 / 4; f += 8) {
+        int4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = c4[f + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int r = 0; r < kPer; ++r)
+            rank[r] += (uint32_t)(v[u].x < mine[r]) + (uint32_t)(v[u].y < mine[r]) + (uint32_t)(v[u].z < mine[r]) +
+                       (uint32_t)(v[u].w < mine[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const uint32_t e = tid + (uint32_t)kSelectThreads * r;
+      if (e < ns && rank[r] < (uint32_t)K) {
+        out[rank[r]] = mine[r];
+        if (so) so[(int64_t)n * a.k + rank[r]] = key_float(s_sk[e]);
+      }
+    }
+    return;
+  }
   // per-chunk counts of the candidates above T and equal to T
   if (in_lds) {
     for (uint32_t i = tid; i < n1; i += kSelectThreads) {
@@ -718,46 +905,18 @@ __global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectW
   const uint32_t T = ws.state[2 * n], take_eq = ws.state[2 * n + 1];
   const uint32_t pos_base = ws.out_off[(int64_t)n * ws.nch + c];
   const uint32_t eqb = ws.eq_before[(int64_t)n * ws.nch + c];
-  uint32_t ngt = 0, neq = 0;
-#pragma unroll
-  for (int e = 0; e < kPerThread1; ++e) {
-    if (jt + e < j1) {
-      ngt += key[e] > T;
-      neq += key[e] == T;
-    }
-  }
-  // counts of this thread's predecessors in the chunk (16 bits each suffice: <= 4096)
-  uint32_t tot;
-  const uint32_t pre = block_exclusive_scan<256>(ngt | (neq << 16), s_wave, &tot);
-  uint32_t gt_before = pre & 0xFFFF;
-  uint32_t eq_before = eqb + (pre >> 16);
-  const uint32_t eq_taken0 = eqb < take_eq ? eqb : take_eq;     // equal keys taken before the chunk
-#pragma unroll
-  for (int e = 0; e < kPerThread1; ++e) {
-    if (jt + e < j1) {
-      const bool is_gt = key[e] > T, is_eq = key[e] == T;
-      if (is_gt || (is_eq && eq_before < take_eq)) {
-        const uint32_t eq_sel_before = (eq_before < take_eq ? eq_before : take_eq) - eq_taken0;
-        const uint32_t pos = pos_base + gt_before + eq_sel_before;
-        if (pos < (uint32_t)K) {
-          out[pos] = (int32_t)(jt + e);
-          if (so) so[(int64_t)n * a.k + pos] = sc[jt + e];
-        }
-      }
-      gt_before += is_gt;
-      eq_before += is_eq;
-    }
-  }
+  emit_ordered<256>(a, n, key, jt, j1, T, take_eq, pos_base, eqb, K, sc, s_wave);
 }
 
 }  // namespace
 
 namespace {
 struct WsLayout {
-  size_t scores, hist, cand_key, cand_idx, chunk_gt, out_off, eq_before, state, d1, total;
+  size_t scores, hist, cand_key, cand_idx, chunk_gt, out_off, eq_before, state, d1, above_key, above_idx, total;
   int nch;
+  bool merged;
 };
-WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
+WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   WsLayout L{};
   const int64_t pitch = (max_visible + 63) / 64 * 64;
@@ -767,7 +926,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
   if (fmt == HCA_F32) return L;
   L.nch = (int)((max_visible + kChunk1 - 1) / kChunk1);
   if (L.nch < 1) L.nch = 1;
-  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 1) * 4);        // histogram + candidate count
+  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 2) * 4);        // histogram, candidate and above counts
   L.cand_key = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.cand_idx = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.chunk_gt = o; o = up(o + (size_t)Nq * L.nch * 4);
@@ -775,13 +934,17 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt) {
   L.eq_before = o; o = up(o + (size_t)Nq * L.nch * 4);
   L.state = o; o = up(o + (size_t)Nq * 2 * 4);
   L.d1 = o; o = up(o + (size_t)Nq * 4);
+  L.merged = Nq >= kDigitMinQ && k >= 1 && k <= kMergedMaxK;
+  const size_t kf = L.merged ? (size_t)k : 0;           // keys above the first digit
+  L.above_key = o; o = up(o + (size_t)Nq * kf * 4);
+  L.above_idx = o; o = up(o + (size_t)Nq * kf * 4);
   L.total = o;
   return L;
 }
 }  // namespace
 
-size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt) {
-  return ws_layout(Nq, max_visible, fmt).total;
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
+  return ws_layout(Nq, max_visible, fmt, k).total;
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
@@ -798,12 +961,15 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(select_small_f64_kernel, dim3(a.Nq), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const WsLayout L = ws_layout(a.Nq, a.max_visible, a.fmt);
+  const WsLayout L = ws_layout(a.Nq, a.max_visible, a.fmt, a.k);
   char* wsb = static_cast<char*>(a.scores);
   a.hist = reinterpret_cast<uint32_t*>(wsb + L.hist);
   SelectWs sw;
   sw.d1 = a.Nq >= kDigitMinQ ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
+  sw.above_count = sw.cand_count + a.Nq;
+  sw.above_key = L.merged ? reinterpret_cast<uint32_t*>(wsb + L.above_key) : nullptr;
+  sw.above_idx = L.merged ? reinterpret_cast<int32_t*>(wsb + L.above_idx) : nullptr;
   sw.cand_key = reinterpret_cast<uint32_t*>(wsb + L.cand_key);
   sw.cand_idx = reinterpret_cast<int32_t*>(wsb + L.cand_idx);
   sw.chunk_gt = reinterpret_cast<uint32_t*>(wsb + L.chunk_gt);
@@ -813,8 +979,8 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   sw.nch = L.nch;
   {
     // the scoring kernel histograms the first digit and the collect phase counts
-    // candidates: clear both first (they are adjacent)
-    const int64_t n16 = ((int64_t)a.Nq * (kBins + 1) * 4 + 15) / 16;
+    // candidates and keys above the first digit: clear them first (they are adjacent)
+    const int64_t n16 = ((int64_t)a.Nq * (kBins + 2) * 4 + 15) / 16;
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
@@ -844,7 +1010,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(select_collect_kernel<false>, cgrid, dim3(256), 0, s, a, sw);
   }
   hipLaunchKernelGGL(select_threshold_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a, sw);
-  hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
+  if (!L.merged) hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
   return hipGetLastError();
 }
 

@@ -135,6 +135,24 @@ def test_select_all_tied_beyond_candidate_list(gpu):
     assert np.array_equal(to_np(dev.idx)[0], np.arange(g.topk, dtype=np.int32))
 
 
+def test_select_tied_many_queries(gpu):
+    # 256 queries take the selection that the threshold phase writes itself: with every
+    # score +0, one query's ties fit the candidate list (V = 2050), one overflows it
+    # (V = 9000) and the rest see fewer than k entries
+    g = synth.FULL_GEOMETRY
+    L = np.full(256, 401, np.int64)
+    L[7], L[200] = 8201, 36001
+    from synth.gen import _decode_layer
+    lay = _decode_layer(np.random.default_rng(41), g, "csa", L, 128, 1.0, "fp8")
+    lay.w = np.zeros_like(lay.w)
+    _print("select: 256 queries, all scores tied, V = 100 / 2050 / 9000")
+    ref, dev, _ = run_and_compare(lay, g)
+    idx = to_np(dev.idx)
+    assert np.array_equal(idx[7], np.arange(g.topk, dtype=np.int32))
+    assert np.array_equal(idx[200], np.arange(g.topk, dtype=np.int32))
+    assert np.array_equal(idx[0][:100], np.arange(100, dtype=np.int32)) and (idx[0][100:] == -1).all()
+
+
 def test_select_large_k(gpu):
     # k larger than V / 4 and than one chunk's 4096 entries: output offsets span chunks
     from dataclasses import replace
