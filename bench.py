@@ -42,12 +42,14 @@ FP4_PEAK_TFLOPS = 10100.0
 ENTRY_BYTES = 448 + 128 + 4          # FP8 nope + BF16 rope + f32 scale
 TOKEN_BYTES = 512 * 2                # raw BF16 window token
 KEY_BYTES = 128                      # FP8 indexer key
+KEY_BYTES_FP4 = 64 + 4               # MXFP4 indexer key: 128 E2M1 codes + 4 E8M0 block scales
 QO_BYTES = 2 * 64 * 512 * 2          # BF16 q and o
 QI_W_BYTES = 64 * 128 + 64 * 4       # FP8 indexer query + f32 head weights
+QI_W_BYTES_FP4 = 64 * KEY_BYTES_FP4 + 64 * 4   # MXFP4 indexer query + f32 head weights
 
 
 # ---------------------------------------------------------------- byte models
-def csa_bytes(lengths, k=512, n_win=128):
+def csa_bytes(lengths, k=512, n_win=128, key_bytes=KEY_BYTES, qiw_bytes=QI_W_BYTES):
     """Algorithmic HBM bytes of one CSA decode step (query at t = L - 1), each
     byte once: indexer keys of the visible entries, the k gathered entries, the
     window tokens, q/o, q_I/w, and the pooled entry + key (write) plus the raw
@@ -56,11 +58,11 @@ def csa_bytes(lengths, k=512, n_win=128):
     keys = 0
     for L in lengths:
         V = L // 4
-        keys += V * KEY_BYTES + QI_W_BYTES
-        total += V * KEY_BYTES + QI_W_BYTES + min(k, V) * ENTRY_BYTES
+        keys += V * key_bytes + qiw_bytes
+        total += V * key_bytes + qiw_bytes + min(k, V) * ENTRY_BYTES
         total += min(n_win, L) * TOKEN_BYTES + QO_BYTES
         if L % 4 == 0:
-            total += ENTRY_BYTES + KEY_BYTES + 4 * 128 * 2
+            total += ENTRY_BYTES + key_bytes + 4 * 128 * 2
     return total, keys
 
 
@@ -185,7 +187,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
-    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|hca|prefill)")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -259,6 +261,24 @@ def main():
                 scoring_kernel_ms=round(float(k2.mean()), 5),
                 scoring_kernel_gbps=round(ck2 / (float(k2.mean()) * 1e-3) / 1e9, 1), replicas=len(sets))
             log(f"[bench] csa 128k: {ms2:.4f} ms/step")
+            del sets
+            torch.cuda.empty_cache()
+        # ---- ragged pair with the FP4 (MXFP4) indexer the pages describe -----
+        if only in (None, "ragged4"):
+            w6 = synth.make("ragged_pair_32", idx_fmt="mxfp4")
+            L6 = [int(x) for x in w6.lengths]
+            cb6, ck6 = csa_bytes(L6, key_bytes=KEY_BYTES_FP4, qiw_bytes=QI_W_BYTES_FP4)
+            hb6, _ = hca_bytes(L6)
+            sets = replicate(device_layers(w6), cb6 + hb6)
+            ms6, k6 = Timed("ragged4", sets).run(args.steps, args.warmup, prof_layer=0, prof_kind="select")
+            k6m = float(k6.mean())
+            secondary["ragged_pair_32_mxfp4_indexer"] = dict(
+                tokens_per_s=round(w6.B / (ms6 * 1e-3), 1), ms_per_step=round(ms6, 4),
+                hbm_gbps=round((cb6 + hb6) / (ms6 * 1e-3) / 1e9, 1), bytes_per_step=cb6 + hb6,
+                scoring_kernel_ms=round(k6m, 5), scoring_key_bytes=ck6,
+                scoring_kernel_gbps=round(ck6 / (k6m * 1e-3) / 1e9, 1),
+                scoring_hbm_frac=round(ck6 / (k6m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), replicas=len(sets))
+            log(f"[bench] ragged pair (MXFP4 indexer): {ms6:.4f} ms/step, scoring kernel {k6m:.4f} ms")
             del sets
             torch.cuda.empty_cache()
         # ---- HCA decode at 1M ----------------------------------------------

@@ -171,8 +171,13 @@ __global__ void __launch_bounds__(256) select_small_f64_kernel(IndexerArgs a) {
 #endif
 // 32-entry tiles per wave: fewer, larger workgroups amortize the per-workgroup
 // query/weight loads and histogram traffic when there are thousands of queries
-template <int FMT> constexpr int tiles_per_wave() { return FMT == HCA_MXFP4 ? HCA_SCORE_TPW4 : HCA_SCORE_TPW; }
-template <int FMT> constexpr int entries_per_wg() { return 4 * 32 * tiles_per_wave<FMT>(); }
+// MXFP4 keys with few queries (decode: each query reads its own sequence's keys, nothing
+// shared through L2) use the decode tiling of the FP8 path
+#ifndef HCA_SCORE_TPW4D
+#define HCA_SCORE_TPW4D 8
+#endif
+constexpr int kFewQ = 256;                               // fewer queries: decode tiling for MXFP4
+constexpr int entries_per_wg_t(int tpw) { return 4 * 32 * tpw; }
 constexpr int kRing = HCA_SCORE_RING;                    // tiles in flight per wave
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -231,15 +236,16 @@ __device__ __forceinline__ float head_sum(const v16f (&acc)[2], const float (&wv
 #ifndef HCA_SCORE_XCD_MAJOR
 #define HCA_SCORE_XCD_MAJOR 1
 #endif
-template <int FMT, bool XQ, int HT>
+// TPW: 32-entry tiles per wave (1024 entries per workgroup at 8)
+template <int FMT, bool XQ, int HT, int TPW>
 __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
-  constexpr bool kStage = FMT == HCA_FP8_E4M3;          // scores staged in LDS, one write per wave
-  static_assert(!kStage || (32 * tiles_per_wave<FMT>()) % 256 == 0, "staged scores: whole 16-byte groups per lane");
+  // scores staged in LDS and written once per wave (whole 16-byte groups per lane)
+  constexpr bool kStage = TPW <= 16 && (32 * TPW) % 256 == 0;
   __shared__ uint32_t s_hist[kBins];
   __shared__ v8bf s_qa[2][8][64];                        // FP8 path: widened query operands, per lane
-  __shared__ __attribute__((aligned(16))) float s_st[kStage ? kScoreThreads / 64 : 1][kStage ? 32 * tiles_per_wave<FMT>() : 4];
+  __shared__ __attribute__((aligned(16))) float s_st[kStage ? kScoreThreads / 64 : 1][kStage ? 32 * TPW : 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, u = lane >> 5;
   int n;
@@ -255,8 +261,8 @@ score_quant_kernel(IndexerArgs a) {
     chunk = blockIdx.x;
   }
   const int64_t V = visible(a, n);
-  constexpr int kTilesPerWave = tiles_per_wave<FMT>();
-  const int64_t ebase = chunk * entries_per_wg<FMT>();
+  constexpr int kTilesPerWave = TPW;
+  const int64_t ebase = chunk * entries_per_wg_t(TPW);
   if (ebase >= V) return;                               // uniform over the workgroup
   const int64_t row0 = a.cache_row_start[a.seq_id[n]];
   const int64_t wbase = ebase + wave * 32 * kTilesPerWave;
@@ -984,21 +990,28 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
-  const int64_t epw = a.fmt == HCA_MXFP4 ? entries_per_wg<HCA_MXFP4>() : entries_per_wg<HCA_FP8_E4M3>();
+  // MXFP4 with few queries takes the decode tiling (chunk-major, HCA_SCORE_TPW4D tiles)
+  const bool few4 = a.fmt == HCA_MXFP4 && a.Nq < kFewQ;
+  const int tpw = a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : few4 ? HCA_SCORE_TPW4D : HCA_SCORE_TPW4;
+  const int64_t epw = entries_per_wg_t(tpw);
   const int64_t chunks = (a.max_visible + epw - 1) / epw;
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
     const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
     const bool h2 = a.H_I == 64;
+    constexpr int T8 = HCA_SCORE_TPW, T4 = HCA_SCORE_TPW4, T4D = HCA_SCORE_TPW4D;
     if (a.fmt == HCA_FP8_E4M3) {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 2>), g2, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 1>), g2, dim3(kScoreThreads), 0, s, a);
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 2, T8>), g2, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 1, T8>), g2, dim3(kScoreThreads), 0, s, a);
+    } else if (few4) {
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2, T4D>), g2, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1, T4D>), g2, dim3(kScoreThreads), 0, s, a);
     } else if (HCA_SCORE_XCD_MAJOR) {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 2>), gx, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 1>), gx, dim3(kScoreThreads), 0, s, a);
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 2, T4>), gx, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 1, T4>), gx, dim3(kScoreThreads), 0, s, a);
     } else {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2>), g2, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1>), g2, dim3(kScoreThreads), 0, s, a);
+      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2, T4>), g2, dim3(kScoreThreads), 0, s, a);
+      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1, T4>), g2, dim3(kScoreThreads), 0, s, a);
     }
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);

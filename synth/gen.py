@@ -245,15 +245,16 @@ def ragged_lengths(seed: int, B: int, lo: int, hi: int, round_every4: bool = Fal
 
 
 def ragged_pair(seed: int = 4, B: int = 32, lo: int = 4096, hi: int = 1048576,
-                round_every4: bool = False, g: Geometry | None = None):
+                round_every4: bool = False, g: Geometry | None = None, idx_fmt: str = "fp8"):
     """A CSA layer then an HCA layer, each a decode step for B ragged sequences.
-    The two layers get independent inputs."""
+    The two layers get independent inputs.  ``idx_fmt`` is the CSA indexer's storage
+    ("fp8", or "mxfp4" for the FP4 indexer the pages describe)."""
     from .configs import FULL_GEOMETRY
     g = g or FULL_GEOMETRY
     lengths = ragged_lengths(seed, B, lo, hi, round_every4)
     rng = np.random.default_rng(seed)
     W_cap = max(g.n_win, g.m_hca)
-    csa = _decode_layer(rng, g, "csa", lengths, W_cap, 1.0, "fp8")
+    csa = _decode_layer(rng, g, "csa", lengths, W_cap, 1.0, idx_fmt)
     hca = _decode_layer(rng, g, "hca", lengths, W_cap, 1.0)
     return SimpleNamespace(name="ragged_pair", kind="ragged_pair", g=g, seed=seed, B=B,
                            lengths=lengths, layers=[csa, hca])

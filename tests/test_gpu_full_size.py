@@ -21,11 +21,12 @@ def _print(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("name", ["csa_decode_128k", "hca_decode_1m", "ragged_pair_32"])
-def test_full_size_decode_every_query(gpu, name):
-    w = synth.make(name)
+@pytest.mark.parametrize("name,over", [("csa_decode_128k", {}), ("hca_decode_1m", {}), ("ragged_pair_32", {}),
+                                       ("ragged_pair_32", {"idx_fmt": "mxfp4"})])
+def test_full_size_decode_every_query(gpu, name, over):
+    w = synth.make(name, **over)
     for lay in w.layers:
-        _print(f"{name} layer={lay.mode} queries={len(lay.q_pos)} "
+        _print(f"{name} {over} layer={lay.mode} queries={len(lay.q_pos)} "
                f"lengths={[int(x) for x in w.lengths]}")
         ref, dev, err = run_and_compare(lay, w.g)
         assert len(ref["queries"]) == len(lay.q_pos)

@@ -63,6 +63,25 @@ def test_csa_decode_many_short_queries(gpu, B):
     _print(f"  rel err {err:.2e}")
 
 
+def test_csa_decode_mxfp4(gpu):
+    # the FP4 indexer in decode: MXFP4 keys and queries, decode tiling; lengths with
+    # ragged tails and pooling in the step
+    g = synth.FULL_GEOMETRY
+    from synth.gen import _decode_layer
+    lay = _decode_layer(np.random.default_rng(19), g, "csa", np.array([8192, 4099, 20001, 1023, 5000], np.int64),
+                        128, 1.0, "mxfp4")
+    _print("csa decode MXFP4 indexer, 5 ragged lengths")
+    ref, dev, err = run_and_compare(lay, g)
+    _print(f"  rel err {err:.2e}")
+
+
+def test_ragged_pair_mxfp4_small(gpu):
+    w = synth.ragged_pair(seed=20, B=6, lo=1024, hi=65536, round_every4=True, idx_fmt="mxfp4")
+    for lay in w.layers:
+        _print(f"ragged pair (MXFP4 indexer) layer={lay.mode} lengths={w.lengths.tolist()}")
+        run_and_compare(lay, w.g)
+
+
 def test_hca_decode_small(gpu):
     w = synth.hca_decode(seed=13, B=2, L=65536)
     _print("hca decode B=2 L=65536")
