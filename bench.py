@@ -147,9 +147,11 @@ def replicate(layers, step_bytes, min_total=1 << 30, cap=64):
     return sets
 
 
-def device_layers(w):
+def device_layers(w, page_rows=None):
+    """Resident device layers; ``page_rows`` = {"csa": rows, "hca": rows} lays each
+    layer's compressed cache out in shuffled pages of that many entries."""
     from long_context_attention_softmax_amd.layer import DeviceLayer
-    return [DeviceLayer.from_host(l, w.g) for l in w.layers]
+    return [DeviceLayer.from_host(l, w.g, page_rows=(page_rows or {}).get(l.mode)) for l in w.layers]
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -187,7 +189,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
-    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|hca|prefill)")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -279,6 +281,24 @@ def main():
                 scoring_kernel_gbps=round(ck6 / (k6m * 1e-3) / 1e9, 1),
                 scoring_hbm_frac=round(ck6 / (k6m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), replicas=len(sets))
             log(f"[bench] ragged pair (MXFP4 indexer): {ms6:.4f} ms/step, scoring kernel {k6m:.4f} ms")
+            del sets
+            torch.cuda.empty_cache()
+        # ---- ragged pair over a paged cache (block tables, shuffled pages) ---
+        if only in (None, "paged"):
+            w7 = synth.make("ragged_pair_32")
+            L7 = [int(x) for x in w7.lengths]
+            cb7, ck7 = csa_bytes(L7)
+            hb7, _ = hca_bytes(L7)
+            pages = {"csa": 256, "hca": 16}
+            sets = replicate(device_layers(w7, pages), cb7 + hb7)
+            ms7, k7 = Timed("paged", sets).run(args.steps, args.warmup, prof_layer=0, prof_kind="select")
+            k7m = float(k7.mean())
+            secondary["ragged_pair_32_paged"] = dict(
+                tokens_per_s=round(w7.B / (ms7 * 1e-3), 1), ms_per_step=round(ms7, 4),
+                hbm_gbps=round((cb7 + hb7) / (ms7 * 1e-3) / 1e9, 1), bytes_per_step=cb7 + hb7,
+                page_rows=pages, scoring_kernel_ms=round(k7m, 5),
+                scoring_kernel_gbps=round(ck7 / (k7m * 1e-3) / 1e9, 1), replicas=len(sets))
+            log(f"[bench] ragged pair (paged cache): {ms7:.4f} ms/step, scoring kernel {k7m:.4f} ms")
             del sets
             torch.cuda.empty_cache()
         # ---- HCA decode at 1M ----------------------------------------------

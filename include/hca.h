@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 1
+#define HCA_ABI_VERSION 2
 
 /* status codes */
 #define HCA_OK             0
@@ -161,7 +161,8 @@ typedef struct hca_kv_compress_desc {
  *
  * Query n belongs to sequence seq_id[n] and sits at absolute position q_pos[n];
  * it sees entries j < V = floor((q_pos[n] + 1) / m) of its sequence, stored at
- * key rows cache_row_start[seq] + j.  For every visible j:
+ * key rows cache_row_start[seq] + j (or through the page table, below).  For
+ * every visible j:
  *   d_h   = q[n, h] . key[j]                        (exact)
  *   I_j   = sum_h w[n, h] * max(d_h, 0)
  * Quantized operands (FP8 or MXFP4, same format for q and keys; d_I = 128,
@@ -175,9 +176,9 @@ typedef struct hca_kv_compress_desc {
  * scores in the same order (f32, or f64 for F32 operands).
  * max_visible must bound V for every query.  q and keys share `fmt`; `q` has
  * Nq*H_I rows (row n*H_I + h).  w is [Nq, H_I] f32 with w >= 0.
- * Quantized keys: max_visible <= 2^23, and max_visible times the key (and, for
- * MXFP4, key-scale) pitch must stay below 2^32 bytes; otherwise
- * HCA_E_UNSUPPORTED.
+ * Quantized keys: max_visible <= 2^23, key (and, for MXFP4, key-scale) pitches
+ * below 2^24 bytes, and max_visible times each such pitch (page_rows times it,
+ * with a page table) below 2^32 bytes; otherwise HCA_E_UNSUPPORTED.
  */
 typedef struct hca_indexer_topk_desc {
   uint32_t struct_size;
@@ -198,6 +199,22 @@ typedef struct hca_indexer_topk_desc {
      and after the scoring kernel, for timing it in isolation; NULL = none */
   void*          prof_begin;
   void*          prof_end;
+  /* Paged compressed cache (optional; NULL = contiguous rows from cache_row_start,
+     which is then required).  "DeepSeek V4 infrastructure" (volanea.com), "Compression
+     only works if the attention path is engineered end to end", asks for a cache
+     format that holds up under continuous batching; the block table is this
+     library's reading of it.  With a page table, entry j of sequence b lives at
+     cache row page_table[b * page_table_pitch + j / page_rows] * page_rows +
+     j % page_rows, and cache_row_start is not read (may be NULL).  page_rows is a
+     power of two in [1, 2^24] (at least 32 for quantized indexer keys);
+     page_table_pitch >= ceil(max_visible / page_rows); every page id a visible
+     entry needs must name a page inside the cache (not checked: the table is
+     device memory).  Bad page_rows or pitch: HCA_E_SHAPE; page_rows below the
+     minimum: HCA_E_UNSUPPORTED. */
+  const int32_t* page_table;
+  int64_t        page_table_pitch;
+  int32_t        page_rows;
+  int32_t        reserved_page;
 } hca_indexer_topk_desc;
 
 /*
@@ -212,7 +229,8 @@ typedef struct hca_indexer_topk_desc {
  *     as hca_indexer_topk writes it);  HCA: every entry j < floor((t+1)/m);
  *   - the window tokens u = max(0, t-n_win+1) .. t read from the ring `win`
  *     (row b*win_cap + u mod win_cap, un-rotated, io_fmt), RoPE-rotated at u;
- * and entry j lives at cache row cache_row_start[b] + j (an idx value outside
+ * and entry j lives at cache row cache_row_start[b] + j, or through the page
+ * table (see the descriptor; an idx value outside
  * [0, floor((t+1)/m)) is skipped, never dereferenced).  The query's RoPE slice
  * is rotated at t.  With logits l_a = tau * q_hat . kappa_a and the per-head sink
  * logit sigma_h (not scaled by tau, zero value vector):
@@ -250,6 +268,22 @@ typedef struct hca_attn_desc {
      kernel (the split combine excluded); NULL = none */
   void*          prof_begin;
   void*          prof_end;
+  /* Paged compressed cache (optional; NULL = contiguous rows from cache_row_start,
+     which is then required).  "DeepSeek V4 infrastructure" (volanea.com), "Compression
+     only works if the attention path is engineered end to end", asks for a cache
+     format that holds up under continuous batching; the block table is this
+     library's reading of it.  With a page table, entry j of sequence b lives at
+     cache row page_table[b * page_table_pitch + j / page_rows] * page_rows +
+     j % page_rows, and cache_row_start is not read (may be NULL).  page_rows is a
+     power of two in [1, 2^24] (at least 32 for quantized indexer keys);
+     page_table_pitch >= ceil(max_visible / page_rows); every page id a visible
+     entry needs must name a page inside the cache (not checked: the table is
+     device memory).  Bad page_rows or pitch: HCA_E_SHAPE; page_rows below the
+     minimum: HCA_E_UNSUPPORTED. */
+  const int32_t* page_table;
+  int64_t        page_table_pitch;
+  int32_t        page_rows;
+  int32_t        reserved_page;
 } hca_attn_desc;
 
 int         hca_abi_version(void);

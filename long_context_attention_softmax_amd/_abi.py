@@ -57,7 +57,9 @@ class IndexerTopkDesc(ctypes.Structure):
                 ("cache_row_start", c_void_p), ("seq_id", c_void_p), ("q_pos", c_void_p),
                 ("idx", c_void_p), ("score", c_void_p),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-                ("prof_begin", c_void_p), ("prof_end", c_void_p)]
+                ("prof_begin", c_void_p), ("prof_end", c_void_p),
+                ("page_table", c_void_p), ("page_table_pitch", c_int64), ("page_rows", c_int32),
+                ("reserved_page", c_int32)]
 
 
 class AttnDesc(ctypes.Structure):
@@ -69,7 +71,9 @@ class AttnDesc(ctypes.Structure):
                 ("idx", c_void_p), ("win", c_void_p), ("win_pitch", c_int64), ("sink", c_void_p),
                 ("seq_id", c_void_p), ("q_pos", c_void_p), ("o", c_void_p), ("lse", c_void_p),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-                ("prof_begin", c_void_p), ("prof_end", c_void_p)]
+                ("prof_begin", c_void_p), ("prof_end", c_void_p),
+                ("page_table", c_void_p), ("page_table_pitch", c_int64), ("page_rows", c_int32),
+                ("reserved_page", c_int32)]
 
 
 class HcaError(RuntimeError):

@@ -55,7 +55,7 @@ __device__ __forceinline__ SetInfo set_info_pos(const AttnArgs& a, int64_t t) {
 
 __device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
   SetInfo si = set_info_pos(a, a.q_pos[n]);
-  si.row0 = a.cache_row_start[a.seq_id[n]];
+  si.row0 = a.page_shift < 0 ? a.cache_row_start[a.seq_id[n]] : 0;   // paged: rows through the table
   return si;
 }
 
@@ -74,7 +74,8 @@ __device__ double key_elem_f64(const AttnArgs& a, const SetInfo& si, int n, int 
   if (p < si.n_ent) {
     int64_t j = (a.mode == HCA_MODE_CSA) ? a.idx[(int64_t)n * a.k + p] : p;
     if (j < 0 || j >= si.V) return 0.0;
-    return (double)reinterpret_cast<const float*>(a.c_f32 + (si.row0 + j) * a.c_f32_pitch)[d];
+    const int64_t row = cache_row(a.page_table, a.page_pitch, a.page_shift, a.seq_id[n], si.row0, j);
+    return (double)reinterpret_cast<const float*>(a.c_f32 + row * a.c_f32_pitch)[d];
   }
   const int64_t u = si.u0 + (p - si.n_ent);
   const int64_t row = (int64_t)a.seq_id[n] * a.win_cap + u % a.win_cap;
@@ -274,13 +275,15 @@ __device__ __forceinline__ int key_kind(const QInfo& qi, int p, int jrow, bool c
 
 // Loads of one key's share, issued without any branch so that they stay in flight
 // while the previous chunk is computed: a key that is not a valid entry reads
-// row 0 of its sequence (the caller guarantees V >= 1) and is masked by `kind`.
+// entry 0 of its sequence (the caller guarantees V >= 1) and is masked by `kind`.
+// Paged caches add one dependent load per key (its page id; the 16 threads of a key
+// read the same one).
 __device__ __forceinline__ EntryRegs entry_load(const AttnArgs& a, const QInfo& qi, int p, int jrow, int q,
                                                 bool csa) {
   EntryRegs e;
   e.kind = key_kind(qi, p, jrow, csa);
   const int64_t j = e.kind == kEntry ? (csa ? (int64_t)jrow : (int64_t)p) : 0;
-  const int64_t row = qi.row0 + j;
+  const int64_t row = cache_row(a.page_table, a.page_pitch, a.page_shift, qi.b, qi.row0, j);
   const char* nope = a.c_nope + row * a.c_nope_pitch + 8 * q;
   e.f0 = *reinterpret_cast<const u2*>(nope);
   e.f1 = *reinterpret_cast<const u2*>(nope + 128);
@@ -414,7 +417,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
     int64_t row0 = 0;
     if (tid < a.Nq) {
       const int b = a.seq_id[tid];
-      row0 = a.cache_row_start[b];
+      row0 = a.page_shift < 0 ? a.cache_row_start[b] : 0;   // paged: rows through the table
       QInfo qi = query_info_pos(a, tid, b);
       s_qi[tid] = qi;
       cnt = (qi.n_set + KC - 1) / KC;

@@ -29,6 +29,29 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// The optional page table of a cache (indexer keys or attention entries).
+int check_pages(const int32_t* table, int64_t pitch, int32_t rows, int64_t max_visible, const int64_t* crs,
+                int min_rows) {
+  if (!table) {
+    REQUIRE(crs, HCA_E_NULL, "cache_row_start is required without a page table");
+    return HCA_OK;
+  }
+  REQUIRE(rows >= 1 && rows <= (1 << 24) && (rows & (rows - 1)) == 0, HCA_E_SHAPE,
+          "page_rows=%d must be a power of two in [1, 2^24]", rows);
+  REQUIRE(rows >= min_rows, HCA_E_UNSUPPORTED, "page_rows=%d below %d", rows, min_rows);
+  REQUIRE(pitch >= (max_visible + rows - 1) / rows, HCA_E_SHAPE,
+          "page_table_pitch %lld < ceil(max_visible / page_rows)", (long long)pitch);
+  REQUIRE(aligned(table, 4), HCA_E_ALIGN, "page_table misaligned");
+  return HCA_OK;
+}
+
+int log2_exact(int32_t v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+
 int check_kv_planes(const hca_kv_planes& p, int D, int D_r, const char* what, bool need) {
   if (p.fmt == HCA_F32) {
     if (!need) return HCA_OK;
@@ -114,8 +137,11 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
   }
   *ws = hca::indexer_workspace_bytes(d->Nq, d->max_visible, fmt, d->k);
   if (d->Nq == 0) return HCA_OK;
-  REQUIRE(d->q.data && d->keys.data && d->w && d->cache_row_start && d->seq_id && d->q_pos && d->idx,
-          HCA_E_NULL, "q, keys, w, cache_row_start, seq_id, q_pos and idx are required");
+  REQUIRE(d->q.data && d->keys.data && d->w && d->seq_id && d->q_pos && d->idx,
+          HCA_E_NULL, "q, keys, w, seq_id, q_pos and idx are required");
+  int prc = check_pages(d->page_table, d->page_table_pitch, d->page_rows, d->max_visible, d->cache_row_start,
+                        fmt == HCA_F32 ? 1 : 32);     // quantized scoring: a 32-entry tile within one page
+  if (prc) return prc;
   const int64_t row_bytes = fmt == HCA_F32 ? 4LL * d->d_I : (fmt == HCA_FP8_E4M3 ? d->d_I : d->d_I / 2);
   REQUIRE(d->q.pitch >= row_bytes && d->keys.pitch >= row_bytes, HCA_E_SHAPE, "q/keys pitch < row bytes");
   if (fmt != HCA_F32) {
@@ -131,10 +157,13 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
     REQUIRE(aligned(d->keys.scales, 4) && d->keys.scale_pitch % 4 == 0, HCA_E_ALIGN,
             "MXFP4 key scale rows must be 4-byte aligned");
   }
-  if (fmt != HCA_F32) {   // the scoring kernel addresses a sequence's key rows with 32-bit offsets
-    REQUIRE(d->keys.pitch * d->max_visible < (1LL << 32) &&
-            (fmt != HCA_MXFP4 || d->keys.scale_pitch * d->max_visible < (1LL << 32)),
-            HCA_E_UNSUPPORTED, "max_visible x key pitch must be < 2^32 bytes");
+  if (fmt != HCA_F32) {   // the scoring kernel addresses key rows with 32-bit offsets from a sequence or page base
+    const int64_t span = d->page_table ? (int64_t)d->page_rows : d->max_visible;
+    REQUIRE(d->keys.pitch * span < (1LL << 32) && (fmt != HCA_MXFP4 || d->keys.scale_pitch * span < (1LL << 32)),
+            HCA_E_UNSUPPORTED, "max_visible (page_rows with pages) x key pitch must be < 2^32 bytes");
+    // ... formed by a 24-bit multiply of the row number and the pitch
+    REQUIRE(d->keys.pitch < (1LL << 24) && (fmt != HCA_MXFP4 || d->keys.scale_pitch < (1LL << 24)),
+            HCA_E_UNSUPPORTED, "quantized key pitches must be < 2^24 bytes");
   }
   REQUIRE(aligned(d->w, 4) && aligned(d->idx, 4) && aligned(d->cache_row_start, 8) && aligned(d->q_pos, 8) &&
           aligned(d->seq_id, 4), HCA_E_ALIGN, "w/idx/cache_row_start/q_pos/seq_id misaligned");
@@ -173,8 +202,10 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   *ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
                                        d->io_fmt == HCA_F32, prefill);
   if (d->Nq == 0) return HCA_OK;
-  REQUIRE(d->q && d->o && d->win && d->sink && d->seq_id && d->q_pos && d->cache_row_start, HCA_E_NULL,
-          "q, o, win, sink, seq_id, q_pos and cache_row_start are required");
+  REQUIRE(d->q && d->o && d->win && d->sink && d->seq_id && d->q_pos, HCA_E_NULL,
+          "q, o, win, sink, seq_id and q_pos are required");
+  int prc = check_pages(d->page_table, d->page_table_pitch, d->page_rows, d->max_visible, d->cache_row_start, 1);
+  if (prc) return prc;
   REQUIRE(d->mode == HCA_MODE_HCA || d->idx, HCA_E_NULL, "CSA needs idx");
   int rc = check_kv_planes(d->cache, d->D, d->D_r, "cache", true);
   if (rc) return rc;
@@ -220,6 +251,8 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   a.c_rope = static_cast<const char*>(d->cache.rope); a.c_rope_pitch = d->cache.rope_pitch;
   a.c_scale = static_cast<const float*>(d->cache.scale);
   a.cache_row_start = d->cache_row_start; a.idx = d->mode == HCA_MODE_CSA ? d->idx : nullptr;
+  a.page_table = d->page_table; a.page_pitch = d->page_table_pitch;
+  a.page_shift = d->page_table ? log2_exact(d->page_rows) : -1;
   a.win = static_cast<const char*>(d->win); a.win_pitch = d->win_pitch;
   a.sink = d->sink; a.seq_id = d->seq_id; a.q_pos = d->q_pos; a.o = d->o; a.lse = d->lse;
   a.workspace = d->workspace; a.prefill = prefill;
@@ -321,6 +354,8 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
   a.keys = static_cast<const char*>(d->keys.data); a.key_pitch = d->keys.pitch;
   a.key_scales = static_cast<const uint8_t*>(d->keys.scales); a.key_scale_pitch = d->keys.scale_pitch;
   a.cache_row_start = d->cache_row_start; a.seq_id = d->seq_id; a.q_pos = d->q_pos;
+  a.page_table = d->page_table; a.page_pitch = d->page_table_pitch;
+  a.page_shift = d->page_table ? log2_exact(d->page_rows) : -1;
   a.idx = d->idx; a.score_out = d->score;
   a.scores = d->workspace;             // the workspace layout is laid out by the launcher
   a.hist = nullptr;

@@ -28,6 +28,13 @@ struct PoolArgs {
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
+// Cache row of entry j of sequence b: contiguous from row0, or through the page table.
+__device__ __forceinline__ int64_t cache_row(const int32_t* pt, int64_t pitch, int shift, int b, int64_t row0,
+                                             int64_t j) {
+  if (shift < 0) return row0 + j;
+  return ((int64_t)pt[(int64_t)b * pitch + (j >> shift)] << shift) + (j & ((1LL << shift) - 1));
+}
+
 struct IndexerArgs {
   int Nq, H_I, d_I, k, m, fmt;        // fmt: HCA_F32 | HCA_FP8_E4M3 | HCA_MXFP4
   int64_t max_visible, score_pitch;   // score_pitch: elements per query row of the workspace
@@ -39,6 +46,7 @@ struct IndexerArgs {
   void* scores;                       // workspace: f32 (quantized) or f64 (F32) [Nq, score_pitch]
   uint32_t* hist;                     // workspace: [Nq, 2048] (quantized only)
   hipEvent_t prof_begin, prof_end;    // optional, around the scoring kernel
+  const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged keys (page_shift >= 0)
 };
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k);
@@ -60,6 +68,7 @@ struct AttnArgs {
   void* workspace;
   int prefill;
   hipEvent_t prof_begin, prof_end;    // optional, around the attention kernel
+  const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged entries (page_shift >= 0)
   double inv_turn[32];                // BF16 path: rope_base^(-2i/64) / (2 pi), turns per position
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -105,7 +105,10 @@ __global__ void __launch_bounds__(256) score_f64_kernel(IndexerArgs a) {
   __syncthreads();
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= V) return;
-  const float* k = reinterpret_cast<const float*>(a.keys + (a.cache_row_start[a.seq_id[n]] + j) * a.key_pitch);
+  const int b = a.seq_id[n];
+  const int64_t row = cache_row(a.page_table, a.page_pitch, a.page_shift, b,
+                                a.page_shift < 0 ? a.cache_row_start[b] : 0, j);
+  const float* k = reinterpret_cast<const float*>(a.keys + row * a.key_pitch);
   double acc = 0.0;
   for (int h = 0; h < a.H_I; ++h) {
     double d = 0.0;
@@ -236,8 +239,9 @@ __device__ __forceinline__ float head_sum(const v16f (&acc)[2], const float (&wv
 #ifndef HCA_SCORE_XCD_MAJOR
 #define HCA_SCORE_XCD_MAJOR 1
 #endif
-// TPW: 32-entry tiles per wave (1024 entries per workgroup at 8)
-template <int FMT, bool XQ, int HT, int TPW>
+// TPW: 32-entry tiles per wave (1024 entries per workgroup at 8).  PAGED: key rows
+// come through the page table, one page per 32-entry tile.
+template <int FMT, bool XQ, int HT, int TPW, bool PAGED>
 __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
 score_quant_kernel(IndexerArgs a) {
 #pragma clang fp contract(off)
@@ -264,7 +268,8 @@ score_quant_kernel(IndexerArgs a) {
   constexpr int kTilesPerWave = TPW;
   const int64_t ebase = chunk * entries_per_wg_t(TPW);
   if (ebase >= V) return;                               // uniform over the workgroup
-  const int64_t row0 = a.cache_row_start[a.seq_id[n]];
+  const int bseq = a.seq_id[n];
+  const int64_t row0 = PAGED ? 0 : a.cache_row_start[bseq];
   const int64_t wbase = ebase + wave * 32 * kTilesPerWave;
 
   // keys stream through a ring of kRing tiles per wave: tile t + kRing is loaded
@@ -277,7 +282,8 @@ score_quant_kernel(IndexerArgs a) {
   // key only, and those columns are never stored.
   // Rows are addressed by 32-bit byte offsets from the sequence's first row
   // (entries < 2^23 and max_visible x pitch < 2^32, checked by the caller), so a
-  // tile costs one full-rate 24-bit multiply per plane.
+  // tile costs one full-rate 24-bit multiply per plane.  Paged, the offsets are
+  // from the first row of the tile's page (pages hold a power of two >= 32 rows).
   const char* const kseq = a.keys + row0 * a.key_pitch;
   const uint8_t* const sseq = FMT == HCA_MXFP4 ? a.key_scales + row0 * a.key_scale_pitch : nullptr;
   const uint32_t j0 = (uint32_t)(wbase + jl), jmax = (uint32_t)(V - 1);
@@ -285,9 +291,27 @@ score_quant_kernel(IndexerArgs a) {
   // MXFP4: the entry's four E8M0 block scales are one aligned 32-bit word; shifted
   // by 8u, its bytes 0 and 2 are this lane's blocks u and 2 + u, which the scaled
   // product selects with op_sel
+  // Paged: lane t < TPW loads the page id of the wave's tile t up front, in one
+  // vector load, so no key load waits on a lookup of its own.  Every lane of tile t
+  // reads an entry of the 32-entry tile that starts at ts: the tile's own start, or
+  // the last visible entry's tile when the tile lies wholly past it.
+  static_assert(TPW <= 64, "one page id per lane");
+  int page_of_tile = 0;
+  if constexpr (PAGED) {
+    const uint32_t ts = min((uint32_t)wbase + 32u * (uint32_t)min(lane, TPW - 1), jmax & ~31u);
+    page_of_tile = a.page_table[(int64_t)bseq * a.page_pitch + (ts >> a.page_shift)];
+  }
   auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2]) {
-    const uint32_t j = min(j0 + 32u * (uint32_t)t, jmax);
-    const char* key = kseq + (uint32_t)((uint32_t)__umul24(j, (uint32_t)a.key_pitch) + lane_off);
+    uint32_t j = min(j0 + 32u * (uint32_t)t, jmax);
+    const char* kb = kseq;
+    const uint8_t* sb = sseq;
+    if constexpr (PAGED) {
+      const int64_t prow = (int64_t)__builtin_amdgcn_readlane(page_of_tile, t) << a.page_shift;
+      kb = a.keys + prow * a.key_pitch;
+      if (FMT == HCA_MXFP4) sb = a.key_scales + prow * a.key_scale_pitch;
+      j &= (1u << a.page_shift) - 1u;
+    }
+    const char* key = kb + (uint32_t)((uint32_t)__umul24(j, (uint32_t)a.key_pitch) + lane_off);
     if (FMT == HCA_FP8_E4M3) {
       const uint4* p = reinterpret_cast<const uint4*>(key);
 #pragma unroll
@@ -295,7 +319,7 @@ score_quant_kernel(IndexerArgs a) {
     } else {
       dst[0] = *reinterpret_cast<const uint4*>(key);
       dst[1] = *reinterpret_cast<const uint4*>(key + 32);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(sseq + (uint32_t)__umul24(j, (uint32_t)a.key_scale_pitch));
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)__umul24(j, (uint32_t)a.key_scale_pitch));
       dsc[0] = (int)(w >> (8 * u));
     }
   };
@@ -949,6 +973,19 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
 }
 }  // namespace
 
+// one scoring launch; the head-tile count (H_I / 32) and paging are template arguments
+template <int FMT, bool XQ, int TPW>
+void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+  const bool h2 = a.H_I == 64;
+  if (a.page_shift >= 0) {
+    if (h2) hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 2, TPW, true>), grid, dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 1, TPW, true>), grid, dim3(kScoreThreads), 0, s, a);
+  } else {
+    if (h2) hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 2, TPW, false>), grid, dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 1, TPW, false>), grid, dim3(kScoreThreads), 0, s, a);
+  }
+}
+
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
   return ws_layout(Nq, max_visible, fmt, k).total;
 }
@@ -998,21 +1035,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   if (a.prof_begin) hipEventRecord(a.prof_begin, s);
   if (chunks > 0) {
     const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
-    const bool h2 = a.H_I == 64;
     constexpr int T8 = HCA_SCORE_TPW, T4 = HCA_SCORE_TPW4, T4D = HCA_SCORE_TPW4D;
-    if (a.fmt == HCA_FP8_E4M3) {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 2, T8>), g2, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_FP8_E4M3, false, 1, T8>), g2, dim3(kScoreThreads), 0, s, a);
-    } else if (few4) {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2, T4D>), g2, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1, T4D>), g2, dim3(kScoreThreads), 0, s, a);
-    } else if (HCA_SCORE_XCD_MAJOR) {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 2, T4>), gx, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, true, 1, T4>), gx, dim3(kScoreThreads), 0, s, a);
-    } else {
-      if (h2) hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 2, T4>), g2, dim3(kScoreThreads), 0, s, a);
-      else hipLaunchKernelGGL((score_quant_kernel<HCA_MXFP4, false, 1, T4>), g2, dim3(kScoreThreads), 0, s, a);
-    }
+    if (a.fmt == HCA_FP8_E4M3) launch_score<HCA_FP8_E4M3, false, T8>(a, g2, s);
+    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s);
+    else if (HCA_SCORE_XCD_MAJOR) launch_score<HCA_MXFP4, true, T4>(a, gx, s);
+    else launch_score<HCA_MXFP4, false, T4>(a, g2, s);
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
   dim3 cgrid((unsigned)L.nch, a.Nq);

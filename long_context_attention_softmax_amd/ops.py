@@ -41,6 +41,21 @@ def _pitch(t: torch.Tensor) -> int:
     return (t.stride(-2) if t.dim() >= 2 else t.shape[-1]) * t.element_size()
 
 
+def _set_pages(d, pages) -> None:
+    """pages = (page_table [B, pages per sequence] int32, page_rows) or None."""
+    if pages is None:
+        return
+    table, rows = pages
+    if table.dtype != torch.int32 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 [B, pages] tensor")
+    _need_cuda(table)
+    d.page_table, d.page_table_pitch, d.page_rows = _ptr(table), table.shape[1], int(rows)
+
+
+def _seqs(cache_row_start, pages) -> int:
+    return cache_row_start.numel() if cache_row_start is not None else pages[0].shape[0]
+
+
 def _i64(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
     if t.dtype != torch.int64 or t.numel() < n or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int64 tensor of >= {n} elements")
@@ -154,25 +169,29 @@ def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch
     A.check(A.lib.hca_kv_compress(ctypes.byref(d), _stream()))
 
 
-def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: torch.Tensor,
+def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: Optional[torch.Tensor],
                      seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
                      max_visible: int, idx: Optional[torch.Tensor] = None,
-                     score: Optional[torch.Tensor] = None, prof=None) -> torch.Tensor:
-    """Top-k entries per query.  q.data is [Nq, H_I, ...]; returns idx [Nq, k] int32."""
+                     score: Optional[torch.Tensor] = None, prof=None, pages=None) -> torch.Tensor:
+    """Top-k entries per query.  q.data is [Nq, H_I, ...]; returns idx [Nq, k] int32.
+    ``pages`` = (page_table, page_rows) addresses a paged key cache instead of
+    cache_row_start (see include/hca.h)."""
     Nq, H_I = q.data.shape[0], q.data.shape[1]
     d_I = q.data.shape[-1] * (2 if q.fmt == A.MXFP4 else 1)
     _need_cuda(w, cache_row_start, seq_id, q_pos, idx, score)
     if idx is None:
         idx = torch.empty((Nq, k), dtype=torch.int32, device=w.device)
     d = A.new_desc(A.IndexerTopkDesc)
-    d.Nq, d.B, d.H_I, d.d_I, d.k, d.m = Nq, cache_row_start.numel(), H_I, d_I, k, m
+    d.Nq, d.B, d.H_I, d.d_I, d.k, d.m = Nq, _seqs(cache_row_start, pages), H_I, d_I, k, m
     d.max_visible = max_visible
     d.q = q.planes()
     d.keys = keys.planes()
     if w.dtype != torch.float32 or not w.is_contiguous():
         raise ValueError("w must be contiguous float32 [Nq, H_I]")
     d.w = _ptr(w)
-    d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    if cache_row_start is not None:
+        d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    _set_pages(d, pages)
     if seq_id.dtype != torch.int32:
         raise ValueError("seq_id must be int32")
     d.seq_id = _ptr(seq_id)
@@ -188,11 +207,12 @@ def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_sta
     return idx
 
 
-def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: torch.Tensor,
+def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: Optional[torch.Tensor],
           win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
           mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
           idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
-          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None) -> torch.Tensor:
+          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None,
+          pages=None) -> torch.Tensor:
     Nq, H, D = q.shape
     _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
     io = A.F32 if q.dtype == torch.float32 else A.BF16
@@ -201,14 +221,16 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: torch
     if o is None:
         o = torch.empty_like(q)
     d = A.new_desc(A.AttnDesc)
-    d.Nq, d.B, d.H, d.D, d.D_r = Nq, cache_row_start.numel(), H, D, D_r
+    d.Nq, d.B, d.H, d.D, d.D_r = Nq, _seqs(cache_row_start, pages), H, D, D_r
     d.mode, d.m, d.k, d.n_win, d.win_cap = mode, m, k, n_win, win.shape[-2]
     d.tau, d.io_fmt, d.rope_base, d.max_visible = tau, io, rope_base, max_visible
     if not q.is_contiguous():
         raise ValueError("q must be contiguous [Nq, H, D]")
     d.q = _ptr(q)
     d.cache = cache.planes()
-    d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    if cache_row_start is not None:
+        d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
+    _set_pages(d, pages)
     if idx is not None:
         if idx.dtype != torch.int32 or not idx.is_contiguous():
             raise ValueError("idx must be contiguous int32 [Nq, k]")

@@ -40,7 +40,7 @@ def assert_codes_equal(got, want, fragile, what):
 
 def check_pool(dev, pooled, lay):
     """Compare the rows the GPU pooled with the oracle's encodings."""
-    rows = torch.from_numpy(np.asarray(pooled["out_row"], np.int64)).to(dev.device)
+    rows = torch.from_numpy(dev.phys_rows(pooled["out_row"])).to(dev.device)
     kv = pooled["kv"]
     if rows.numel() == 0:
         return
@@ -76,12 +76,14 @@ def check_pool(dev, pooled, lay):
             assert_codes_equal(hi_g, hi_w, fr[:, 1::2], "pooled MXFP4 key (odd)")
 
 
-def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, check_scores=True):
+def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, check_scores=True,
+                    page_rows=None):
     """Run the layer's step on the GPU and compare every stage with the oracle.
+    ``page_rows`` lays the compressed cache out in shuffled pages of that size.
 
-    Returns (oracle result, device layer)."""
+    Returns (oracle result, device layer, output error)."""
     from long_context_attention_softmax_amd.layer import DeviceLayer
-    dev = dev or DeviceLayer.from_host(lay, g)
+    dev = dev or DeviceLayer.from_host(lay, g, page_rows=page_rows)
     tol = tol if tol is not None else (TOL_F32 if dev.f32 else TOL_QUANT)
     dev.pool()
     score = None

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 1
+    assert A.lib.hca_abi_version() == 2
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
                     (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
@@ -129,6 +129,34 @@ def test_indexer_validation_and_workspace():
     assert call("hca_indexer_topk", idx_desc(Nq=0)) == 0
 
 
+def test_indexer_page_table_validation():
+    # the workspace is one byte short, so a call that passes every page check stops
+    # at the workspace check (the last one) and nothing is launched
+    ws = dict(workspace=FAKE, workspace_bytes=1)
+    paged = dict(cache_row_start=None, page_table=FAKE, page_table_pitch=256, page_rows=128, **ws)
+    assert call("hca_indexer_topk", idx_desc(**paged)) == -6          # NULL cache_row_start is fine with pages
+    assert call("hca_indexer_topk", idx_desc(cache_row_start=None, **ws)) == -1
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_rows=96))) == -2    # not a power of two
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_rows=0))) == -2
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_rows=1 << 25))) == -2
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_rows=16))) == -5    # a 32-entry tile spans pages
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_table_pitch=255))) == -2   # < 32768 / 128
+    assert call("hca_indexer_topk", idx_desc(**dict(paged, page_table=FAKE + 2))) == -3
+    d = idx_desc(**dict(paged, max_visible=1 << 23, page_table_pitch=1 << 16))
+    d.keys.pitch = 1024        # 2^23 rows x 1 KiB is fine when offsets are taken within a 128-row page ...
+    assert call("hca_indexer_topk", d) == -6
+    d.page_rows, d.page_table_pitch = 1 << 22, 2   # ... but not within a 2^22-row page
+    assert call("hca_indexer_topk", d) == -5
+    d = idx_desc(**ws)
+    d.keys.pitch = 1 << 24     # the row offset is a 24-bit product
+    assert call("hca_indexer_topk", d) == -5
+    d = idx_desc(**dict(paged, page_rows=1))
+    d.q.fmt = d.keys.fmt = A.F32
+    d.q.pitch = d.keys.pitch = 512
+    d.max_visible, d.page_table_pitch = 4096, 4096
+    assert call("hca_indexer_topk", d) == -6       # f64 scoring takes any page size
+
+
 def attn_desc(**kw):
     d = A.new_desc(A.AttnDesc)
     d.Nq, d.B, d.H, d.D, d.D_r, d.mode, d.m, d.k, d.n_win, d.win_cap = 8, 8, 64, 512, 64, 0, 4, 512, 128, 128
@@ -165,6 +193,21 @@ def test_attention_validation():
     assert call("hca_attn_decode", d) == -3
     assert call("hca_attn_decode", attn_desc(Nq=0)) == 0
     assert b"" != A.lib.hca_last_error()
+
+
+def test_attention_page_table_validation():
+    # seq_id is misaligned: the last check, so a call that passes the page checks
+    # stops there and nothing is launched
+    last = dict(seq_id=FAKE + 2, workspace=FAKE, workspace_bytes=1 << 40)
+    paged = dict(cache_row_start=None, page_table=FAKE, page_table_pitch=32768, page_rows=1, **last)
+    for fn in ("hca_attn_decode", "hca_attn_prefill"):
+        assert call(fn, attn_desc(cache_row_start=None, **last)) == -1
+        assert call(fn, attn_desc(**paged)) == -3                       # any power of two, even 1
+        assert b"index arrays" in A.lib.hca_last_error()
+        assert call(fn, attn_desc(**dict(paged, page_rows=3))) == -2
+        assert call(fn, attn_desc(**dict(paged, page_rows=64, page_table_pitch=511))) == -2
+        assert call(fn, attn_desc(**dict(paged, page_table=FAKE + 1))) == -3
+        assert b"page_table" in A.lib.hca_last_error()
 
 
 def test_binding_refuses_host_tensors():

@@ -21,14 +21,16 @@ def _print(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("name,over", [("csa_decode_128k", {}), ("hca_decode_1m", {}), ("ragged_pair_32", {}),
-                                       ("ragged_pair_32", {"idx_fmt": "mxfp4"})])
-def test_full_size_decode_every_query(gpu, name, over):
+@pytest.mark.parametrize("name,over,page_rows", [("csa_decode_128k", {}, None), ("hca_decode_1m", {}, None),
+                                                 ("ragged_pair_32", {}, None),
+                                                 ("ragged_pair_32", {"idx_fmt": "mxfp4"}, None),
+                                                 ("ragged_pair_32", {}, 256)])
+def test_full_size_decode_every_query(gpu, name, over, page_rows):
     w = synth.make(name, **over)
     for lay in w.layers:
-        _print(f"{name} {over} layer={lay.mode} queries={len(lay.q_pos)} "
+        _print(f"{name} {over} page_rows={page_rows} layer={lay.mode} queries={len(lay.q_pos)} "
                f"lengths={[int(x) for x in w.lengths]}")
-        ref, dev, err = run_and_compare(lay, w.g)
+        ref, dev, err = run_and_compare(lay, w.g, page_rows=page_rows)
         assert len(ref["queries"]) == len(lay.q_pos)
         _print(f"  rel err {err:.2e}")
 
