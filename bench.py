@@ -147,11 +147,17 @@ def replicate(layers, step_bytes, min_total=1 << 30, cap=64):
     return sets
 
 
-def device_layers(w, page_rows=None):
+def device_layers(w, page_rows=None, split_chunks=None):
     """Resident device layers; ``page_rows`` = {"csa": rows, "hca": rows} lays each
-    layer's compressed cache out in shuffled pages of that many entries."""
+    layer's compressed cache out in shuffled pages of that many entries;
+    ``split_chunks`` = {"csa": n, "hca": n} selects the batch-invariant fixed split."""
     from long_context_attention_softmax_amd.layer import DeviceLayer
-    return [DeviceLayer.from_host(l, w.g, page_rows=(page_rows or {}).get(l.mode)) for l in w.layers]
+    out = []
+    for l in w.layers:
+        d = DeviceLayer.from_host(l, w.g, page_rows=(page_rows or {}).get(l.mode))
+        d.split_chunks = (split_chunks or {}).get(l.mode, 0)
+        out.append(d)
+    return out
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -189,7 +195,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
-    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|hca|prefill)")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -299,6 +305,22 @@ def main():
                 page_rows=pages, scoring_kernel_ms=round(k7m, 5),
                 scoring_kernel_gbps=round(ck7 / (k7m * 1e-3) / 1e9, 1), replicas=len(sets))
             log(f"[bench] ragged pair (paged cache): {ms7:.4f} ms/step, scoring kernel {k7m:.4f} ms")
+            del sets
+            torch.cuda.empty_cache()
+        # ---- ragged pair, batch-invariant decode (fixed split) ---------------
+        if only in (None, "invariant"):
+            w8 = synth.make("ragged_pair_32")
+            L8 = [int(x) for x in w8.lengths]
+            cb8, _ = csa_bytes(L8)
+            hb8, _ = hca_bytes(L8)
+            split = {"csa": 2, "hca": 3}
+            sets = replicate(device_layers(w8, split_chunks=split), cb8 + hb8)
+            ms8, k8 = Timed("invariant", sets).run(args.steps, args.warmup, prof_layer=1, prof_kind="attend")
+            secondary["ragged_pair_32_batch_invariant"] = dict(
+                tokens_per_s=round(w8.B / (ms8 * 1e-3), 1), ms_per_step=round(ms8, 4),
+                hbm_gbps=round((cb8 + hb8) / (ms8 * 1e-3) / 1e9, 1), bytes_per_step=cb8 + hb8,
+                split_chunks=split, hca_attention_kernel_ms=round(float(k8.mean()), 5), replicas=len(sets))
+            log(f"[bench] ragged pair (batch-invariant split): {ms8:.4f} ms/step")
             del sets
             torch.cuda.empty_cache()
         # ---- HCA decode at 1M ----------------------------------------------

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 2
+#define HCA_ABI_VERSION 3
 
 /* status codes */
 #define HCA_OK             0
@@ -283,7 +283,21 @@ typedef struct hca_attn_desc {
   const int32_t* page_table;
   int64_t        page_table_pitch;
   int32_t        page_rows;
-  int32_t        reserved_page;
+  /* Batch-invariant decode ("DeepSeek V4 infrastructure" (volanea.com), "TileLang
+     and deterministic kernels are part of the product strategy": batch-invariant,
+     deterministic kernels and bitwise reproducibility).  0 = the default decode plan, which cuts the chunks of all
+     queries (64 set slots each: entries, then window tokens) into equal runs over
+     the workgroups, so the rounding of a query's output depends on the rest of the
+     batch.  split_chunks > 0 (hca_attn_decode, BF16): each query's own chunks are
+     cut into runs of split_chunks chunks from its first chunk and the runs are
+     merged in order, so o and lse of a query are the same bits whatever the batch
+     holds and however it is ordered (for a fixed split_chunks).  A query may then
+     need at most 256 runs: ceil(ceil((min(k, max_visible) or max_visible, plus
+     n_win) / 64) / split_chunks) <= 256, else HCA_E_UNSUPPORTED; negative:
+     HCA_E_SHAPE.  Ignored by hca_attn_prefill (one workgroup per query, never split)
+     and by the F32 path (one workgroup per query and head); both are batch-invariant
+     already, as is hca_indexer_topk (exact scores, canonical top-k). */
+  int32_t        split_chunks;
 } hca_attn_desc;
 
 int         hca_abi_version(void);

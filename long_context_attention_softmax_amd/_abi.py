@@ -73,7 +73,7 @@ class AttnDesc(ctypes.Structure):
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
                 ("prof_begin", c_void_p), ("prof_end", c_void_p),
                 ("page_table", c_void_p), ("page_table_pitch", c_int64), ("page_rows", c_int32),
-                ("reserved_page", c_int32)]
+                ("split_chunks", c_int32)]
 
 
 class HcaError(RuntimeError):

@@ -158,6 +158,10 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
 // all fall in one run is finished there; otherwise each run leaves a partial
 // (max, sum, unnormalized o) in the workspace and a combine kernel merges them in
 // run order with the sink.  Prefill (many queries): one workgroup per query.
+// Fixed split (decode with split_chunks > 0): each query's own chunk list is cut
+// into runs of split_chunks chunks from its first chunk, one workgroup per run, so
+// every run boundary, partial and merge depends on that query alone and its result
+// is the same bits whatever else is in the batch.
 constexpr int kD = 512, kDr = 64, kDn = 448;
 constexpr int KC = 64;                     // keys per chunk
 constexpr int kKsPitch = kD + 8;           // bf16 per LDS key row (1040 B: rows 4 banks apart)
@@ -165,9 +169,11 @@ constexpr int kPtPitch = 16 + 4;           // bf16 per LDS row of P^T (16 heads)
 constexpr int kThreads = 512;              // 8 waves
 constexpr int kIdxWin = 2048;              // index-list positions held in LDS
 constexpr int kMaxDecodeQ = 256;           // queries of one flattened (decode) launch
+constexpr int kMaxRuns = 256;              // runs one combine workgroup merges (one thread each)
 #ifndef HCA_ATTN_GRID
 #define HCA_ATTN_GRID 256                  // workgroups of a decode launch
 #endif
+static_assert(HCA_ATTN_GRID <= kMaxRuns, "a flattened query spans at most every workgroup");
 #ifndef HCA_ATTN_MIN_CHUNKS
 #define HCA_ATTN_MIN_CHUNKS 1              // fewest chunks per decode workgroup
 #endif
@@ -351,10 +357,21 @@ struct PartialPtrs {
 
 __host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-__host__ __device__ inline PartialPtrs partial_ptrs(void* ws, int Nq, int H) {
+// Flat: equal chunk ranges over the workgroups.  Query: one workgroup per query.
+// Split: one workgroup per run (batches of more than kMaxDecodeQ queries).
+// SplitFlat: equal shares of whole runs over the workgroups.
+enum { kLayoutFlat = 0, kLayoutQuery = 1, kLayoutSplit = 2, kLayoutSplitFlat = 3 };
+
+// partial slots: one per (workgroup, query) of a flattened launch, one per run of
+// a fixed-split launch
+__host__ __device__ inline size_t partial_slots(int Nq, int split_runs) {
+  return split_runs > 0 ? (size_t)Nq * split_runs : (size_t)HCA_ATTN_GRID + Nq;
+}
+
+__host__ __device__ inline PartialPtrs partial_ptrs(void* ws, int Nq, int H, int split_runs) {
   PartialPtrs p;
   char* b = static_cast<char*>(ws);
-  const size_t slots = (size_t)HCA_ATTN_GRID + Nq;
+  const size_t slots = partial_slots(Nq, split_runs);
   const size_t hdr = round256((size_t)(Nq + 2) * 4);
   const size_t ml = round256(slots * H * 4);
   p.pref = reinterpret_cast<int*>(b);
@@ -374,14 +391,16 @@ __device__ __forceinline__ int find_query(const int* pref, int nq, int c) {
   return lo;
 }
 
-__global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_query) {
+template <int layout>
+__global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[KC * kKsPitch];
   __shared__ __attribute__((aligned(16))) float4 s_sx[8][4][64];
   __shared__ __attribute__((aligned(16))) __bf16 Pt[8][KC * kPtPitch];
   __shared__ int32_t s_idx[kIdxWin];
   __shared__ QInfo s_qi[kMaxDecodeQ];
   __shared__ int s_pref[kMaxDecodeQ + 1];
-  __shared__ int s_wsum[8];
+  __shared__ int s_rpref[layout == kLayoutSplitFlat ? kMaxDecodeQ + 1 : 1];   // run prefix
+  __shared__ int s_wsum[16];
   __shared__ double s_inv[32];
   __shared__ uint8_t s_kval[KC];
 
@@ -391,13 +410,21 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
   const int hg = wave & 3, dh = wave >> 2;
   const bool active = hg < NHG;
   const bool csa = a.mode == HCA_MODE_CSA;
+  constexpr bool per_query = layout == kLayoutQuery || layout == kLayoutSplit;
+  constexpr bool split_flat = layout == kLayoutSplitFlat;
+  constexpr bool fixed_split = layout == kLayoutSplit || layout == kLayoutSplitFlat;
 
   if (tid < 32) s_inv[tid] = a.inv_turn[tid];       // turns per position
   // ---- the chunk list and this workgroup's run [c0, c1)
   int nq_local, qbase, c0, c1;
+  int run = 0, n_runs = 1;                          // fixed split: this run, the query's runs
   PartialPtrs pp{};
   if (per_query) {
     qbase = blockIdx.x;
+    if constexpr (layout == kLayoutSplit) {
+      qbase = blockIdx.x / a.split_runs;
+      run = blockIdx.x - qbase * a.split_runs;
+    }
     nq_local = 1;
     if (tid == 0) {
       const QInfo qi = query_info(a, qbase);
@@ -408,12 +435,18 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
     __syncthreads();
     c0 = 0;
     c1 = s_pref[1];
+    if constexpr (layout == kLayoutSplit) {
+      n_runs = (c1 + a.split_chunks - 1) / a.split_chunks;
+      c0 = run * a.split_chunks;
+      c1 = min(c0 + a.split_chunks, c1);
+      pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
+    }
   } else {
     qbase = 0;
     nq_local = a.Nq;
     // the chunk counts need only the positions; the dependent cache-row load is
     // in flight during the scan and stored with the rest of the query record
-    int cnt = 0;
+    int cnt = 0, nr = 0;
     int64_t row0 = 0;
     if (tid < a.Nq) {
       const int b = a.seq_id[tid];
@@ -421,34 +454,53 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
       QInfo qi = query_info_pos(a, tid, b);
       s_qi[tid] = qi;
       cnt = (qi.n_set + KC - 1) / KC;
+      if (split_flat) nr = (cnt + a.split_chunks - 1) / a.split_chunks;
     }
-    int x = cnt;
+    int x = cnt, xr = nr;                  // inclusive scans of chunks (and runs)
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o, 64);
       if (lane >= o) x += y;
+      if constexpr (split_flat) {
+        const int yr = __shfl_up(xr, o, 64);
+        if (lane >= o) xr += yr;
+      }
     }
-    if (lane == 63) s_wsum[wave] = x;
+    if (lane == 63) { s_wsum[wave] = x; if (split_flat) s_wsum[8 + wave] = xr; }
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    if (tid < a.Nq) s_pref[tid + 1] = base + x;
-    if (tid == 0) s_pref[0] = 0;
+    int base = 0, rbase = 0;
+    for (int w = 0; w < wave; ++w) { base += s_wsum[w]; if (split_flat) rbase += s_wsum[8 + w]; }
+    if (tid < a.Nq) { s_pref[tid + 1] = base + x; if (split_flat) s_rpref[tid + 1] = rbase + xr; }
+    if (tid == 0) { s_pref[0] = 0; if (split_flat) s_rpref[0] = 0; }
     __syncthreads();
     const int total = s_pref[a.Nq];
-    int per = (total + gridDim.x - 1) / gridDim.x;
-    if (per < HCA_ATTN_MIN_CHUNKS) per = HCA_ATTN_MIN_CHUNKS;
-    pp = partial_ptrs(a.workspace, a.Nq, a.H);
-    if (blockIdx.x == 0) {
-      for (int i = tid; i <= a.Nq; i += kThreads) pp.pref[i] = s_pref[i];
-      if (tid == 0) pp.pref[a.Nq + 1] = per;
+    if constexpr (split_flat) {
+      // whole runs [r0, r1): a run is never cut, so its partial depends on its query alone
+      const int runs = s_rpref[a.Nq];
+      const int per = (runs + gridDim.x - 1) / gridDim.x;
+      const int r0 = blockIdx.x * per, r1 = min(r0 + per, runs);
+      c0 = c1 = 0;
+      if (r0 < r1) {
+        const int n0 = find_query(s_rpref, a.Nq, r0), n1 = find_query(s_rpref, a.Nq, r1 - 1);
+        c0 = s_pref[n0] + (r0 - s_rpref[n0]) * a.split_chunks;
+        c1 = min(s_pref[n1] + (r1 - s_rpref[n1]) * a.split_chunks, s_pref[n1 + 1]);
+      }
+      pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
+    } else {
+      int per = (total + gridDim.x - 1) / gridDim.x;
+      if (per < HCA_ATTN_MIN_CHUNKS) per = HCA_ATTN_MIN_CHUNKS;
+      pp = partial_ptrs(a.workspace, a.Nq, a.H, 0);
+      if (blockIdx.x == 0) {
+        for (int i = tid; i <= a.Nq; i += kThreads) pp.pref[i] = s_pref[i];
+        if (tid == 0) pp.pref[a.Nq + 1] = per;
+      }
+      c0 = blockIdx.x * per;
+      c1 = min(c0 + per, total);
     }
-    c0 = blockIdx.x * per;
-    c1 = min(c0 + per, total);
     if (tid < a.Nq) s_qi[tid].row0 = row0;
   }
-  if (c0 >= c1) {
-    if (per_query && active) {              // empty set: the sink alone, o = 0
+  if (c0 >= c1) {                           // fixed split: runs past the query's last
+    if (per_query && run == 0 && active) {  // empty set: the sink alone, o = 0
       const int n = qbase;
       const int hrow0 = 16 * hg + 4 * g;
 #pragma unroll
@@ -514,6 +566,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
 
   // ---- per-query state
   int nl = ns;
+  int seg0 = c0;                                     // first chunk of the current query segment
   v8bf qa[8];
   v4f acc[16];
   float m_run[4], l_run[4];
@@ -601,7 +654,8 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s_sx[wave][kt][lane] = make_float4(sc[kt][0], sc[kt][1], sc[kt][2], sc[kt][3]);
     }
-    const bool last_of_query = !more || s_pref[nl + 1] == c + 1;
+    // a segment ends with its query's chunks, or (fixed split) with its run
+    const bool last_of_query = !more || s_pref[nl + 1] == c + 1 || (fixed_split && c + 1 - seg0 == a.split_chunks);
     if (more && last_of_query && active) q_issue(ns);  // the next query's rows, in flight from here
     __syncthreads();
     if (active) {
@@ -701,7 +755,11 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
         }
         const int n = qbase + nl;
         const int hrow0 = 16 * hg + 4 * g;
-        const bool direct = per_query || (s_pref[nl] >= c0 && s_pref[nl + 1] <= c1);
+        bool direct;
+        if constexpr (layout == kLayoutQuery) direct = true;
+        else if constexpr (layout == kLayoutSplit) direct = n_runs == 1;
+        else if constexpr (split_flat) direct = s_rpref[nl + 1] - s_rpref[nl] == 1;
+        else direct = s_pref[nl] >= c0 && s_pref[nl + 1] <= c1;
         if (direct) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -717,7 +775,9 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
             if (a.lse && r == 0 && dh == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
           }
         } else {
-          const size_t slot = (size_t)blockIdx.x + n;
+          size_t slot;
+          if constexpr (fixed_split) slot = (size_t)n * a.split_runs + (seg0 - s_pref[nl]) / a.split_chunks;
+          else slot = (size_t)blockIdx.x + n;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int h = hrow0 + i;
@@ -735,7 +795,8 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
       __syncthreads();                     // every wave is done with Ks, Pt, s_sx
       HCA_COMMIT();                        // (also waits for the next query's rows)
       if (last_of_query) {
-        nl = ns;                           // the staged chunk's query is next
+        if constexpr (fixed_split) seg0 = c + 1;
+        nl = ns;                           // the staged chunk's query is next (or its next run)
         if (active) q_finish(nl);
       }
       __syncthreads();
@@ -749,23 +810,35 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a, int per_
 // merge the runs of one (query, head) in run order, with the sink: run s holds
 // (m_s, l_s, o_s / l_s), so o = sum_s w_s (o_s / l_s) / (e^(sigma - M) + sum_s w_s)
 // with w_s = 2^(m_s - M) l_s
+// Fixed split (split_runs > 0): query n's runs are slots n * split_runs + s, s <
+// its run count; the attention kernel has already finished queries with one run.
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
-  __shared__ float s_w[HCA_ATTN_GRID];
+  __shared__ float s_w[kMaxRuns];
   __shared__ float s_red[8];
   const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H);
-  const int cb = pp.pref[n], ce = pp.pref[n + 1], per = pp.pref[a.Nq + 1];
+  PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
   const float sig = a.sink[h] * (float)kLog2e;
   __bf16* out = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD;
-  if (cb == ce) {                          // empty set: the sink alone, o = 0
+  int S;                                   // runs to merge (one thread each)
+  size_t slot0;
+  const int cnt = a.split_runs > 0 ? (query_info(a, n).n_set + KC - 1) / KC : pp.pref[n + 1] - pp.pref[n];
+  if (cnt == 0) {                          // empty set (no window, nothing visible): the sink alone, o = 0
     for (int d = tid; d < kD; d += 256) out[d] = (__bf16)0.0f;
     if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
     return;
   }
-  const int w0 = cb / per, w1 = (ce - 1) / per;
-  if (w0 == w1) return;                    // finished by its single run
-  const int S = w1 - w0 + 1;               // <= the number of workgroups (one thread each)
-  const size_t slot0 = ((size_t)w0 + n) * a.H + h, sstride = (size_t)a.H;
+  if (a.split_runs > 0) {
+    S = (cnt + a.split_chunks - 1) / a.split_chunks;
+    if (S <= 1) return;                    // finished by its single run
+    slot0 = (size_t)n * a.split_runs * a.H + h;
+  } else {
+    const int cb = pp.pref[n], ce = pp.pref[n + 1], per = pp.pref[a.Nq + 1];
+    const int w0 = cb / per, w1 = (ce - 1) / per;
+    if (w0 == w1) return;                  // finished by its single run
+    S = w1 - w0 + 1;                       // <= the number of workgroups
+    slot0 = ((size_t)w0 + n) * a.H + h;
+  }
+  const size_t sstride = (size_t)a.H;
   float m = -INFINITY, l = 0.0f;
   if (tid < S) { m = pp.m[slot0 + tid * sstride]; l = pp.l[slot0 + tid * sstride]; }
   const float mx = wave_max(m);
@@ -803,11 +876,25 @@ bool decode_layout(int Nq, int prefill, int mode, int k, int n_win, int64_t max_
 
 }  // namespace
 
+int64_t attention_max_chunks(int mode, int k, int n_win, int64_t max_visible) {
+  const int64_t n_ent = mode == HCA_MODE_CSA ? (k < max_visible ? (int64_t)k : max_visible) : max_visible;
+  return (n_ent + n_win + KC - 1) / KC;
+}
+
+int64_t attention_split_runs(int mode, int k, int n_win, int64_t max_visible, int split_chunks) {
+  if (split_chunks <= 0) return 0;
+  return (attention_max_chunks(mode, k, n_win, max_visible) + split_chunks - 1) / split_chunks;
+}
+
+int attention_max_runs() { return kMaxRuns; }
+
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
-                                 int64_t max_visible, int io_f32, int prefill) {
+                                 int64_t max_visible, int io_f32, int prefill, int split_chunks) {
   (void)D;
-  if (io_f32 || !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
-  const size_t slots = (size_t)HCA_ATTN_GRID + Nq;
+  if (io_f32 || prefill) return 0;
+  const int64_t runs = attention_split_runs(mode, k, n_win, max_visible, split_chunks);
+  if (runs <= 0 && !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
+  const size_t slots = partial_slots(Nq, (int)runs);
   return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + slots * H * kD * 2;
 }
 
@@ -819,11 +906,25 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
     return hipGetLastError();
   }
-  const bool dec = decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible);
-  if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
-  hipLaunchKernelGGL(attn_mqa_kernel, dim3(dec ? HCA_ATTN_GRID : a.Nq), dim3(kThreads), 0, s, a, dec ? 0 : 1);
-  if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
-  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
+  if (a.split_runs > 0 && !a.prefill) {
+    // few queries: whole runs shared over the workgroups; otherwise one workgroup per run
+    const bool flat = decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible);
+    const unsigned grid = flat ? HCA_ATTN_GRID : (unsigned)((int64_t)a.Nq * a.split_runs);
+    if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
+    if (flat) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplitFlat>, dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplit>, dim3(grid), dim3(kThreads), 0, s, a);
+    if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
+    if (a.split_runs > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  AttnArgs b = a;
+  b.split_runs = 0;                        // prefill never splits a query
+  const bool dec = decode_layout(b.Nq, b.prefill, b.mode, b.k, b.n_win, b.max_visible);
+  if (b.prof_begin) (void)hipEventRecord(b.prof_begin, s);
+  if (dec) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b);
+  else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutQuery>, dim3(b.Nq), dim3(kThreads), 0, s, b);
+  if (b.prof_end) (void)hipEventRecord(b.prof_end, s);
+  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(b.Nq, b.H), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

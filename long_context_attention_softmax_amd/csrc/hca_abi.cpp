@@ -199,8 +199,16 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   } else {
     return fail(HCA_E_DTYPE, "io_fmt %d is not F32 or BF16", d->io_fmt);
   }
+  REQUIRE(d->split_chunks >= 0, HCA_E_SHAPE, "split_chunks=%d < 0", d->split_chunks);
+  if (!prefill && d->io_fmt == HCA_BF16 && d->split_chunks > 0) {
+    const int64_t runs = hca::attention_split_runs(d->mode, d->k, d->n_win, d->max_visible, d->split_chunks);
+    REQUIRE(runs <= hca::attention_max_runs(), HCA_E_UNSUPPORTED,
+            "split_chunks=%d cuts a query into up to %lld runs (at most %d)", d->split_chunks, (long long)runs,
+            hca::attention_max_runs());
+    REQUIRE((int64_t)d->Nq * runs < (1LL << 31), HCA_E_UNSUPPORTED, "Nq x runs per query must be < 2^31");
+  }
   *ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
-                                       d->io_fmt == HCA_F32, prefill);
+                                       d->io_fmt == HCA_F32, prefill, d->split_chunks);
   if (d->Nq == 0) return HCA_OK;
   REQUIRE(d->q && d->o && d->win && d->sink && d->seq_id && d->q_pos, HCA_E_NULL,
           "q, o, win, sink, seq_id and q_pos are required");
@@ -256,6 +264,8 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   a.win = static_cast<const char*>(d->win); a.win_pitch = d->win_pitch;
   a.sink = d->sink; a.seq_id = d->seq_id; a.q_pos = d->q_pos; a.o = d->o; a.lse = d->lse;
   a.workspace = d->workspace; a.prefill = prefill;
+  a.split_chunks = prefill || a.io_f32 ? 0 : d->split_chunks;
+  a.split_runs = (int)hca::attention_split_runs(a.mode, d->k, a.n_win, a.max_visible, a.split_chunks);
   a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
   return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
@@ -304,7 +314,7 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
       REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size mismatch");
       REQUIRE(d->Nq >= 0 && d->H >= 1 && d->D >= 1 && d->max_visible >= 0, HCA_E_SHAPE, "bad shapes");
       ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
-                                          d->io_fmt == HCA_F32, op == HCA_OP_ATTN_PREFILL);
+                                          d->io_fmt == HCA_F32, op == HCA_OP_ATTN_PREFILL, d->split_chunks);
       rc = HCA_OK;
       break;
     }

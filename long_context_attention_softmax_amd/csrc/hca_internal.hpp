@@ -69,10 +69,14 @@ struct AttnArgs {
   int prefill;
   hipEvent_t prof_begin, prof_end;    // optional, around the attention kernel
   const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged entries (page_shift >= 0)
+  int split_chunks, split_runs;       // decode fixed split: chunks per run, most runs of a query (0 = off)
   double inv_turn[32];                // BF16 path: rope_base^(-2i/64) / (2 pi), turns per position
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
-                                 int64_t max_visible, int io_f32, int prefill);
+                                 int64_t max_visible, int io_f32, int prefill, int split_chunks);
+// most runs of one query under a fixed split of split_chunks chunks (0 when split_chunks <= 0)
+int64_t attention_split_runs(int mode, int k, int n_win, int64_t max_visible, int split_chunks);
+int attention_max_runs();
 
 }  // namespace hca

@@ -91,6 +91,7 @@ class DeviceLayer:
         self.o: Optional[torch.Tensor] = None
         self.lse: Optional[torch.Tensor] = None
         self.pages = None            # (page_table [B, pitch] int32, page_rows) when paged
+        self.split_chunks = 0        # decode: > 0 = fixed split, batch-invariant outputs
         self._phys: Optional[np.ndarray] = None
 
     def phys_rows(self, rows) -> np.ndarray:
@@ -177,7 +178,8 @@ class DeviceLayer:
                   mode=self.mode, m=self.m, n_win=g.n_win, D_r=g.D_r, max_visible=self.max_visible,
                   k=g.topk if self.mode == A.MODE_CSA else 0,
                   idx=self.idx if self.mode == A.MODE_CSA else None, tau=g.tau,
-                  rope_base=g.rope_base, o=self.o, lse=self.lse, prof=prof, pages=self.pages)
+                  rope_base=g.rope_base, o=self.o, lse=self.lse, prof=prof, pages=self.pages,
+                  split_chunks=self.split_chunks)
 
     def step(self, prefill: bool = False, pool: bool = True, prof_select=None, prof_attend=None):
         if pool:

@@ -212,7 +212,7 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: Optio
           mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
           idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
           o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None,
-          pages=None) -> torch.Tensor:
+          pages=None, split_chunks: int = 0) -> torch.Tensor:
     Nq, H, D = q.shape
     _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
     io = A.F32 if q.dtype == torch.float32 else A.BF16
@@ -224,6 +224,7 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: Optio
     d.Nq, d.B, d.H, d.D, d.D_r = Nq, _seqs(cache_row_start, pages), H, D, D_r
     d.mode, d.m, d.k, d.n_win, d.win_cap = mode, m, k, n_win, win.shape[-2]
     d.tau, d.io_fmt, d.rope_base, d.max_visible = tau, io, rope_base, max_visible
+    d.split_chunks = split_chunks
     if not q.is_contiguous():
         raise ValueError("q must be contiguous [Nq, H, D]")
     d.q = _ptr(q)

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 2
+    assert A.lib.hca_abi_version() == 3
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
                     (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
@@ -208,6 +208,26 @@ def test_attention_page_table_validation():
         assert call(fn, attn_desc(**dict(paged, page_rows=64, page_table_pitch=511))) == -2
         assert call(fn, attn_desc(**dict(paged, page_table=FAKE + 1))) == -3
         assert b"page_table" in A.lib.hca_last_error()
+
+
+def test_attention_fixed_split_validation():
+    # seq_id misaligned (the last check): a call that passes the split checks stops there
+    last = dict(seq_id=FAKE + 2, workspace=FAKE, workspace_bytes=1 << 40)
+    assert call("hca_attn_decode", attn_desc(split_chunks=-1, **last)) == -2
+    assert call("hca_attn_decode", attn_desc(split_chunks=1, **last)) == -3     # CSA: 10 chunks, 10 runs
+    assert b"index arrays" in A.lib.hca_last_error()
+    # HCA over 2^20 entries + 128 window slots = 16386 chunks: 64 per run is 257 runs, 65 is 253
+    hca = dict(mode=1, m=128, k=0, idx=None, max_visible=1 << 20, **last)
+    assert call("hca_attn_decode", attn_desc(split_chunks=64, **hca)) == -5
+    assert b"runs" in A.lib.hca_last_error()
+    assert call("hca_attn_decode", attn_desc(split_chunks=65, **hca)) == -3
+    assert call("hca_attn_prefill", attn_desc(split_chunks=1, **hca)) == -3     # prefill never splits
+    # the fixed split sizes its partials per (query, run): Nq x 10 runs x 64 heads
+    n0, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert A.lib.hca_workspace_bytes(A.OP_ATTN_DECODE, ctypes.byref(attn_desc(split_chunks=1)), ctypes.byref(n1)) == 0
+    assert n1.value >= 8 * 10 * 64 * 512 * 2
+    assert A.lib.hca_workspace_bytes(A.OP_ATTN_PREFILL, ctypes.byref(attn_desc(split_chunks=1)), ctypes.byref(n0)) == 0
+    assert n0.value == 0
 
 
 def test_binding_refuses_host_tensors():
