@@ -131,10 +131,17 @@ def scores_for_query(cache: _Cache, lay, g, qi, t, b):
 def run_layer(lay, g, queries=None, pooled=None):
     """Oracle step of one layer.  ``queries``: indices of the queries to evaluate
     (default all).  Returns pooled entries, idx [nq, k] (CSA), scores, o [nq, H, D]
-    and lse [nq, H]."""
-    if pooled is None:
+    and lse [nq, H].
+
+    Layer modes: "csa" and "hca" as above; "swa" is the sliding-window-only block
+    ("DeepSeek V4: How They Crushed the Million-Token Memory Problem"
+    (sameershanbhag.com), "Two kinds of memory instead of one": the final
+    multi-token-prediction block runs sliding-window only): no compressed entries,
+    nothing pooled, the set is the window tokens alone (pooled is then None)."""
+    swa = lay.mode == "swa"
+    if pooled is None and not swa:
         pooled = pool_layer(lay, g)
-    cache = _Cache(lay, g, pooled)
+    cache = None if swa else _Cache(lay, g, pooled)
     nq_all = len(lay.q_pos)
     qs = np.arange(nq_all) if queries is None else np.asarray(queries)
     ring = raw_values(lay.win, lay.fmt)
@@ -153,9 +160,9 @@ def run_layer(lay, g, queries=None, pooled=None):
             out_sel[n, sel >= 0] = I[sel[sel >= 0]]
             gaps.append(topk.kth_gap(I, g.topk))
             js = sel[sel >= 0]
-        else:
+        elif not swa:
             js = np.arange(V)
-        ent = cache.entries(int(lay.cache_row_start[b]) + js)
+        ent = np.zeros((0, g.D)) if swa else cache.entries(int(lay.cache_row_start[b]) + js)
         win = attend.window_keys(ring, b, t, g.n_win, lay.W_cap, g.D_r, g.rope_base)
         keys = np.concatenate([ent, win], axis=0)
         qh = attend.query_hat(query_values(lay, qi), t, g.D_r, g.rope_base)

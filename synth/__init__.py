@@ -13,4 +13,4 @@ arrays produced here.
 from .configs import (CONFIGS, Geometry, TINY_GEOMETRY, FULL_GEOMETRY,  # noqa: F401
                       config_by_name)
 from .gen import (tiny, csa_decode, hca_decode, csa_prefill, ragged_pair,  # noqa: F401
-                  make, fp8_codes, bf16_bits, mxfp4_draw)
+                  swa_layer, make, fp8_codes, bf16_bits, mxfp4_draw)

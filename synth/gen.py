@@ -212,6 +212,28 @@ def _decode_layer(rng, g: Geometry, mode: str, lengths: np.ndarray, W_cap: int,
     return lay
 
 
+def swa_layer(rng, g: Geometry, lengths: np.ndarray, W_cap: int, kv_std: float = 1.0, fmt: str = "quant"):
+    """A sliding-window-only decode layer (the multi-token-prediction block): each
+    sequence's query t = L_b - 1 attends to its last n_win raw tokens and the sink;
+    there is no compressed cache and nothing to pool.
+    Draw order: window ring, q, sink."""
+    lengths = np.asarray(lengths, np.int64)
+    B = len(lengths)
+    lay = SimpleNamespace(mode="swa", m=1, fmt=fmt, B=B, W_cap=W_cap, n_rows=0,
+                          cache_row_start=np.zeros(B, np.int64), n_visible=np.zeros(B, np.int64))
+    if fmt == "f32":
+        lay.win = _normal(rng, (B, W_cap, g.D), kv_std)
+        lay.q = _normal(rng, (B, g.H, g.D), 1 / math.sqrt(g.D))
+    else:
+        lay.win = _bf16_normal(rng, (B, W_cap, g.D), kv_std)
+        lay.q = _bf16_normal(rng, (B, g.H, g.D), 1 / math.sqrt(g.D))
+    lay.sink = _normal(rng, (g.H,), 1.0)
+    lay.q_pos = (lengths - 1).astype(np.int64)
+    lay.seq_id = np.arange(B, dtype=np.int32)
+    lay.pool = _cat_blocks([])
+    return lay
+
+
 def csa_decode(seed: int = 1, B: int = 8, L: int = 131072, g: Geometry | None = None,
                idx_fmt: str = "fp8"):
     from .configs import FULL_GEOMETRY

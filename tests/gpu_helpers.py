@@ -40,6 +40,8 @@ def assert_codes_equal(got, want, fragile, what):
 
 def check_pool(dev, pooled, lay):
     """Compare the rows the GPU pooled with the oracle's encodings."""
+    if pooled is None:                     # window-only layer: nothing pooled
+        return
     rows = torch.from_numpy(dev.phys_rows(pooled["out_row"])).to(dev.device)
     kv = pooled["kv"]
     if rows.numel() == 0:
