@@ -70,6 +70,12 @@ extern "C" {
 /* attention modes */
 #define HCA_MODE_CSA 0   /* attend to the indexer-selected entries */
 #define HCA_MODE_HCA 1   /* attend to every visible entry */
+/* attend to the sliding window and the sink only: the multi-token-prediction block
+   ("DeepSeek V4: How They Crushed the Million-Token Memory Problem"
+   (sameershanbhag.com), "Two kinds of memory instead of one": the final block is
+   sliding-window only).  No compressed entry is read: cache, cache_row_start,
+   page_table, idx, k, m and max_visible are ignored (may be NULL / 0). */
+#define HCA_MODE_SWA 2
 
 /* operation ids for hca_workspace_bytes / hca_struct_size */
 #define HCA_OP_KV_COMPRESS  0

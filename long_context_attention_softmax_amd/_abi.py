@@ -17,7 +17,7 @@ HCA_OK = 0
 ERRORS = {-1: "HCA_E_NULL", -2: "HCA_E_SHAPE", -3: "HCA_E_ALIGN", -4: "HCA_E_DTYPE",
           -5: "HCA_E_UNSUPPORTED", -6: "HCA_E_WORKSPACE", -7: "HCA_E_LAUNCH", -8: "HCA_E_VERSION"}
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
-MODE_CSA, MODE_HCA = 0, 1
+MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
 OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL = 0, 1, 2, 3
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES = 100, 101
 

@@ -55,7 +55,8 @@ __device__ __forceinline__ SetInfo set_info_pos(const AttnArgs& a, int64_t t) {
 
 __device__ __forceinline__ SetInfo set_info(const AttnArgs& a, int n) {
   SetInfo si = set_info_pos(a, a.q_pos[n]);
-  si.row0 = a.page_shift < 0 ? a.cache_row_start[a.seq_id[n]] : 0;   // paged: rows through the table
+  // paged: rows through the table; no row map: no entry is ever read (window only)
+  si.row0 = a.page_shift < 0 && a.cache_row_start ? a.cache_row_start[a.seq_id[n]] : 0;
   return si;
 }
 
@@ -450,7 +451,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
     int64_t row0 = 0;
     if (tid < a.Nq) {
       const int b = a.seq_id[tid];
-      row0 = a.page_shift < 0 ? a.cache_row_start[b] : 0;   // paged: rows through the table
+      row0 = a.page_shift < 0 && a.cache_row_start ? a.cache_row_start[b] : 0;   // paged / window only
       QInfo qi = query_info_pos(a, tid, b);
       s_qi[tid] = qi;
       cnt = (qi.n_set + KC - 1) / KC;

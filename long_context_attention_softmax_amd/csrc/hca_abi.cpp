@@ -178,22 +178,28 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
   REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size %u != %zu",
           d->struct_size, sizeof(hca_attn_desc));
-  REQUIRE(d->Nq >= 0 && d->B >= 1 && d->H >= 1 && d->m >= 1 && d->n_win >= 0, HCA_E_SHAPE,
-          "Nq>=0, B>=1, H>=1, m>=1, n_win>=0 required");
-  REQUIRE(d->mode == HCA_MODE_CSA || d->mode == HCA_MODE_HCA, HCA_E_SHAPE, "mode %d unknown", d->mode);
-  REQUIRE(d->mode == HCA_MODE_HCA || (d->k >= 1 && d->k <= (1 << 20)), HCA_E_SHAPE, "CSA needs 1 <= k <= 2^20");
+  REQUIRE(d->Nq >= 0 && d->B >= 1 && d->H >= 1 && (d->m >= 1 || d->mode == HCA_MODE_SWA) && d->n_win >= 0,
+          HCA_E_SHAPE, "Nq>=0, B>=1, H>=1, m>=1, n_win>=0 required");
+  REQUIRE(d->mode == HCA_MODE_CSA || d->mode == HCA_MODE_HCA || d->mode == HCA_MODE_SWA, HCA_E_SHAPE,
+          "mode %d unknown", d->mode);
+  const bool swa = d->mode == HCA_MODE_SWA;
+  REQUIRE(d->mode != HCA_MODE_CSA || (d->k >= 1 && d->k <= (1 << 20)), HCA_E_SHAPE, "CSA needs 1 <= k <= 2^20");
   REQUIRE(d->win_cap >= 1 && d->win_cap >= d->n_win, HCA_E_SHAPE, "win_cap must be >= max(1, n_win)");
-  REQUIRE(d->max_visible >= 0 && d->max_visible < (1LL << 31), HCA_E_SHAPE, "max_visible out of range");
+  REQUIRE(swa || (d->max_visible >= 0 && d->max_visible < (1LL << 31)), HCA_E_SHAPE, "max_visible out of range");
   REQUIRE(d->D_r >= 0 && d->D_r % 2 == 0 && d->D_r <= d->D, HCA_E_SHAPE, "D_r must be even and <= D");
   REQUIRE(d->rope_base > 0.0, HCA_E_SHAPE, "rope_base must be > 0");
-  const int64_t max_set = (d->mode == HCA_MODE_CSA ? (int64_t)d->k : d->max_visible) + d->n_win;
+  // the window-only mode runs as HCA over no visible entry
+  const int emode = swa ? HCA_MODE_HCA : d->mode;
+  const int64_t evis = swa ? 0 : d->max_visible;
+  const int ek = d->mode == HCA_MODE_CSA ? d->k : 0;
+  const int64_t max_set = (emode == HCA_MODE_CSA ? (int64_t)ek : evis) + d->n_win;
   if (d->io_fmt == HCA_F32) {
-    REQUIRE(d->cache.fmt == HCA_F32, HCA_E_DTYPE, "io_fmt F32 needs an F32 cache");
+    REQUIRE(swa || d->cache.fmt == HCA_F32, HCA_E_DTYPE, "io_fmt F32 needs an F32 cache");
     REQUIRE(d->D <= 1024 && d->D >= 2, HCA_E_SHAPE, "F32 attention needs 2 <= D <= 1024");
     REQUIRE(d->D_r <= 1024, HCA_E_SHAPE, "D_r too large");
     REQUIRE(max_set <= 4096, HCA_E_UNSUPPORTED, "F32 attention supports at most 4096 keys per query");
   } else if (d->io_fmt == HCA_BF16) {
-    REQUIRE(d->cache.fmt == HCA_FP8_E4M3, HCA_E_DTYPE, "io_fmt BF16 needs an FP8_E4M3 cache");
+    REQUIRE(swa || d->cache.fmt == HCA_FP8_E4M3, HCA_E_DTYPE, "io_fmt BF16 needs an FP8_E4M3 cache");
     REQUIRE(d->D == 512 && d->D_r == 64, HCA_E_UNSUPPORTED, "BF16 attention needs D=512, D_r=64");
     REQUIRE(d->H % 16 == 0 && d->H <= 64, HCA_E_UNSUPPORTED, "BF16 attention needs H in {16,32,48,64}");
   } else {
@@ -201,28 +207,30 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   }
   REQUIRE(d->split_chunks >= 0, HCA_E_SHAPE, "split_chunks=%d < 0", d->split_chunks);
   if (!prefill && d->io_fmt == HCA_BF16 && d->split_chunks > 0) {
-    const int64_t runs = hca::attention_split_runs(d->mode, d->k, d->n_win, d->max_visible, d->split_chunks);
+    const int64_t runs = hca::attention_split_runs(emode, ek, d->n_win, evis, d->split_chunks);
     REQUIRE(runs <= hca::attention_max_runs(), HCA_E_UNSUPPORTED,
             "split_chunks=%d cuts a query into up to %lld runs (at most %d)", d->split_chunks, (long long)runs,
             hca::attention_max_runs());
     REQUIRE((int64_t)d->Nq * runs < (1LL << 31), HCA_E_UNSUPPORTED, "Nq x runs per query must be < 2^31");
   }
-  *ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
+  *ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, emode, ek, d->n_win, evis,
                                        d->io_fmt == HCA_F32, prefill, d->split_chunks);
   if (d->Nq == 0) return HCA_OK;
   REQUIRE(d->q && d->o && d->win && d->sink && d->seq_id && d->q_pos, HCA_E_NULL,
           "q, o, win, sink, seq_id and q_pos are required");
-  int prc = check_pages(d->page_table, d->page_table_pitch, d->page_rows, d->max_visible, d->cache_row_start, 1);
-  if (prc) return prc;
-  REQUIRE(d->mode == HCA_MODE_HCA || d->idx, HCA_E_NULL, "CSA needs idx");
-  int rc = check_kv_planes(d->cache, d->D, d->D_r, "cache", true);
-  if (rc) return rc;
+  if (!swa) {
+    int prc = check_pages(d->page_table, d->page_table_pitch, d->page_rows, d->max_visible, d->cache_row_start, 1);
+    if (prc) return prc;
+  }
+  REQUIRE(d->mode != HCA_MODE_CSA || d->idx, HCA_E_NULL, "CSA needs idx");
+  int rc = check_kv_planes(d->cache, d->D, d->D_r, "cache", !swa);
+  if (rc && !swa) return rc;
   const int eb = elem_bytes(d->io_fmt);
   REQUIRE(d->win_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE, "win_pitch too small");
   if (d->io_fmt == HCA_BF16) {
     REQUIRE(aligned(d->q, 16) && aligned(d->o, 2) && aligned(d->win, 16) && d->win_pitch % 16 == 0 &&
-            aligned(d->cache.nope, 16) && d->cache.nope_pitch % 16 == 0 && aligned(d->cache.rope, 16) &&
-            d->cache.rope_pitch % 16 == 0, HCA_E_ALIGN, "BF16 attention needs 16-byte aligned rows");
+            (swa || (aligned(d->cache.nope, 16) && d->cache.nope_pitch % 16 == 0 && aligned(d->cache.rope, 16) &&
+                     d->cache.rope_pitch % 16 == 0)), HCA_E_ALIGN, "BF16 attention needs 16-byte aligned rows");
   } else {
     REQUIRE(aligned(d->q, 4) && aligned(d->o, 4) && aligned(d->win, 4) && d->win_pitch % 4 == 0,
             HCA_E_ALIGN, "F32 attention needs 4-byte aligned rows");
@@ -248,24 +256,26 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   if (rc) return rc;
   if (d->Nq == 0) return HCA_OK;
   hca::AttnArgs a{};
-  a.Nq = d->Nq; a.H = d->H; a.D = d->D; a.D_r = d->D_r; a.mode = d->mode; a.m = d->m;
+  const bool swa = d->mode == HCA_MODE_SWA;   // runs as HCA with no visible entry: no cache read
+  a.Nq = d->Nq; a.H = d->H; a.D = d->D; a.D_r = d->D_r; a.mode = swa ? HCA_MODE_HCA : d->mode;
+  a.m = swa ? 1 : d->m;
   a.k = d->mode == HCA_MODE_CSA ? d->k : 0; a.n_win = d->n_win; a.win_cap = d->win_cap;
   a.io_f32 = d->io_fmt == HCA_F32; a.tau = d->tau; a.rope_base = d->rope_base;
   // RoPE frequencies of the 32 pairs in turns per position, formed once here in fp64
   for (int i = 0; i < 32; ++i) a.inv_turn[i] = std::pow(d->rope_base, -2.0 * i / 64.0) / (2.0 * M_PI);
-  a.max_visible = d->max_visible; a.q = d->q; a.cache_fmt = d->cache.fmt;
+  a.max_visible = swa ? 0 : d->max_visible; a.q = d->q; a.cache_fmt = d->cache.fmt;
   a.c_f32 = static_cast<const char*>(d->cache.f32); a.c_f32_pitch = d->cache.f32_pitch;
   a.c_nope = static_cast<const char*>(d->cache.nope); a.c_nope_pitch = d->cache.nope_pitch;
   a.c_rope = static_cast<const char*>(d->cache.rope); a.c_rope_pitch = d->cache.rope_pitch;
   a.c_scale = static_cast<const float*>(d->cache.scale);
-  a.cache_row_start = d->cache_row_start; a.idx = d->mode == HCA_MODE_CSA ? d->idx : nullptr;
-  a.page_table = d->page_table; a.page_pitch = d->page_table_pitch;
-  a.page_shift = d->page_table ? log2_exact(d->page_rows) : -1;
+  a.cache_row_start = swa ? nullptr : d->cache_row_start; a.idx = d->mode == HCA_MODE_CSA ? d->idx : nullptr;
+  a.page_table = swa ? nullptr : d->page_table; a.page_pitch = d->page_table_pitch;
+  a.page_shift = a.page_table ? log2_exact(d->page_rows) : -1;
   a.win = static_cast<const char*>(d->win); a.win_pitch = d->win_pitch;
   a.sink = d->sink; a.seq_id = d->seq_id; a.q_pos = d->q_pos; a.o = d->o; a.lse = d->lse;
   a.workspace = d->workspace; a.prefill = prefill;
   a.split_chunks = prefill || a.io_f32 ? 0 : d->split_chunks;
-  a.split_runs = (int)hca::attention_split_runs(a.mode, d->k, a.n_win, a.max_visible, a.split_chunks);
+  a.split_runs = (int)hca::attention_split_runs(a.mode, a.k, a.n_win, a.max_visible, a.split_chunks);
   a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
   return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
@@ -312,8 +322,11 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
       const hca_attn_desc* d = static_cast<const hca_attn_desc*>(desc);
       REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
       REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size mismatch");
-      REQUIRE(d->Nq >= 0 && d->H >= 1 && d->D >= 1 && d->max_visible >= 0, HCA_E_SHAPE, "bad shapes");
-      ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, d->mode, d->k, d->n_win, d->max_visible,
+      REQUIRE(d->Nq >= 0 && d->H >= 1 && d->D >= 1 && (d->max_visible >= 0 || d->mode == HCA_MODE_SWA),
+              HCA_E_SHAPE, "bad shapes");
+      const bool swa = d->mode == HCA_MODE_SWA;
+      ws = hca::attention_workspace_bytes(d->Nq, d->H, d->D, swa ? HCA_MODE_HCA : d->mode,
+                                          d->mode == HCA_MODE_CSA ? d->k : 0, d->n_win, swa ? 0 : d->max_visible,
                                           d->io_fmt == HCA_F32, op == HCA_OP_ATTN_PREFILL, d->split_chunks);
       rc = HCA_OK;
       break;

@@ -103,7 +103,9 @@ class DeviceLayer:
     def from_host(cls, lay, g, device="cuda", page_rows: Optional[int] = None,
                   page_seed: int = 0) -> "DeviceLayer":
         d = cls()
-        d.mode = A.MODE_CSA if lay.mode == "csa" else A.MODE_HCA
+        d.mode = {"csa": A.MODE_CSA, "hca": A.MODE_HCA, "swa": A.MODE_SWA}[lay.mode]
+        if d.mode == A.MODE_SWA:
+            return cls._window_only(d, lay, g, torch.device(device))
         d.m, d.g, d.device = lay.m, g, torch.device(device)
         d.f32 = lay.fmt == "f32"
         dev = d.device
@@ -157,9 +159,26 @@ class DeviceLayer:
         d.lse = torch.empty((d.Nq, g.H), dtype=torch.float32, device=dev)
         return d
 
+    @staticmethod
+    def _window_only(d, lay, g, dev):
+        """The sliding-window-only layer: ring, queries and sink; no cache."""
+        d.m, d.g, d.device, d.f32 = 1, g, dev, lay.fmt == "f32"
+        d.win = _t(lay.win, dev, None if d.f32 else torch.bfloat16)
+        d.q = _t(lay.q, dev, None if d.f32 else torch.bfloat16)
+        d.W_cap, d.max_visible, d.Nq = lay.W_cap, 0, len(lay.q_pos)
+        d.cache = d.cache_row_start = None
+        d.q_pos = _t(lay.q_pos.astype(np.int64), dev)
+        d.seq_id = _t(lay.seq_id.astype(np.int32), dev)
+        d.sink = _t(lay.sink.astype(np.float32), dev)
+        d.o = torch.empty_like(d.q)
+        d.lse = torch.empty((d.Nq, g.H), dtype=torch.float32, device=dev)
+        return d
+
     # ----------------------------------------------------------------- steps
     def pool(self, debug: Optional[torch.Tensor] = None):
         g = self.g
+        if self.mode == A.MODE_SWA:
+            return
         hca_kv_compress(self.win, self.block_row, self.block_pos, self.out_row, self.gate_w, self.gate_b,
                         self.cache, m=self.m, D_r=g.D_r, rope_base=g.rope_base,
                         raw_idx=self.win_idx if self.mode == A.MODE_CSA else None,

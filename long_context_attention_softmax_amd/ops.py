@@ -207,7 +207,7 @@ def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_sta
     return idx
 
 
-def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: Optional[torch.Tensor],
+def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_start: Optional[torch.Tensor],
           win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
           mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
           idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
@@ -221,14 +221,16 @@ def _attn(prefill: bool, q: torch.Tensor, cache: KVCache, cache_row_start: Optio
     if o is None:
         o = torch.empty_like(q)
     d = A.new_desc(A.AttnDesc)
-    d.Nq, d.B, d.H, d.D, d.D_r = Nq, _seqs(cache_row_start, pages), H, D, D_r
+    d.Nq, d.H, d.D, d.D_r = Nq, H, D, D_r
+    d.B = _seqs(cache_row_start, pages) if (cache_row_start is not None or pages) else win.shape[0]
     d.mode, d.m, d.k, d.n_win, d.win_cap = mode, m, k, n_win, win.shape[-2]
     d.tau, d.io_fmt, d.rope_base, d.max_visible = tau, io, rope_base, max_visible
     d.split_chunks = split_chunks
     if not q.is_contiguous():
         raise ValueError("q must be contiguous [Nq, H, D]")
     d.q = _ptr(q)
-    d.cache = cache.planes()
+    if cache is not None:                  # None: the window-only mode reads no cache
+        d.cache = cache.planes()
     if cache_row_start is not None:
         d.cache_row_start = _ptr(_i64(cache_row_start, 1, "cache_row_start"))
     _set_pages(d, pages)

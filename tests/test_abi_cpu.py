@@ -230,6 +230,24 @@ def test_attention_fixed_split_validation():
     assert n0.value == 0
 
 
+def test_attention_window_only_validation():
+    # no cache, row map, page table, index list, m, k or max_visible: the call passes every
+    # check up to the misaligned seq_id (the last one), so nothing is launched
+    last = dict(seq_id=FAKE + 2, workspace=FAKE, workspace_bytes=1 << 40)
+    bare = dict(mode=2, m=0, k=0, max_visible=-5, cache_row_start=None, idx=None, **last)
+    for fn in ("hca_attn_decode", "hca_attn_prefill"):
+        d = attn_desc(**bare)
+        d.cache = A.KvPlanes()             # every plane NULL, fmt 0
+        assert call(fn, d) == -3
+        assert b"index arrays" in A.lib.hca_last_error()
+    assert call("hca_attn_decode", attn_desc(mode=3, **last)) == -2
+    assert call("hca_attn_decode", attn_desc(**dict(bare, win=None))) == -1     # the ring is still required
+    # the workspace of a window-only decode covers its at most two chunks per query, not max_visible
+    n = ctypes.c_size_t(0)
+    assert A.lib.hca_workspace_bytes(A.OP_ATTN_DECODE, ctypes.byref(attn_desc(**bare)), ctypes.byref(n)) == 0
+    assert 0 < n.value < 64 << 20
+
+
 def test_binding_refuses_host_tensors():
     import torch
     from long_context_attention_softmax_amd import ops

@@ -1,0 +1,59 @@
+"""GPU parity of the layer variants: the window-only layer of the
+multi-token-prediction block (HCA_MODE_SWA: sliding window and sink, no compressed
+cache), in decode, prefill, the f32 path and the batch-invariant split.  Bars as in
+the other parity tests: output per-row relative error <= 2e-2 (BF16) / 1e-5 (f32)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(msg):
+    print(msg, flush=True)
+
+
+def test_window_only_decode_bf16(gpu):
+    g = synth.FULL_GEOMETRY
+    lens = np.array([1, 50, 128, 129, 4096, 1 << 20, 777], np.int64)   # windows shorter than n_win too
+    lay = synth.swa_layer(np.random.default_rng(61), g, lens, 128)
+    _print(f"window-only decode lengths={lens.tolist()}")
+    run_and_compare(lay, g)
+
+
+def test_window_only_f32(gpu):
+    g = synth.TINY_GEOMETRY
+    lens = np.array([3, 40, 300], np.int64)
+    lay = synth.swa_layer(np.random.default_rng(62), g, lens, max(g.n_win, 8), fmt="f32")
+    _print(f"window-only f32 lengths={lens.tolist()} n_win={g.n_win}")
+    run_and_compare(lay, g)
+
+
+def test_window_only_prefill(gpu):
+    from synth.gen import _bf16_normal
+    g = synth.FULL_GEOMETRY
+    L, T, W_cap = 5000, 256, 512            # 256 queries of one sequence; the ring holds T + n_win tokens
+    rng = np.random.default_rng(63)
+    lay = synth.swa_layer(rng, g, np.array([L], np.int64), W_cap)
+    lay.q_pos = np.arange(L - T, L, dtype=np.int64)
+    lay.seq_id = np.zeros(T, np.int32)
+    lay.q = _bf16_normal(rng, (T, g.H, g.D), 1 / np.sqrt(g.D))
+    _print("window-only prefill, 256 queries")
+    run_and_compare(lay, g, prefill=True)
+
+
+def test_window_only_fixed_split_invariant(gpu):
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    from test_gpu_batch_invariant import _check_invariant
+    g = replace(synth.FULL_GEOMETRY)
+    lens = np.array([1, 70, 128, 500, 1 << 16], np.int64)
+    lay = synth.swa_layer(np.random.default_rng(64), g, lens, 128)
+    dev = DeviceLayer.from_host(lay, g)
+    dev.split_chunks = 1
+    _print("window-only, split_chunks=1: parity, then each query alone vs reversed batch")
+    run_and_compare(lay, g, dev=dev)
+    _check_invariant(dev, [list(range(dev.Nq))[::-1]])
