@@ -195,7 +195,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
-    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|hca|prefill)")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|prologue|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -322,6 +322,40 @@ def main():
                 split_chunks=split, hca_attention_kernel_ms=round(float(k8.mean()), 5), replicas=len(sets))
             log(f"[bench] ragged pair (batch-invariant split): {ms8:.4f} ms/step")
             del sets
+            torch.cuda.empty_cache()
+        # ---- q / KV normalization prologue at the prefill chunk's size --------
+        if only in (None, "prologue"):
+            from long_context_attention_softmax_amd.ops import hca_qkv_prologue
+            T, H, D, W = 4096, 64, 512, 4352
+            gen = torch.Generator(device="cuda").manual_seed(9)
+            q = torch.randn((T, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+            kv = torch.randn((T, D), generator=gen, device="cuda").to(torch.bfloat16)
+            ring = torch.zeros((1, W, D), dtype=torch.bfloat16, device="cuda")
+            gq = torch.rand(D, generator=gen, device="cuda") + 0.5
+            gk = torch.rand(D, generator=gen, device="cuda") + 0.5
+            seq = torch.zeros(T, dtype=torch.int32, device="cuda")
+            pos = torch.arange(1 << 20, (1 << 20) + T, dtype=torch.int64, device="cuda")
+            qo = torch.empty_like(q)
+            pbytes = 2 * (T * H * D * 2) + 2 * (T * D * 2)             # q and tokens, read and written
+
+            def run():
+                hca_qkv_prologue(q, gq, kv, gk, seq, pos, ring, q_out=qo)
+            for _ in range(args.warmup):
+                run()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record()
+                run()
+                b.record()
+            torch.cuda.synchronize()
+            pm = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            secondary["qkv_prologue_4096x64"] = dict(
+                kernel_ms=round(pm, 5), bytes=pbytes, gbps=round(pbytes / (pm * 1e-3) / 1e9, 1),
+                hbm_frac=round(pbytes / (pm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                config={"queries": T, "heads": H, "D": D, "tokens": T, "io": "bf16"})
+            log(f"[bench] qkv prologue 4096 x 64 heads: {pm:.4f} ms, {pbytes / (pm * 1e-3) / 1e9:.0f} GB/s")
+            del q, kv, ring, qo
             torch.cuda.empty_cache()
         # ---- HCA decode at 1M ----------------------------------------------
         if only in (None, "hca"):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 3
+#define HCA_ABI_VERSION 4
 
 /* status codes */
 #define HCA_OK             0
@@ -82,6 +82,7 @@ extern "C" {
 #define HCA_OP_INDEXER_TOPK 1
 #define HCA_OP_ATTN_DECODE  2
 #define HCA_OP_ATTN_PREFILL 3
+#define HCA_OP_QKV_PROLOGUE 4
 #define HCA_STRUCT_KV_PLANES  100
 #define HCA_STRUCT_IDX_PLANES 101
 
@@ -306,6 +307,48 @@ typedef struct hca_attn_desc {
   int32_t        split_chunks;
 } hca_attn_desc;
 
+/*
+ * Query and key-value normalization, and the append of new tokens to the window
+ * ring.  "DeepSeek V4 infrastructure" (volanea.com), "Compression only works if the
+ * attention path is engineered end to end": the attention path normalizes queries
+ * and key-value vectors.  Read as root-mean-square normalization with a learned
+ * per-dimension scale, over the D dims of a row:
+ *   y_d = gamma_d * x_d / sqrt(sum_e(x_e^2) / D + eps)
+ * evaluated in fp64 (the sum in a fixed order) and rounded once into io_fmt, so a
+ * stored code differs from the exact one only for a value within about 1e-15 of a
+ * rounding boundary.
+ *   - q: the Nq * H head vectors of q_in (contiguous [Nq, H, D]) are written,
+ *     normalized with gamma_q, to q_out (which may equal q_in);
+ *   - new tokens: row i of kv_in (Nt rows, pitch kv_pitch) is normalized with
+ *     gamma_kv and written to the ring `win` at row tok_seq[i] * W_cap +
+ *     (tok_pos[i] mod W_cap) (pitch win_pitch): the sliding-window state that
+ *     pooling and the window branch read.  A token whose tok_seq is outside [0, B)
+ *     is skipped.  Two tokens of one call must not share a ring row;
+ *   - optional index stream (CSA): row i of idx_in (d_I dims, io_fmt) is copied
+ *     unchanged into win_idx at the same ring row (idx_in NULL = none).
+ * io_fmt HCA_F32 or HCA_BF16 (all rows); D a multiple of 8 (BF16) or 4 (F32), at
+ * most 4096 (BF16) / 2048 (F32); d_I likewise; rows and pitches 16-byte aligned;
+ * gamma_q, gamma_kv: [D] float, 16-byte aligned; eps >= 0 and finite.  Nq = 0 or Nt = 0 skips a part.
+ * The library needs no workspace for this call.
+ */
+typedef struct hca_qkv_prologue_desc {
+  uint32_t struct_size;
+  int32_t  io_fmt;
+  int32_t  Nq, H, D;
+  int32_t  Nt, B, W_cap, d_I;
+  double   eps;
+  const void*    q_in;
+  void*          q_out;
+  const float*   gamma_q;
+  const void*    kv_in;    int64_t kv_pitch;
+  const float*   gamma_kv;
+  const int32_t* tok_seq;   /* [Nt] */
+  const int64_t* tok_pos;   /* [Nt] */
+  void*          win;      int64_t win_pitch;
+  const void*    idx_in;   int64_t idx_pitch;
+  void*          win_idx;  int64_t win_idx_pitch;
+} hca_qkv_prologue_desc;
+
 int         hca_abi_version(void);
 const char* hca_last_error(void);
 /* sizeof the descriptor of an HCA_OP_* id, or of an HCA_STRUCT_* plane struct; 0 if unknown */
@@ -317,6 +360,7 @@ int hca_kv_compress(const hca_kv_compress_desc* desc, void* stream);
 int hca_indexer_topk(const hca_indexer_topk_desc* desc, void* stream);
 int hca_attn_decode(const hca_attn_desc* desc, void* stream);
 int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
+int hca_qkv_prologue(const hca_qkv_prologue_desc* desc, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,11 +18,11 @@ ERRORS = {-1: "HCA_E_NULL", -2: "HCA_E_SHAPE", -3: "HCA_E_ALIGN", -4: "HCA_E_DTY
           -5: "HCA_E_UNSUPPORTED", -6: "HCA_E_WORKSPACE", -7: "HCA_E_LAUNCH", -8: "HCA_E_VERSION"}
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
-OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL = 0, 1, 2, 3
+OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE = 0, 1, 2, 3, 4
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES = 100, 101
 
 EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes",
-           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill"]
+           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_qkv_prologue"]
 
 
 class KvPlanes(ctypes.Structure):
@@ -76,6 +76,16 @@ class AttnDesc(ctypes.Structure):
                 ("split_chunks", c_int32)]
 
 
+class QkvPrologueDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("io_fmt", c_int32), ("Nq", c_int32), ("H", c_int32),
+                ("D", c_int32), ("Nt", c_int32), ("B", c_int32), ("W_cap", c_int32), ("d_I", c_int32),
+                ("eps", c_double), ("q_in", c_void_p), ("q_out", c_void_p), ("gamma_q", c_void_p),
+                ("kv_in", c_void_p), ("kv_pitch", c_int64), ("gamma_kv", c_void_p),
+                ("tok_seq", c_void_p), ("tok_pos", c_void_p), ("win", c_void_p), ("win_pitch", c_int64),
+                ("idx_in", c_void_p), ("idx_pitch", c_int64), ("win_idx", c_void_p),
+                ("win_idx_pitch", c_int64)]
+
+
 class HcaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
@@ -98,7 +108,8 @@ def _load():
     lib.hca_workspace_bytes.restype = c_int
     lib.hca_workspace_bytes.argtypes = [c_int, c_void_p, ctypes.POINTER(c_size_t)]
     for name, dt in [("hca_kv_compress", KvCompressDesc), ("hca_indexer_topk", IndexerTopkDesc),
-                     ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc)]:
+                     ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc),
+                     ("hca_qkv_prologue", QkvPrologueDesc)]:
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [ctypes.POINTER(dt), c_void_p]

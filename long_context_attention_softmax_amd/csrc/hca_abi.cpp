@@ -250,6 +250,47 @@ int launched(hipError_t e) {
   return HCA_OK;
 }
 
+// ------------------------------------------------------------------- qkv prologue
+int validate_prologue(const hca_qkv_prologue_desc* d) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_qkv_prologue_desc), HCA_E_VERSION, "struct_size %u != %zu",
+          d->struct_size, sizeof(hca_qkv_prologue_desc));
+  REQUIRE(d->io_fmt == HCA_F32 || d->io_fmt == HCA_BF16, HCA_E_DTYPE, "io_fmt %d is not F32 or BF16", d->io_fmt);
+  const bool f32 = d->io_fmt == HCA_F32;
+  const int per = f32 ? 4 : 8, eb = f32 ? 4 : 2;
+  REQUIRE(d->Nq >= 0 && d->Nt >= 0, HCA_E_SHAPE, "Nq and Nt must be >= 0");
+  REQUIRE(d->D >= per && d->D % per == 0 && d->D <= hca::prologue_max_dim(f32), HCA_E_SHAPE,
+          "D=%d must be a multiple of %d in [%d, %d]", d->D, per, per, hca::prologue_max_dim(f32));
+  REQUIRE(d->eps >= 0.0 && std::isfinite(d->eps), HCA_E_SHAPE, "eps must be finite and >= 0");
+  REQUIRE(d->Nq == 0 || (d->H >= 1 && (int64_t)d->Nq * d->H + d->Nt < (1LL << 33)), HCA_E_SHAPE,
+          "H must be >= 1 (and Nq * H + Nt < 2^33)");
+  if (d->Nq > 0) {
+    REQUIRE(d->q_in && d->q_out && d->gamma_q, HCA_E_NULL, "q_in, q_out and gamma_q are required");
+    REQUIRE(aligned(d->q_in, 16) && aligned(d->q_out, 16) && aligned(d->gamma_q, 16), HCA_E_ALIGN,
+            "q rows must be 16-byte aligned");
+  }
+  if (d->Nt > 0) {
+    REQUIRE(d->kv_in && d->gamma_kv && d->tok_seq && d->tok_pos && d->win, HCA_E_NULL,
+            "kv_in, gamma_kv, tok_seq, tok_pos and win are required");
+    REQUIRE(d->B >= 1 && d->W_cap >= 1, HCA_E_SHAPE, "B and W_cap must be >= 1");
+    REQUIRE(d->kv_pitch >= (int64_t)eb * d->D && d->win_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE,
+            "kv_pitch / win_pitch < D elements");
+    REQUIRE(aligned(d->kv_in, 16) && aligned(d->win, 16) && d->kv_pitch % 16 == 0 && d->win_pitch % 16 == 0 &&
+            aligned(d->gamma_kv, 16) && aligned(d->tok_seq, 4) && aligned(d->tok_pos, 8), HCA_E_ALIGN,
+            "token rows must be 16-byte aligned");
+    if (d->idx_in) {
+      REQUIRE(d->win_idx, HCA_E_NULL, "idx_in needs win_idx");
+      REQUIRE(d->d_I >= per && d->d_I % per == 0 && d->d_I <= hca::prologue_max_dim(f32), HCA_E_SHAPE,
+              "d_I=%d must be a multiple of %d", d->d_I, per);
+      REQUIRE(d->idx_pitch >= (int64_t)eb * d->d_I && d->win_idx_pitch >= (int64_t)eb * d->d_I, HCA_E_SHAPE,
+              "idx_pitch / win_idx_pitch < d_I elements");
+      REQUIRE(aligned(d->idx_in, 16) && aligned(d->win_idx, 16) && d->idx_pitch % 16 == 0 &&
+              d->win_idx_pitch % 16 == 0, HCA_E_ALIGN, "index-stream rows must be 16-byte aligned");
+    }
+  }
+  return HCA_OK;
+}
+
 int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   size_t ws = 0;
   int rc = validate_attn(d, prefill, &ws);
@@ -294,6 +335,7 @@ size_t hca_struct_size(int which) {
     case HCA_OP_INDEXER_TOPK: return sizeof(hca_indexer_topk_desc);
     case HCA_OP_ATTN_DECODE:
     case HCA_OP_ATTN_PREFILL: return sizeof(hca_attn_desc);
+    case HCA_OP_QKV_PROLOGUE: return sizeof(hca_qkv_prologue_desc);
     case HCA_STRUCT_KV_PLANES: return sizeof(hca_kv_planes);
     case HCA_STRUCT_IDX_PLANES: return sizeof(hca_idx_planes);
     default: return 0;
@@ -331,6 +373,10 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
       rc = HCA_OK;
       break;
     }
+    case HCA_OP_QKV_PROLOGUE:
+      rc = validate_prologue(static_cast<const hca_qkv_prologue_desc*>(desc));
+      ws = 0;
+      break;
     default: return fail(HCA_E_SHAPE, "unknown op %d", op);
   }
   if (rc) return rc;
@@ -389,5 +435,20 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
 int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }
 
 int hca_attn_prefill(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 1); }
+
+int hca_qkv_prologue(const hca_qkv_prologue_desc* d, void* stream) {
+  int rc = validate_prologue(d);
+  if (rc) return rc;
+  hca::PrologueArgs a{};
+  a.Nq = d->Nq; a.H = d->Nq > 0 ? d->H : 0; a.D = d->D; a.Nt = d->Nt; a.W_cap = d->W_cap; a.B = d->B;
+  a.d_I = d->d_I; a.f32 = d->io_fmt == HCA_F32; a.eps = d->eps;
+  a.q_in = static_cast<const char*>(d->q_in); a.q_out = static_cast<char*>(d->q_out); a.gamma_q = d->gamma_q;
+  a.kv_in = static_cast<const char*>(d->kv_in); a.kv_pitch = d->kv_pitch; a.gamma_kv = d->gamma_kv;
+  a.tok_seq = d->tok_seq; a.tok_pos = d->tok_pos;
+  a.win = static_cast<char*>(d->win); a.win_pitch = d->win_pitch;
+  a.idx_in = d->Nt > 0 ? static_cast<const char*>(d->idx_in) : nullptr; a.idx_pitch = d->idx_pitch;
+  a.win_idx = static_cast<char*>(d->win_idx); a.win_idx_pitch = d->win_idx_pitch;
+  return launched(hca::launch_prologue(a, static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

@@ -79,4 +79,17 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
 int64_t attention_split_runs(int mode, int k, int n_win, int64_t max_visible, int split_chunks);
 int attention_max_runs();
 
+struct PrologueArgs {
+  int Nq, H, D, Nt, W_cap, B, d_I, f32;
+  double eps;
+  const char* q_in; char* q_out; const float* gamma_q;      // q rows: [Nq * H, D], contiguous
+  const char* kv_in; int64_t kv_pitch; const float* gamma_kv;
+  const int32_t* tok_seq; const int64_t* tok_pos;
+  char* win; int64_t win_pitch;                             // ring row: seq * W_cap + pos mod W_cap
+  const char* idx_in; int64_t idx_pitch;                    // optional index stream (copied)
+  char* win_idx; int64_t win_idx_pitch;
+};
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+int prologue_max_dim(int f32);
+
 }  // namespace hca

@@ -264,3 +264,53 @@ def hca_attn_decode(*args, **kw) -> torch.Tensor:
 def hca_attn_prefill(*args, **kw) -> torch.Tensor:
     """One-softmax attention of a chunk of consecutive query positions."""
     return _attn(True, *args, **kw)
+
+
+def hca_qkv_prologue(q_in: Optional[torch.Tensor], gamma_q: Optional[torch.Tensor],
+                     kv_in: Optional[torch.Tensor], gamma_kv: Optional[torch.Tensor],
+                     tok_seq: Optional[torch.Tensor], tok_pos: Optional[torch.Tensor],
+                     win: Optional[torch.Tensor], *, eps: float = 1e-6,
+                     q_out: Optional[torch.Tensor] = None, idx_in: Optional[torch.Tensor] = None,
+                     win_idx: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """Normalize q ([Nq, H, D], into ``q_out``, default in place) and the new tokens
+    ``kv_in`` ([Nt, D]), writing each token to the ring ``win`` ([B, W_cap, D]) at
+    (tok_seq, tok_pos mod W_cap); ``idx_in`` rows are copied to ``win_idx`` at the
+    same slots (see include/hca.h).  Returns q_out."""
+    _need_cuda(q_in, gamma_q, kv_in, gamma_kv, tok_seq, tok_pos, win, q_out, idx_in, win_idx)
+    d = A.new_desc(A.QkvPrologueDesc)
+    ref = q_in if q_in is not None else kv_in
+    if ref is None:
+        raise ValueError("nothing to do: q_in and kv_in are both None")
+    d.io_fmt = A.F32 if ref.dtype == torch.float32 else A.BF16
+    d.eps = float(eps)
+    d.D = ref.shape[-1]
+    if q_in is not None:
+        if not q_in.is_contiguous() or q_in.dim() != 3:
+            raise ValueError("q_in must be contiguous [Nq, H, D]")
+        q_out = q_in if q_out is None else q_out
+        if q_out.shape != q_in.shape or q_out.dtype != q_in.dtype or not q_out.is_contiguous():
+            raise ValueError("q_out must match q_in")
+        d.Nq, d.H = q_in.shape[0], q_in.shape[1]
+        d.q_in, d.q_out, d.gamma_q = _ptr(q_in), _ptr(q_out), _ptr(_f32(gamma_q, d.D, "gamma_q"))
+    if kv_in is not None:
+        if kv_in.dim() != 2 or win.dim() != 3:
+            raise ValueError("kv_in must be [Nt, D] and win [B, W_cap, D]")
+        if tok_seq.dtype != torch.int32:
+            raise ValueError("tok_seq must be int32")
+        d.Nt, d.B, d.W_cap = kv_in.shape[0], win.shape[0], win.shape[1]
+        d.kv_in, d.kv_pitch, d.gamma_kv = _ptr(kv_in), _pitch(kv_in), _ptr(_f32(gamma_kv, d.D, "gamma_kv"))
+        d.tok_seq, d.tok_pos = _ptr(tok_seq.contiguous()), _ptr(_i64(tok_pos, d.Nt, "tok_pos"))
+        w2 = win.reshape(-1, win.shape[-1])
+        d.win, d.win_pitch = _ptr(w2), _pitch(w2)
+        if idx_in is not None:
+            wi = win_idx.reshape(-1, win_idx.shape[-1])
+            d.d_I = idx_in.shape[-1]
+            d.idx_in, d.idx_pitch, d.win_idx, d.win_idx_pitch = _ptr(idx_in), _pitch(idx_in), _ptr(wi), _pitch(wi)
+    A.check(A.lib.hca_qkv_prologue(ctypes.byref(d), _stream()))
+    return q_out
+
+
+def _f32(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
+    if t is None or t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    return t

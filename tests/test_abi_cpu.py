@@ -29,9 +29,10 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 3
+    assert A.lib.hca_abi_version() == 4
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
+                    (A.OP_QKV_PROLOGUE, A.QkvPrologueDesc),
                     (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
         assert A.lib.hca_struct_size(op) == ctypes.sizeof(cls), cls
     assert A.lib.hca_struct_size(12345) == 0
@@ -246,6 +247,44 @@ def test_attention_window_only_validation():
     n = ctypes.c_size_t(0)
     assert A.lib.hca_workspace_bytes(A.OP_ATTN_DECODE, ctypes.byref(attn_desc(**bare)), ctypes.byref(n)) == 0
     assert 0 < n.value < 64 << 20
+
+
+def pro_desc(**kw):
+    d = A.new_desc(A.QkvPrologueDesc)
+    d.io_fmt, d.Nq, d.H, d.D, d.Nt, d.B, d.W_cap, d.eps = A.BF16, 4, 64, 512, 4, 4, 128, 1e-6
+    d.q_in = d.q_out = d.gamma_q = d.kv_in = d.gamma_kv = d.tok_seq = d.tok_pos = d.win = FAKE
+    d.kv_pitch = d.win_pitch = 1024
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_prologue_validation():
+    # every case fails validation (a valid descriptor would launch on fake pointers)
+    n = ctypes.c_size_t(7)
+    assert A.lib.hca_workspace_bytes(A.OP_QKV_PROLOGUE, ctypes.byref(pro_desc()), ctypes.byref(n)) == 0
+    assert n.value == 0                                          # no workspace
+    d = pro_desc()
+    d.struct_size = 12
+    assert call("hca_qkv_prologue", d) == -8
+    assert call("hca_qkv_prologue", pro_desc(io_fmt=A.FP8_E4M3)) == -4
+    assert call("hca_qkv_prologue", pro_desc(D=500)) == -2       # not a multiple of 8
+    assert call("hca_qkv_prologue", pro_desc(D=8192)) == -2      # more than a wave's registers hold
+    assert call("hca_qkv_prologue", pro_desc(eps=-1.0)) == -2
+    assert call("hca_qkv_prologue", pro_desc(eps=float("inf"))) == -2
+    assert call("hca_qkv_prologue", pro_desc(H=0)) == -2
+    assert call("hca_qkv_prologue", pro_desc(gamma_q=None)) == -1
+    assert call("hca_qkv_prologue", pro_desc(q_in=FAKE + 8)) == -3
+    assert call("hca_qkv_prologue", pro_desc(gamma_q=FAKE + 4)) == -3
+    assert call("hca_qkv_prologue", pro_desc(W_cap=0)) == -2
+    assert call("hca_qkv_prologue", pro_desc(win=None)) == -1
+    assert call("hca_qkv_prologue", pro_desc(kv_pitch=512)) == -2
+    assert call("hca_qkv_prologue", pro_desc(win_pitch=1032)) == -3
+    assert call("hca_qkv_prologue", pro_desc(idx_in=FAKE)) == -1                 # no win_idx
+    assert call("hca_qkv_prologue", pro_desc(idx_in=FAKE, win_idx=FAKE, d_I=100, idx_pitch=256,
+                                             win_idx_pitch=256)) == -2
+    assert call("hca_qkv_prologue", pro_desc(Nt=0, win=None, kv_in=None, D=20)) == -2   # q part alone still checked
+    assert call("hca_qkv_prologue", pro_desc(Nq=0, Nt=0)) == 0                   # nothing to do
 
 
 def test_binding_refuses_host_tensors():
