@@ -20,4 +20,4 @@ Pages cited (by title, with their site):
   * "DeepSeek V4: How They Crushed the Million-Token Memory Problem"
     (sameershanbhag.com), section "Two kinds of memory instead of one".
 """
-from . import quant, rope, pool, indexer, topk, attend, step, prologue  # noqa: F401
+from . import quant, rope, pool, indexer, topk, attend, step, prologue, project  # noqa: F401
