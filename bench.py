@@ -195,7 +195,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
-    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|prologue|hca|prefill)")
+    ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|prologue|outproj|hca|prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -356,6 +356,41 @@ def main():
                 config={"queries": T, "heads": H, "D": D, "tokens": T, "io": "bf16"})
             log(f"[bench] qkv prologue 4096 x 64 heads: {pm:.4f} ms, {pbytes / (pm * 1e-3) / 1e9:.0f} GB/s")
             del q, kv, ring, qo
+            torch.cuda.empty_cache()
+        # ---- grouped output projection (64 heads x 512 -> 8 groups x 1024) ----
+        if only in (None, "outproj"):
+            from long_context_attention_softmax_amd.ops import hca_out_proj
+            Hh, Dd, Gg, dg = 64, 512, 8, 1024
+            Kg = Hh // Gg * Dd
+            gen = torch.Generator(device="cuda").manual_seed(11)
+            wts = [(torch.randn((Gg, dg, Kg), generator=gen, device="cuda") * Kg ** -0.5).to(torch.bfloat16)
+                   for _ in range(4)]                                  # rotated so the cache never holds them
+            res = {}
+            for Nq in (32, 4096):
+                o = (torch.randn((Nq, Hh, Dd), generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
+                y = torch.empty((Nq, Gg, dg), dtype=torch.float32, device="cuda")
+                for i in range(args.warmup):
+                    hca_out_proj(o, wts[i % 4], G=Gg, y=y)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.steps)]
+                for i, (a, b) in enumerate(ev):
+                    a.record()
+                    hca_out_proj(o, wts[i % 4], G=Gg, y=y)
+                    b.record()
+                torch.cuda.synchronize()
+                pm = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+                wbytes = Gg * dg * Kg * 2
+                flops = 2.0 * Nq * Gg * dg * Kg
+                res[Nq] = pm
+                key = "decode_32" if Nq == 32 else "prefill_4096"
+                secondary[f"out_proj_{key}"] = dict(
+                    kernel_ms=round(pm, 5), weight_bytes=wbytes,
+                    gbps=round((wbytes + Nq * Hh * Dd * 2 + Nq * Gg * dg * 4) / (pm * 1e-3) / 1e9, 1),
+                    tflops=round(flops / (pm * 1e-3) / 1e12, 1),
+                    config={"rows": Nq, "heads": Hh, "D": Dd, "groups": Gg, "d_g": dg, "out": "f32"})
+                del o, y
+            log(f"[bench] out proj: decode {res[32]:.4f} ms, prefill {res[4096]:.4f} ms")
+            del wts
             torch.cuda.empty_cache()
         # ---- HCA decode at 1M ----------------------------------------------
         if only in (None, "hca"):

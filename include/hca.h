@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 4
+#define HCA_ABI_VERSION 5
 
 /* status codes */
 #define HCA_OK             0
@@ -83,6 +83,7 @@ extern "C" {
 #define HCA_OP_ATTN_DECODE  2
 #define HCA_OP_ATTN_PREFILL 3
 #define HCA_OP_QKV_PROLOGUE 4
+#define HCA_OP_OUT_PROJ     5
 #define HCA_STRUCT_KV_PLANES  100
 #define HCA_STRUCT_IDX_PLANES 101
 
@@ -349,6 +350,32 @@ typedef struct hca_qkv_prologue_desc {
   void*          win_idx;  int64_t win_idx_pitch;
 } hca_qkv_prologue_desc;
 
+/*
+ * Grouped output projection after attention.  "DeepSeek V4 infrastructure"
+ * (volanea.com), "Compression only works if the attention path is engineered end to
+ * end": CSA's attention ends in a grouped output projection.  Read as: the H heads
+ * form G consecutive groups of H / G heads; group g's head outputs, concatenated in
+ * head order (K_g = (H / G) * D values), are multiplied by the group's own weights,
+ * and the G results are concatenated:
+ *   y[n, g * d_g + c] = sum_{k < K_g} o[n, g * K_g + k] * W[g * d_g + c, k]
+ * o: Nq rows of H * D BF16 (attention's o, heads in order; pitch o_pitch bytes);
+ * W: G * d_g rows of K_g BF16 (output unit c of group g at row g * d_g + c; pitch
+ * w_pitch); y: Nq rows of G * d_g values in out_fmt (HCA_F32 or HCA_BF16, pitch
+ * y_pitch).  Products of BF16 values are exact; they are summed in binary32 in a
+ * fixed order (four partial sums over consecutive quarters of k, added in order),
+ * then rounded once to out_fmt.  Needs H % G == 0, K_g a multiple of 256, d_g a
+ * multiple of 32, 16-byte aligned rows (HCA_E_UNSUPPORTED / HCA_E_SHAPE /
+ * HCA_E_ALIGN otherwise).  No workspace.
+ */
+typedef struct hca_out_proj_desc {
+  uint32_t struct_size;
+  int32_t  out_fmt;
+  int32_t  Nq, H, D, G, d_g;
+  const void* o;  int64_t o_pitch;
+  const void* w;  int64_t w_pitch;
+  void*       y;  int64_t y_pitch;
+} hca_out_proj_desc;
+
 int         hca_abi_version(void);
 const char* hca_last_error(void);
 /* sizeof the descriptor of an HCA_OP_* id, or of an HCA_STRUCT_* plane struct; 0 if unknown */
@@ -361,6 +388,7 @@ int hca_indexer_topk(const hca_indexer_topk_desc* desc, void* stream);
 int hca_attn_decode(const hca_attn_desc* desc, void* stream);
 int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
 int hca_qkv_prologue(const hca_qkv_prologue_desc* desc, void* stream);
+int hca_out_proj(const hca_out_proj_desc* desc, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,11 +18,12 @@ ERRORS = {-1: "HCA_E_NULL", -2: "HCA_E_SHAPE", -3: "HCA_E_ALIGN", -4: "HCA_E_DTY
           -5: "HCA_E_UNSUPPORTED", -6: "HCA_E_WORKSPACE", -7: "HCA_E_LAUNCH", -8: "HCA_E_VERSION"}
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
-OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE = 0, 1, 2, 3, 4
+OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE, OP_OUT_PROJ = 0, 1, 2, 3, 4, 5
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES = 100, 101
 
 EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes",
-           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_qkv_prologue"]
+           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_qkv_prologue",
+           "hca_out_proj"]
 
 
 class KvPlanes(ctypes.Structure):
@@ -86,6 +87,12 @@ class QkvPrologueDesc(ctypes.Structure):
                 ("win_idx_pitch", c_int64)]
 
 
+class OutProjDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("out_fmt", c_int32), ("Nq", c_int32), ("H", c_int32),
+                ("D", c_int32), ("G", c_int32), ("d_g", c_int32), ("o", c_void_p), ("o_pitch", c_int64),
+                ("w", c_void_p), ("w_pitch", c_int64), ("y", c_void_p), ("y_pitch", c_int64)]
+
+
 class HcaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
@@ -109,7 +116,7 @@ def _load():
     lib.hca_workspace_bytes.argtypes = [c_int, c_void_p, ctypes.POINTER(c_size_t)]
     for name, dt in [("hca_kv_compress", KvCompressDesc), ("hca_indexer_topk", IndexerTopkDesc),
                      ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc),
-                     ("hca_qkv_prologue", QkvPrologueDesc)]:
+                     ("hca_qkv_prologue", QkvPrologueDesc), ("hca_out_proj", OutProjDesc)]:
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [ctypes.POINTER(dt), c_void_p]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libhca.so")
-SOURCES = ["hca_abi.cpp", "pool.hip", "indexer.hip", "attn.hip", "prologue.hip"]
+SOURCES = ["hca_abi.cpp", "pool.hip", "indexer.hip", "attn.hip", "prologue.hip", "gproj.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

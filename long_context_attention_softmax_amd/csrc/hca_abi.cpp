@@ -250,6 +250,31 @@ int launched(hipError_t e) {
   return HCA_OK;
 }
 
+// --------------------------------------------------------------- output projection
+int validate_out_proj(const hca_out_proj_desc* d) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_out_proj_desc), HCA_E_VERSION, "struct_size %u != %zu",
+          d->struct_size, sizeof(hca_out_proj_desc));
+  REQUIRE(d->out_fmt == HCA_F32 || d->out_fmt == HCA_BF16, HCA_E_DTYPE, "out_fmt %d is not F32 or BF16",
+          d->out_fmt);
+  REQUIRE(d->Nq >= 0 && d->H >= 1 && d->D >= 1 && d->G >= 1 && d->d_g >= 1, HCA_E_SHAPE, "bad shapes");
+  REQUIRE(d->H % d->G == 0, HCA_E_SHAPE, "H=%d is not a multiple of G=%d", d->H, d->G);
+  const int64_t K_g = (int64_t)(d->H / d->G) * d->D;
+  REQUIRE(K_g % hca::gproj_k_multiple() == 0 && K_g < (1LL << 30), HCA_E_UNSUPPORTED,
+          "K_g = H/G * D = %lld must be a multiple of %d", (long long)K_g, hca::gproj_k_multiple());
+  REQUIRE(d->d_g % 32 == 0 && (int64_t)d->G * (d->d_g / 32) < (1LL << 31), HCA_E_UNSUPPORTED,
+          "d_g=%d must be a multiple of 32", d->d_g);
+  REQUIRE(((int64_t)d->Nq + 31) / 32 < 65536, HCA_E_UNSUPPORTED, "Nq too large for one launch");
+  if (d->Nq == 0) return HCA_OK;
+  REQUIRE(d->o && d->w && d->y, HCA_E_NULL, "o, w and y are required");
+  const int eb = d->out_fmt == HCA_F32 ? 4 : 2;
+  REQUIRE(d->o_pitch >= 2LL * d->H * d->D && d->w_pitch >= 2 * K_g &&
+          d->y_pitch >= (int64_t)eb * d->G * d->d_g, HCA_E_SHAPE, "o/w/y pitch shorter than a row");
+  REQUIRE(aligned(d->o, 16) && aligned(d->w, 16) && aligned(d->y, eb) && d->o_pitch % 16 == 0 &&
+          d->w_pitch % 16 == 0 && d->y_pitch % eb == 0, HCA_E_ALIGN, "o / w rows must be 16-byte aligned");
+  return HCA_OK;
+}
+
 // ------------------------------------------------------------------- qkv prologue
 int validate_prologue(const hca_qkv_prologue_desc* d) {
   REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
@@ -336,6 +361,7 @@ size_t hca_struct_size(int which) {
     case HCA_OP_ATTN_DECODE:
     case HCA_OP_ATTN_PREFILL: return sizeof(hca_attn_desc);
     case HCA_OP_QKV_PROLOGUE: return sizeof(hca_qkv_prologue_desc);
+    case HCA_OP_OUT_PROJ: return sizeof(hca_out_proj_desc);
     case HCA_STRUCT_KV_PLANES: return sizeof(hca_kv_planes);
     case HCA_STRUCT_IDX_PLANES: return sizeof(hca_idx_planes);
     default: return 0;
@@ -375,6 +401,10 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
     }
     case HCA_OP_QKV_PROLOGUE:
       rc = validate_prologue(static_cast<const hca_qkv_prologue_desc*>(desc));
+      ws = 0;
+      break;
+    case HCA_OP_OUT_PROJ:
+      rc = validate_out_proj(static_cast<const hca_out_proj_desc*>(desc));
       ws = 0;
       break;
     default: return fail(HCA_E_SHAPE, "unknown op %d", op);
@@ -435,6 +465,18 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
 int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }
 
 int hca_attn_prefill(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 1); }
+
+int hca_out_proj(const hca_out_proj_desc* d, void* stream) {
+  int rc = validate_out_proj(d);
+  if (rc) return rc;
+  hca::GprojArgs a{};
+  a.M = d->Nq; a.G = d->G; a.d_g = d->d_g; a.out_f32 = d->out_fmt == HCA_F32;
+  a.K_g = (int64_t)(d->H / d->G) * d->D;
+  a.o = static_cast<const char*>(d->o); a.o_pitch = d->o_pitch;
+  a.w = static_cast<const char*>(d->w); a.w_pitch = d->w_pitch;
+  a.y = static_cast<char*>(d->y); a.y_pitch = d->y_pitch;
+  return launched(hca::launch_gproj(a, static_cast<hipStream_t>(stream)));
+}
 
 int hca_qkv_prologue(const hca_qkv_prologue_desc* d, void* stream) {
   int rc = validate_prologue(d);

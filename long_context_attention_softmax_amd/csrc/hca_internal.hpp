@@ -92,4 +92,14 @@ struct PrologueArgs {
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 int prologue_max_dim(int f32);
 
+struct GprojArgs {
+  int M, G, d_g, out_f32;
+  int64_t K_g;
+  const char* o; int64_t o_pitch;     // [M] rows of G * K_g BF16
+  const char* w; int64_t w_pitch;     // [G * d_g] rows of K_g BF16
+  char* y; int64_t y_pitch;           // [M] rows of G * d_g (f32 or BF16)
+};
+hipError_t launch_gproj(const GprojArgs& a, hipStream_t s);
+int gproj_k_multiple();
+
 }  // namespace hca

@@ -314,3 +314,26 @@ def _f32(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
     if t is None or t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
     return t
+
+
+def hca_out_proj(o: torch.Tensor, w: torch.Tensor, *, G: int, y: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Grouped output projection (see include/hca.h): o [Nq, H, D] BF16, w [G, d_g, K_g]
+    BF16 with K_g = H / G * D; returns y [Nq, G, d_g] (float32 or bfloat16)."""
+    _need_cuda(o, w, y)
+    if o.dim() != 3 or not o.is_contiguous() or w.dim() != 3 or not w.is_contiguous():
+        raise ValueError("o must be contiguous [Nq, H, D] and w contiguous [G, d_g, K_g]")
+    Nq, H, D = o.shape
+    d_g = w.shape[1]
+    if y is None:
+        y = torch.empty((Nq, G, d_g), dtype=out_dtype, device=o.device)
+    if not y.is_contiguous() or y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("y must be contiguous float32 or bfloat16 [Nq, G, d_g]")
+    d = A.new_desc(A.OutProjDesc)
+    d.out_fmt = A.F32 if y.dtype == torch.float32 else A.BF16
+    d.Nq, d.H, d.D, d.G, d.d_g = Nq, H, D, G, d_g
+    d.o, d.o_pitch = _ptr(o), H * D * 2
+    d.w, d.w_pitch = _ptr(w), w.shape[2] * 2
+    d.y, d.y_pitch = _ptr(y), G * d_g * y.element_size()
+    A.check(A.lib.hca_out_proj(ctypes.byref(d), _stream()))
+    return y

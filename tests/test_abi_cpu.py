@@ -29,10 +29,10 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 4
+    assert A.lib.hca_abi_version() == 5
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
-                    (A.OP_QKV_PROLOGUE, A.QkvPrologueDesc),
+                    (A.OP_QKV_PROLOGUE, A.QkvPrologueDesc), (A.OP_OUT_PROJ, A.OutProjDesc),
                     (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
         assert A.lib.hca_struct_size(op) == ctypes.sizeof(cls), cls
     assert A.lib.hca_struct_size(12345) == 0
@@ -285,6 +285,31 @@ def test_prologue_validation():
                                              win_idx_pitch=256)) == -2
     assert call("hca_qkv_prologue", pro_desc(Nt=0, win=None, kv_in=None, D=20)) == -2   # q part alone still checked
     assert call("hca_qkv_prologue", pro_desc(Nq=0, Nt=0)) == 0                   # nothing to do
+
+
+def proj_desc(**kw):
+    d = A.new_desc(A.OutProjDesc)
+    d.out_fmt, d.Nq, d.H, d.D, d.G, d.d_g = A.F32, 32, 64, 512, 8, 1024
+    d.o, d.o_pitch, d.w, d.w_pitch, d.y, d.y_pitch = FAKE, 65536, FAKE, 8192, FAKE, 32768
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_out_proj_validation():
+    # every case fails validation (a valid descriptor would launch on fake pointers)
+    n = ctypes.c_size_t(7)
+    assert A.lib.hca_workspace_bytes(A.OP_OUT_PROJ, ctypes.byref(proj_desc()), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert call("hca_out_proj", proj_desc(out_fmt=A.FP8_E4M3)) == -4
+    assert call("hca_out_proj", proj_desc(G=3)) == -2                  # 64 heads do not split in 3
+    assert call("hca_out_proj", proj_desc(G=64, D=128)) == -5          # K_g = 128: not a multiple of 256
+    assert call("hca_out_proj", proj_desc(d_g=1000)) == -5
+    assert call("hca_out_proj", proj_desc(w=None)) == -1
+    assert call("hca_out_proj", proj_desc(w_pitch=4096)) == -2         # shorter than K_g = 4096 BF16
+    assert call("hca_out_proj", proj_desc(o=FAKE + 8)) == -3
+    assert call("hca_out_proj", proj_desc(y_pitch=32770)) == -3
+    assert call("hca_out_proj", proj_desc(Nq=0)) == 0
 
 
 def test_binding_refuses_host_tensors():
