@@ -5,12 +5,12 @@
 // a batch of G products of o's group slice [M, K_g] with W[g]^T [K_g, d_g].
 //
 // A workgroup computes one group's tile of 64 rows (two 32-row blocks; one when M
-// <= 32) by 32 output units.  Its four waves split K_g in four slices; in each,
-// lane (j, u) streams 64 contiguous bytes of output unit j's weights (k = kb + 32u
-// .. kb + 32u + 31) and of the matching activation rows per 64-k chunk, and the
-// chunk feeds four 32x32x16 BF16 MFMAs per row block (MFMA s takes the lane's
-// elements 8s .. 8s + 7: the same k permutation for both operands).  Loads run
-// one chunk ahead of the products.  The four partial tiles are summed through LDS
+// <= 32) by 32 output units.  Its four waves split K_g in four slices; per 64-k
+// chunk each wave loads its weight tile (32 units x 128 bytes) and activation tiles
+// with coalesced 16-byte loads (eight lanes per 128-byte row), stages them in its own
+// LDS region, and reads them back in the MFMA operand layout for four 32x32x16 BF16
+// MFMAs per row block (MFMA s: lane (j, u) takes row j's k = 32u + 8s .. + 7 of
+// both tiles).  Loads run one chunk ahead of the products.  The four partial tiles are summed through LDS
 // in wave order (deterministic).  With M <= 64 every
 // weight is read once per launch: bound by HBM bandwidth on W.
 #include "device_common.hpp"
@@ -34,62 +34,92 @@ __device__ __forceinline__ uint16_t bf16_of(float f) {          // round to near
   return (uint16_t)(u >> 16);
 }
 
-template <int RB, bool OUT_F32>
-__global__ void __launch_bounds__(64 * kGpWaves) gproj_kernel(GprojArgs a) {
-  __shared__ float s_part[kGpWaves - 1][RB][16][64];
+// LDS tile rows: 64 k of BF16 (128 bytes) plus 16 bytes of padding, so the lanes of
+// an MFMA operand read (32 rows, the same 16-byte column) spread over the banks
+constexpr int kTileRow = 144;
+
+// NW waves split K_g (8 with one row block, 4 with two: LDS holds both)
+template <int RB, bool OUT_F32, int NW>
+__global__ void __launch_bounds__(64 * NW) gproj_kernel(GprojArgs a) {
+  __shared__ float s_part[NW - 1][RB][16][64];
+  // per wave: the weight tile (32 units) and RB activation tiles (32 rows each) of a chunk
+  __shared__ __attribute__((aligned(16))) char s_tile[NW][1 + RB][32 * kTileRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 31, u = lane >> 5;
   const int tiles_g = a.d_g / 32;
   const int g = blockIdx.x / tiles_g, c0 = (blockIdx.x - g * tiles_g) * 32;
   const int m0 = blockIdx.y * 32 * RB;
-  const int64_t kslice = a.K_g / kGpWaves;
-  // this lane's weight row (output unit c0 + j) and activation rows; rows past M read
-  // row 0 instead (a row of the product depends on its own activation row only, and
-  // such rows are not stored)
-  const char* wrow = a.w + ((int64_t)g * a.d_g + c0 + j) * a.w_pitch + (wave * kslice + 32 * u) * 2;
-  const char* arow[RB];
+  const int64_t kslice = a.K_g / NW;
+  // coalesced loads: in load q, lane l brings 16 bytes (k = 8 (l % 8) .. + 7 of the
+  // chunk) of tile row 8q + l / 8; rows past M read row 0 instead (a row of the
+  // product depends on its own activation row only, and such rows are not stored)
+  const int lr = lane >> 3, lc = lane & 7;
+  const char* const wsrc = a.w + ((int64_t)g * a.d_g + c0 + lr) * a.w_pitch + (wave * kslice + 8 * lc) * 2;
+  const int64_t wstep = 8 * a.w_pitch;                       // tile row t + 8
+  const char* xsrc[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = m0 + 32 * rb + j;
-    arow[rb] = a.o + (int64_t)(r < a.M ? r : 0) * a.o_pitch + (g * a.K_g + wave * kslice + 32 * u) * 2;
-  }
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = m0 + 32 * rb + 8 * q + lr;
+      xsrc[rb][q] = a.o + (int64_t)(r < a.M ? r : 0) * a.o_pitch + (g * a.K_g + wave * kslice + 8 * lc) * 2;
+    }
+  char* const tiles = s_tile[wave][0];
+  const int st_off = lr * kTileRow + 16 * lc;                // this lane's staging slot (tile row lr + 8q)
   v16f acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) acc[rb] = (v16f){};
   const int nch = (int)(kslice / 64);
-  uint4 wb[4], xb[RB][4];
-  auto load = [&](int ch, uint4 (&w4)[4], uint4 (&x4)[RB][4]) {
-    const uint4* wp = reinterpret_cast<const uint4*>(wrow + (int64_t)ch * 128);
+  {                                                // chunk 0 into the tiles
+    uint4 w0[4], x0[RB][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w4[q] = wp[q];
+    for (int q = 0; q < 4; ++q) {
+      w0[q] = *reinterpret_cast<const uint4*>(wsrc + q * wstep);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint4* xp = reinterpret_cast<const uint4*>(arow[rb] + (int64_t)ch * 128);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x4[rb][q] = xp[q];
+      for (int rb = 0; rb < RB; ++rb) x0[rb][q] = *reinterpret_cast<const uint4*>(xsrc[rb][q]);
     }
-  };
-  load(0, wb, xb);
-  for (int ch = 0; ch < nch; ++ch) {
-    uint4 wn[4], xn[RB][4];
-    if (ch + 1 < nch) load(ch + 1, wn, xn);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<uint4*>(tiles + st_off + 8 * q * kTileRow) = w0[q];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(xb[rb][s]), as_bf(wb[s]), acc[rb], 0, 0, 0);
+        *reinterpret_cast<uint4*>(tiles + (1 + rb) * 32 * kTileRow + st_off + 8 * q * kTileRow) = x0[rb][q];
     }
-    if (ch + 1 < nch) {
+  }
+  for (int ch = 0; ch < nch; ++ch) {
+    const bool more = ch + 1 < nch;                // uniform
+    const int64_t nxt = (int64_t)(more ? ch + 1 : ch) * 128;
+    uint4 wn[4], xn[RB][4];                        // the next chunk, in flight while this one multiplies
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wn[q] = *reinterpret_cast<const uint4*>(wsrc + q * wstep + nxt);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) xn[rb][q] = *reinterpret_cast<const uint4*>(xsrc[rb][q] + nxt);
+    }
+    // MFMA s: lane (j, u) supplies row j's k = 32u + 8s .. + 7 of both tiles
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = j * kTileRow + 64 * u + 16 * s;
+      const uint4 b = *reinterpret_cast<const uint4*>(tiles + off);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf(*reinterpret_cast<const uint4*>(tiles + (1 + rb) * 32 * kTileRow + off)), as_bf(b), acc[rb], 0, 0, 0);
+    }
+    // one wave's LDS operations run in order: the reads above complete before the
+    // next chunk overwrites the tiles
+    if (more) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        wb[q] = wn[q];
+        *reinterpret_cast<uint4*>(tiles + st_off + 8 * q * kTileRow) = wn[q];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) xb[rb][q] = xn[rb][q];
+        for (int rb = 0; rb < RB; ++rb)
+          *reinterpret_cast<uint4*>(tiles + (1 + rb) * 32 * kTileRow + st_off + 8 * q * kTileRow) = xn[rb][q];
       }
     }
   }
   // partial tiles of waves 1..3 through LDS; wave 0 sums in wave order and stores
-  if (wave > 0) {
+  if (wave > 0) {   // partial tiles of the other waves
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -103,7 +133,7 @@ __global__ void __launch_bounds__(64 * kGpWaves) gproj_kernel(GprojArgs a) {
     for (int i = 0; i < 16; ++i) {
       float v = acc[rb][i];
 #pragma unroll
-      for (int w = 0; w < kGpWaves - 1; ++w) v += s_part[w][rb][i][lane];
+      for (int w = 0; w < NW - 1; ++w) v += s_part[w][rb][i][lane];
       // accumulator layout of the 32x32 product: lane (j, u), element i holds row
       // 8 (i / 4) + 4u + i % 4 of column j
       const int row = m0 + 32 * rb + 8 * (i >> 2) + 4 * u + (i & 3);
@@ -124,13 +154,15 @@ hipError_t launch_gproj(const GprojArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const bool one = a.M <= 32;
   const dim3 grid((unsigned)(a.G * (a.d_g / 32)), (unsigned)((a.M + (one ? 31 : 63)) / (one ? 32 : 64)));
-  const dim3 block(64 * kGpWaves);
-  if (one) {
-    if (a.out_f32) hipLaunchKernelGGL((gproj_kernel<1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gproj_kernel<1, false>), grid, block, 0, s, a);
+  if (one && a.K_g % (8 * 64) == 0) {
+    if (a.out_f32) hipLaunchKernelGGL((gproj_kernel<1, true, 8>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gproj_kernel<1, false, 8>), grid, dim3(512), 0, s, a);
+  } else if (one) {
+    if (a.out_f32) hipLaunchKernelGGL((gproj_kernel<1, true, kGpWaves>), grid, dim3(64 * kGpWaves), 0, s, a);
+    else hipLaunchKernelGGL((gproj_kernel<1, false, kGpWaves>), grid, dim3(64 * kGpWaves), 0, s, a);
   } else {
-    if (a.out_f32) hipLaunchKernelGGL((gproj_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gproj_kernel<2, false>), grid, block, 0, s, a);
+    if (a.out_f32) hipLaunchKernelGGL((gproj_kernel<2, true, kGpWaves>), grid, dim3(64 * kGpWaves), 0, s, a);
+    else hipLaunchKernelGGL((gproj_kernel<2, false, kGpWaves>), grid, dim3(64 * kGpWaves), 0, s, a);
   }
   return hipGetLastError();
 }
