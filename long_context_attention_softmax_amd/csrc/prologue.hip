@@ -100,11 +100,30 @@ __device__ __forceinline__ void norm_rows(const char* src, int64_t src_pitch, ch
           for (int e = 0; e < 4; ++e)
             ow[e] = __float_as_uint((float)(lane_elem<true>(v[r][i], e) * inv * (double)g[e]));
         } else {
+          // fast path: the binary32 product x * fl32(inv * gamma) is within two binary32
+          // units of the exact value, so unless its low 16 bits lie within 4 units of
+          // the BF16 midpoint its nearest-even BF16 code is the exact value's; lanes
+          // with such an element redo the vector in fp64
+          bool slow = false;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint16_t lo = bf16_rne(lane_elem<false>(v[r][i], 2 * e) * inv * (double)g[2 * e]);
-            const uint16_t hi = bf16_rne(lane_elem<false>(v[r][i], 2 * e + 1) * inv * (double)g[2 * e + 1]);
-            ow[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+            uint32_t hw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float sc = (float)(inv * (double)g[2 * e + h]);
+              const uint32_t y = __float_as_uint((float)lane_elem<false>(v[r][i], 2 * e + h) * sc);
+              slow |= (y & 0xFFFFu) - 0x7FFCu <= 8u;
+              hw[h] = (y + 0x7FFFu + ((y >> 16) & 1u)) >> 16;
+            }
+            ow[e] = hw[0] | (hw[1] << 16);
+          }
+          if (slow) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint16_t lo = bf16_rne(lane_elem<false>(v[r][i], 2 * e) * inv * (double)g[2 * e]);
+              const uint16_t hi = bf16_rne(lane_elem<false>(v[r][i], 2 * e + 1) * inv * (double)g[2 * e + 1]);
+              ow[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+            }
           }
         }
         reinterpret_cast<uint4*>(dst + r * dst_pitch)[vi] = o;
