@@ -57,3 +57,18 @@ def test_window_only_fixed_split_invariant(gpu):
     _print("window-only, split_chunks=1: parity, then each query alone vs reversed batch")
     run_and_compare(lay, g, dev=dev)
     _check_invariant(dev, [list(range(dev.Nq))[::-1]])
+
+
+@pytest.mark.parametrize("split", [0, 1])
+def test_window_only_empty_set(gpu, split):
+    """n_win = 0 in the window-only mode: every set is empty, so o = 0 and lse = the
+    sink (the oracle's attention over no keys); default plan and fixed split."""
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    g = replace(synth.FULL_GEOMETRY, n_win=0)
+    lens = np.array([1, 300, 5000], np.int64)
+    lay = synth.swa_layer(np.random.default_rng(65), g, lens, 16)
+    dev = DeviceLayer.from_host(lay, g)
+    dev.split_chunks = split
+    _print(f"window-only with n_win=0, split_chunks={split}")
+    ref, _, err = run_and_compare(lay, g, dev=dev)
+    assert np.all(ref["o"] == 0) and err == 0.0

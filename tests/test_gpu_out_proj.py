@@ -67,3 +67,13 @@ def test_out_proj_full_size_sampled(gpu):
         err = row_rel_err(got.reshape(len(rows), -1), ref.reshape(len(rows), -1))
         _print(f"out proj Nq={Nq} d_g={d_g}: {len(rows)} rows checked, rel err {err:.2e}")
         assert err <= 1e-4
+
+
+def test_out_proj_no_rows(gpu):
+    """Zero rows: nothing launched, the (empty) result returned."""
+    from long_context_attention_softmax_amd.ops import hca_out_proj
+    o = torch.zeros((0, H, D), dtype=torch.bfloat16, device=gpu)
+    w = torch.zeros((G, 32, H // G * D), dtype=torch.bfloat16, device=gpu)
+    y = hca_out_proj(o, w, G=G)
+    torch.cuda.synchronize()
+    assert y.shape == (0, G, 32)

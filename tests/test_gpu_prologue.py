@@ -114,3 +114,31 @@ def test_step_with_prologue(gpu):
                          torch.from_numpy(seq).to(gpu), torch.from_numpy(pos).to(gpu), dev.win, eps=eps)
         ref, _, err = run_and_compare(ref_lay, g, dev=dev)
         _print(f"  rel err {err:.2e}")
+
+
+def test_prologue_one_part_only(gpu):
+    """Only queries (no tokens), then only tokens (no queries): each part alone, the
+    other's buffers untouched."""
+    from long_context_attention_softmax_amd.ops import hca_qkv_prologue
+    from oracle import quant
+    rng = np.random.default_rng(73)
+    D, H = 512, 16
+    q = _bf16(rng.normal(size=(3, H, D)) * 4.0)
+    gq = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    dq = _dev_bits(q, gpu)
+    _print("prologue: queries only")
+    hca_qkv_prologue(dq, torch.from_numpy(gq).to(gpu), None, None, None, None, None)
+    want, fr = opro.encode(opro.rms_norm(quant.bf16_decode(q), gq, 1e-6), "bf16")
+    got = to_np(dq)
+    assert np.array_equal(got[~fr], want[~fr])
+    tok = _bf16(rng.normal(size=(2, D)))
+    ring = np.zeros((2, 4, D), np.uint16)
+    dring = _dev_bits(ring, gpu)
+    gk = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    _print("prologue: tokens only")
+    hca_qkv_prologue(None, None, _dev_bits(tok, gpu), torch.from_numpy(gk).to(gpu),
+                     torch.tensor([1, 0], dtype=torch.int32, device=gpu),
+                     torch.tensor([6, 3], dtype=torch.int64, device=gpu), dring)
+    wk, fk = opro.encode(opro.rms_norm(quant.bf16_decode(tok), gk, 1e-6), "bf16")
+    ring_w = opro.append_ring(ring, np.array([1, 0]), np.array([6, 3]), wk)
+    assert not fk.any() and np.array_equal(to_np(dring), ring_w)
