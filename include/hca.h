@@ -362,7 +362,8 @@ typedef struct hca_qkv_prologue_desc {
  * W: G * d_g rows of K_g BF16 (output unit c of group g at row g * d_g + c; pitch
  * w_pitch); y: Nq rows of G * d_g values in out_fmt (HCA_F32 or HCA_BF16, pitch
  * y_pitch).  Products of BF16 values are exact; they are summed in binary32 in a
- * fixed order (four partial sums over consecutive quarters of k, added in order),
+ * fixed order (up to 64 rows: partial sums over consecutive quarters or eighths of
+ * k, added in order; more rows with d_g a multiple of 128: one sum over k in order),
  * then rounded once to out_fmt.  Needs H % G == 0, K_g a multiple of 256, d_g a
  * multiple of 32, 16-byte aligned rows (HCA_E_UNSUPPORTED / HCA_E_SHAPE /
  * HCA_E_ALIGN otherwise).  No workspace.

@@ -146,12 +146,117 @@ __global__ void __launch_bounds__(64 * NW) gproj_kernel(GprojArgs a) {
   }
 }
 
+// Many rows (> 64): one group's 128-row x 128-unit tile per workgroup over the whole
+// of K_g.  Per 64-k chunk the four waves load both operand tiles together (eight
+// lanes per 128-byte row, coalesced) into a double-buffered LDS pair; wave w then
+// computes rows 64 (w / 2) .. + 63 by units 64 (w % 2) .. + 63 as 2 x 2 blocks of
+// 32x32x16 BF16 MFMAs, each operand fragment read once per k step and used twice.
+// Each output is one wave's sum over k in order (deterministic).
+constexpr int kTB = 128;          // tile rows and units
+
+template <bool OUT_F32>
+__global__ void __launch_bounds__(256) gproj_tiled_kernel(GprojArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_a[2][kTB * kTileRow];
+  __shared__ __attribute__((aligned(16))) char s_w[2][kTB * kTileRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, u = lane >> 5;
+  const int tiles_g = a.d_g / kTB;
+  const int g = blockIdx.x / tiles_g, c0 = (blockIdx.x - g * tiles_g) * kTB;
+  const int m0 = blockIdx.y * kTB;
+  // load slot q of thread t: tile row (256 q + t) / 8, 16-byte column t % 8
+  const int lr = tid >> 3, lc = tid & 7;
+  const char* asrc[4];
+  const char* wsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = 32 * q + lr;
+    const int r = m0 + t;
+    asrc[q] = a.o + (int64_t)(r < a.M ? r : 0) * a.o_pitch + ((int64_t)g * a.K_g + 8 * lc) * 2;
+    wsrc[q] = a.w + ((int64_t)g * a.d_g + c0 + t) * a.w_pitch + 8 * lc * 2;
+  }
+  const int st = lr * kTileRow + 16 * lc;                    // + 32 q rows
+  v16f acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = (v16f){};
+  const int nch = (int)(a.K_g / 64);
+  {
+    uint4 ra[4], rw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = *reinterpret_cast<const uint4*>(asrc[q]);
+      rw[q] = *reinterpret_cast<const uint4*>(wsrc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<uint4*>(s_a[0] + st + 32 * q * kTileRow) = ra[q];
+      *reinterpret_cast<uint4*>(s_w[0] + st + 32 * q * kTileRow) = rw[q];
+    }
+  }
+  __syncthreads();
+  const int ar = 64 * (wave >> 1), wr = 64 * (wave & 1);    // this wave's rows and units in the tile
+  for (int ch = 0; ch < nch; ++ch) {
+    const int b = ch & 1;
+    const bool more = ch + 1 < nch;                          // uniform
+    const int64_t nxt = (int64_t)(more ? ch + 1 : ch) * 128;
+    uint4 ra[4], rw[4];                                      // the next chunk, in flight
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = *reinterpret_cast<const uint4*>(asrc[q] + nxt);
+      rw[q] = *reinterpret_cast<const uint4*>(wsrc[q] + nxt);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = j * kTileRow + 64 * u + 16 * s;
+      v8bf fa[2], fw[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        fa[x] = as_bf(*reinterpret_cast<const uint4*>(s_a[b] + (ar + 32 * x) * kTileRow + off));
+        fw[x] = as_bf(*reinterpret_cast<const uint4*>(s_w[b] + (wr + 32 * x) * kTileRow + off));
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fw[y], acc[x][y], 0, 0, 0);
+    }
+    if (more) {                                              // the other buffer: no one reads it now
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<uint4*>(s_a[b ^ 1] + st + 32 * q * kTileRow) = ra[q];
+        *reinterpret_cast<uint4*>(s_w[b ^ 1] + st + 32 * q * kTileRow) = rw[q];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = m0 + ar + 32 * x + 8 * (i >> 2) + 4 * u + (i & 3);
+        if (row < a.M) {
+          char* yp = a.y + (int64_t)row * a.y_pitch + ((int64_t)g * a.d_g + c0 + wr + 32 * y + j) * (OUT_F32 ? 4 : 2);
+          if (OUT_F32) *reinterpret_cast<float*>(yp) = acc[x][y][i];
+          else *reinterpret_cast<uint16_t*>(yp) = bf16_of(acc[x][y][i]);
+        }
+      }
+}
+
 }  // namespace
 
 int gproj_k_multiple() { return kGpWaves * 64; }
 
 hipError_t launch_gproj(const GprojArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.M > 64 && a.d_g % kTB == 0) {                       // many rows: shared operand tiles
+    const dim3 grid((unsigned)(a.G * (a.d_g / kTB)), (unsigned)((a.M + kTB - 1) / kTB));
+    if (a.out_f32) hipLaunchKernelGGL(gproj_tiled_kernel<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(gproj_tiled_kernel<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const bool one = a.M <= 32;
   const dim3 grid((unsigned)(a.G * (a.d_g / 32)), (unsigned)((a.M + (one ? 31 : 63)) / (one ? 32 : 64)));
   if (one && a.K_g % (8 * 64) == 0) {

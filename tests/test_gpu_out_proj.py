@@ -33,11 +33,13 @@ def _dev(bits, gpu):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(gpu).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("Nq", [1, 5, 32, 33, 100])
+# (rows, units per group): up to 64 rows the K-split kernel; more rows with units a
+# multiple of 128 the tiled kernel (ragged last row tile included)
+@pytest.mark.parametrize("Nq,d_g", [(1, 64), (5, 64), (32, 64), (33, 64), (100, 64), (65, 128), (100, 128),
+                                    (300, 256)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_out_proj_parity(gpu, Nq, out):
+def test_out_proj_parity(gpu, Nq, d_g, out):
     from long_context_attention_softmax_amd.ops import hca_out_proj
-    d_g = 64
     o, w = _inputs(80 + Nq, Nq, d_g)
     ref = project.grouped_out_proj(quant.bf16_decode(o), quant.bf16_decode(w))
     _print(f"out proj Nq={Nq} G={G} d_g={d_g} out={out}")
