@@ -247,7 +247,8 @@ typedef struct hca_indexer_topk_desc {
  *   lse = M + log(e^(sigma_h - M) + sum_a e^(l_a - M))        (optional output)
  * io_fmt HCA_F32 needs cache fmt HCA_F32 (fp64 arithmetic, any D <= 1024, at most
  * 8192 keys per query); io_fmt HCA_BF16 needs cache fmt HCA_FP8_E4M3, D = 512,
- * D_r = 64, H a multiple of 16 up to 64 (BF16 MFMA, fp32 softmax).
+ * D_r = 64, H a multiple of 16 up to 64 (BF16 MFMA, fp32 softmax), with q, o, the
+ * ring and the cache rows 16-byte aligned (HCA_E_ALIGN otherwise).
  * The ring must hold every window token of every query: win_cap >= n_win plus the
  * spread of the query positions of one sequence.  max_visible bounds
  * floor((t+1)/m) over all queries.  hca_attn_prefill takes the same descriptor

@@ -813,19 +813,23 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
 // with w_s = 2^(m_s - M) l_s
 // Fixed split (split_runs > 0): query n's runs are slots n * split_runs + s, s <
 // its run count; the attention kernel has already finished queries with one run.
+// One wave per (query, head), four heads per workgroup: the runs' (max, sum) are
+// reduced with cross-lane operations (lane t holds runs t, t + 64, ...; its own runs
+// in order, then a fixed butterfly), the weights go through the wave's own LDS row,
+// and lane t merges dims 8t .. 8t + 7 of every run in run order.
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
-  __shared__ float s_w[kMaxRuns];
-  __shared__ float s_red[8];
-  const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_w[4][kMaxRuns];
+  const int n = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;                    // H is a multiple of 16
   PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
   const float sig = a.sink[h] * (float)kLog2e;
   __bf16* out = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD;
-  int S;                                   // runs to merge (one thread each)
+  int S;                                   // runs to merge
   size_t slot0;
   const int cnt = a.split_runs > 0 ? (query_info(a, n).n_set + KC - 1) / KC : pp.pref[n + 1] - pp.pref[n];
   if (cnt == 0) {                          // empty set (no window, nothing visible): the sink alone, o = 0
-    for (int d = tid; d < kD; d += 256) out[d] = (__bf16)0.0f;
-    if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
+    *reinterpret_cast<uint4*>(out + 8 * lane) = (uint4){0u, 0u, 0u, 0u};
+    if (a.lse && lane == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
     return;
   }
   if (a.split_runs > 0) {
@@ -840,31 +844,49 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     slot0 = ((size_t)w0 + n) * a.H + h;
   }
   const size_t sstride = (size_t)a.H;
-  float m = -INFINITY, l = 0.0f;
-  if (tid < S) { m = pp.m[slot0 + tid * sstride]; l = pp.l[slot0 + tid * sstride]; }
-  const float mx = wave_max(m);
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), sig);
-  const float w = tid < S ? exp2f(m - M) * l : 0.0f;
-  if (tid < S) s_w[tid] = w;
-  const float ws = wave_sum(w);            // fixed-order denominator
-  if (lane == 0) s_red[4 + wave] = ws;
-  __syncthreads();
-  const float den = exp2f(sig - M) + ((s_red[4] + s_red[5]) + (s_red[6] + s_red[7]));
-  const float inv = 1.0f / den;
-  // thread t: dims 2t, 2t + 1 of every run's row
-  const uint32_t* po = reinterpret_cast<const uint32_t*>(pp.o + slot0 * kD) + tid;
-  const size_t ostride = sstride * kD / 2;
-  float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const uint32_t v = po[s * ostride];
-    a0 += bf16_to_f32((uint16_t)v) * s_w[s];
-    a1 += bf16_to_f32((uint16_t)(v >> 16)) * s_w[s];
+  float mr[kMaxRuns / 64], lr[kMaxRuns / 64];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kMaxRuns / 64; ++r) {
+    const int sidx = lane + 64 * r;
+    mr[r] = -INFINITY;
+    lr[r] = 0.0f;
+    if (sidx < S) { mr[r] = pp.m[slot0 + sidx * sstride]; lr[r] = pp.l[slot0 + sidx * sstride]; }
+    mx = fmaxf(mx, mr[r]);
   }
-  reinterpret_cast<uint32_t*>(out)[tid] = pack_bf16x2(a0 * inv, a1 * inv);
-  if (a.lse && tid == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
+  const float M = fmaxf(wave_max(mx), sig);
+  float ws = 0.0f;                         // this lane's runs in order, then the butterfly
+#pragma unroll
+  for (int r = 0; r < kMaxRuns / 64; ++r) {
+    const int sidx = lane + 64 * r;
+    if (sidx < S) {
+      const float w = exp2f(mr[r] - M) * lr[r];
+      s_w[wave][sidx] = w;
+      ws += w;
+    }
+  }
+  const float den = exp2f(sig - M) + wave_sum(ws);
+  const float inv = 1.0f / den;
+  // the wave's own LDS writes above are complete before these reads (in-order LDS)
+  const __bf16* po = pp.o + slot0 * kD + 8 * lane;
+  const size_t ostride = sstride * kD;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sidx = 0; sidx < S; ++sidx) {
+    const uint4 v = *reinterpret_cast<const uint4*>(po + sidx * ostride);
+    const float w = s_w[wave][sidx];
+    const uint32_t* vw = &v.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_to_f32((uint16_t)vw[e]) * w;
+      acc[2 * e + 1] += bf16_to_f32((uint16_t)(vw[e] >> 16)) * w;
+    }
+  }
+  uint4 o4;
+  uint32_t* ow = &o4.x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ow[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<uint4*>(out + 8 * lane) = o4;
+  if (a.lse && lane == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
 }
 
 // Decode layout: few queries spread over one flattened chunk list (chunk counts
@@ -915,7 +937,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (flat) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplitFlat>, dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplit>, dim3(grid), dim3(kThreads), 0, s, a);
     if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
-    if (a.split_runs > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
+    if (a.split_runs > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H / 4), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   AttnArgs b = a;
@@ -925,7 +947,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (dec) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b);
   else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutQuery>, dim3(b.Nq), dim3(kThreads), 0, s, b);
   if (b.prof_end) (void)hipEventRecord(b.prof_end, s);
-  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(b.Nq, b.H), dim3(256), 0, s, b);
+  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(b.Nq, b.H / 4), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -228,7 +228,7 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   const int eb = elem_bytes(d->io_fmt);
   REQUIRE(d->win_pitch >= (int64_t)eb * d->D, HCA_E_SHAPE, "win_pitch too small");
   if (d->io_fmt == HCA_BF16) {
-    REQUIRE(aligned(d->q, 16) && aligned(d->o, 2) && aligned(d->win, 16) && d->win_pitch % 16 == 0 &&
+    REQUIRE(aligned(d->q, 16) && aligned(d->o, 16) && aligned(d->win, 16) && d->win_pitch % 16 == 0 &&
             (swa || (aligned(d->cache.nope, 16) && d->cache.nope_pitch % 16 == 0 && aligned(d->cache.rope, 16) &&
                      d->cache.rope_pitch % 16 == 0)), HCA_E_ALIGN, "BF16 attention needs 16-byte aligned rows");
   } else {

@@ -192,6 +192,7 @@ def test_attention_validation():
     assert call("hca_attn_decode", d) == -5
     d = attn_desc(q=FAKE + 4, workspace=FAKE, workspace_bytes=1 << 40)
     assert call("hca_attn_decode", d) == -3
+    assert call("hca_attn_decode", attn_desc(o=FAKE + 2, workspace=FAKE, workspace_bytes=1 << 40)) == -3
     assert call("hca_attn_decode", attn_desc(Nq=0)) == 0
     assert b"" != A.lib.hca_last_error()
 
