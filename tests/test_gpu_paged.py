@@ -68,3 +68,23 @@ def test_paged_step_bit_identical_to_contiguous(gpu, idx_fmt):
             outs.append((idx, to_np(dev.o).copy(), to_np(dev.lse).copy()))
         for a, b in zip(*outs):
             assert (a is None and b is None) or np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("idx_fmt", ["fp8", "mxfp4"])
+def test_paged_with_fixed_split_bit_identical(gpu, idx_fmt):
+    """Paging and the batch-invariant split together: the paged step with split_chunks
+    reproduces the contiguous step with the same split bit for bit."""
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    w = synth.ragged_pair(seed=21, B=5, lo=2048, hi=200000, round_every4=True, idx_fmt=idx_fmt)
+    for lay in w.layers:
+        _print(f"paged + split_chunks=2 vs contiguous + split_chunks=2, {idx_fmt}, layer={lay.mode}")
+        outs = []
+        for pr in (None, 32):
+            dev = DeviceLayer.from_host(lay, w.g, page_rows=pr)
+            dev.split_chunks = 2
+            dev.step()
+            torch.cuda.synchronize()
+            idx = to_np(dev.idx).copy() if dev.idx is not None else None
+            outs.append((idx, to_np(dev.o).copy(), to_np(dev.lse).copy()))
+        for a, b in zip(*outs):
+            assert (a is None and b is None) or np.array_equal(a, b)
