@@ -142,3 +142,40 @@ def test_prologue_one_part_only(gpu):
     wk, fk = opro.encode(opro.rms_norm(quant.bf16_decode(tok), gk, 1e-6), "bf16")
     ring_w = opro.append_ring(ring, np.array([1, 0]), np.array([6, 3]), wk)
     assert not fk.any() and np.array_equal(to_np(dring), ring_w)
+
+
+@pytest.mark.parametrize("fmt,D", [("bf16", 1024), ("bf16", 2048), ("bf16", 4096), ("f32", 512), ("f32", 1024),
+                                   ("f32", 2048)])
+def test_prologue_wide_rows(gpu, fmt, D):
+    """Rows of 2, 4 and 8 sixteen-byte vectors per lane (the wider kernel variants)."""
+    from long_context_attention_softmax_amd.ops import hca_qkv_prologue
+    from oracle import quant
+    rng = np.random.default_rng(74 + D)
+    Nq, H, Nt, B, W = 3, 5, 4, 2, 8
+    q = rng.normal(size=(Nq, H, D)) * rng.uniform(0.1, 10.0, size=(Nq, H, 1))
+    kv = rng.normal(size=(Nt, D)) * 3.0
+    gq, gk = rng.uniform(0.5, 1.5, D).astype(np.float32), rng.uniform(0.5, 1.5, D).astype(np.float32)
+    seq, pos = np.array([0, 1, 0, 1], np.int32), np.array([2, 9, 3, 5], np.int64)
+    if fmt == "bf16":
+        qs, kvs = _bf16(q), _bf16(kv)
+        qv, kvv = quant.bf16_decode(qs), quant.bf16_decode(kvs)
+        ring0 = np.zeros((B, W, D), np.uint16)
+        t = lambda a: _dev_bits(a, gpu)                            # noqa: E731
+        raw = lambda a: a                                          # noqa: E731
+    else:
+        qs, kvs = q.astype(np.float32), kv.astype(np.float32)
+        qv, kvv = qs.astype(np.float64), kvs.astype(np.float64)
+        ring0 = np.zeros((B, W, D), np.float32)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)   # noqa: E731
+        raw = lambda a: a.view(np.uint32)                          # noqa: E731
+    wq, fq = opro.encode(opro.rms_norm(qv, gq, 1e-6), fmt)
+    wk, fk = opro.encode(opro.rms_norm(kvv, gk, 1e-6), fmt)
+    dq, dring = t(qs), t(ring0)
+    _print(f"prologue {fmt} D={D}")
+    hca_qkv_prologue(dq, torch.from_numpy(gq).to(gpu), t(kvs), torch.from_numpy(gk).to(gpu),
+                     torch.from_numpy(seq).to(gpu), torch.from_numpy(pos).to(gpu), dring)
+    torch.cuda.synchronize()
+    got = raw(to_np(dq))
+    assert np.array_equal(got[~fq], wq[~fq])
+    ring_w = opro.append_ring(raw(ring0), seq, pos, wk)
+    assert not fk.any() and np.array_equal(raw(to_np(dring)), ring_w)
