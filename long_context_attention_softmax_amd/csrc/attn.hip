@@ -152,7 +152,8 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
 // same in both waves), so both hold identical probabilities and each accumulates
 // P.V for its own 256 output dims.  The compressed entries of chunk c+1 are loaded
 // into registers while chunk c is computed, then widened to BF16 into the LDS
-// tile; window tokens (at most two chunks per query) are staged directly.
+// tile; window tokens (the set positions after the entries, any n_win) are staged
+// directly from the ring.
 //
 // Decode (few queries): the chunks of all queries form one list that is cut into
 // equal runs, one per workgroup, so ragged lengths balance.  A query whose chunks
