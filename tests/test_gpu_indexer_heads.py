@@ -19,7 +19,7 @@ def _print(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("idx_fmt,page_rows", [("fp8", None), ("mxfp4", None), ("mxfp4", 64)])
+@pytest.mark.parametrize("idx_fmt,page_rows", [("fp8", None), ("fp8", 32), ("mxfp4", None), ("mxfp4", 64)])
 def test_decode_32_indexer_heads(gpu, idx_fmt, page_rows):
     from synth.gen import _decode_layer
     lens = np.array([8192, 4099, 30001, 1023, 5000], np.int64)
@@ -28,7 +28,8 @@ def test_decode_32_indexer_heads(gpu, idx_fmt, page_rows):
     run_and_compare(lay, G32, page_rows=page_rows)
 
 
-def test_prefill_32_indexer_heads(gpu):
+@pytest.mark.parametrize("page_rows", [None, 128])
+def test_prefill_32_indexer_heads(gpu, page_rows):
     w = synth.csa_prefill(seed=111, prefix=8192, T=256, g=G32)
-    _print("H_I=32 prefill, 256 queries")
-    run_and_compare(w.layers[0], G32, prefill=True)
+    _print(f"H_I=32 prefill, 256 queries, page_rows={page_rows}")
+    run_and_compare(w.layers[0], G32, prefill=True, page_rows=page_rows)
