@@ -28,6 +28,21 @@ def test_every_declared_function_is_exported():
         assert hasattr(A.lib, n), n
 
 
+def test_constants_match_the_header():
+    # every HCA_* integer constant of include/hca.h has the same value in the binding
+    defs = dict((m.group(1), int(m.group(2))) for m in
+                re.finditer(r"^#define HCA_(\w+)\s+(-?\d+)", open(HEADER).read(), re.M))
+    assert defs.pop("ABI_VERSION") == A.lib.hca_abi_version()
+    errors = {v: k for k, v in A.ERRORS.items()}
+    for name, value in defs.items():
+        if name.startswith("E_"):
+            assert errors["HCA_" + name] == value, name
+        elif name == "OK":
+            assert A.HCA_OK == value
+        else:
+            assert getattr(A, name) == value, name
+
+
 def test_version_and_struct_sizes():
     assert A.lib.hca_abi_version() == 5
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
