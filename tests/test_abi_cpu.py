@@ -336,3 +336,34 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         ops.hca_kv_compress(x, i, i, i, torch.zeros(512), torch.zeros(4), ops.KVCache(f32=torch.zeros(4, 512)),
                             m=4, D_r=64)
+
+
+def test_struct_field_offsets_match_the_header(tmp_path):
+    # the C compiler's offsetof for every field the ctypes mirror declares
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"hca_kv_compress_desc": A.KvCompressDesc, "hca_indexer_topk_desc": A.IndexerTopkDesc,
+               "hca_attn_desc": A.AttnDesc, "hca_kv_planes": A.KvPlanes, "hca_idx_planes": A.IdxPlanes,
+               "hca_qkv_prologue_desc": A.QkvPrologueDesc, "hca_out_proj_desc": A.OutProjDesc}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hca.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        for f in cls._fields_:
+            lines.append(f'  printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "offsets.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "offsets"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    n = 0
+    for line in filter(None, out):
+        cname, field, off = line.split()
+        cls = structs[cname]
+        want = ctypes.sizeof(cls) if field == "sizeof" else getattr(cls, field).offset
+        assert int(off) == want, f"{cname}.{field}: C {off}, ctypes {want}"
+        n += 1
+    assert n == sum(len(c._fields_) + 1 for c in structs.values())
