@@ -336,6 +336,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         ops.hca_kv_compress(x, i, i, i, torch.zeros(512), torch.zeros(4), ops.KVCache(f32=torch.zeros(4, 512)),
                             m=4, D_r=64)
+    q = torch.zeros(2, 4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.hca_qkv_prologue(q, torch.ones(512), None, None, None, None, None)
+    with pytest.raises(ValueError):
+        ops.hca_out_proj(q, torch.zeros(2, 32, 1024, dtype=torch.bfloat16), G=2)
+    with pytest.raises(ValueError):
+        ops.hca_attn_decode(q, None, None, torch.zeros(2, 8, 512, dtype=torch.bfloat16), torch.zeros(4),
+                            torch.zeros(2, dtype=torch.int32), i, mode=2, m=1, n_win=8, D_r=64, max_visible=0)
 
 
 def test_struct_field_offsets_match_the_header(tmp_path):
