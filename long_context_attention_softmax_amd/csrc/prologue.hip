@@ -16,7 +16,10 @@ namespace hca {
 namespace {
 
 constexpr int kWaves = 4;         // waves per workgroup
-constexpr int kQRows = 4;         // query rows per wave (their loads issued together)
+#ifndef HCA_PRO_QROWS
+#define HCA_PRO_QROWS 4
+#endif
+constexpr int kQRows = HCA_PRO_QROWS;   // query rows per wave (their loads issued together)
 constexpr int kMaxVec = 8;        // 16-byte vectors per lane: D <= 64 * 8 * (8 BF16 | 4 F32)
 
 template <bool F32>
