@@ -488,6 +488,16 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
         c1 = min(s_pref[n1] + (r1 - s_rpref[n1]) * a.split_chunks, s_pref[n1 + 1]);
       }
       pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
+      // a query with no run (empty set: nothing visible, no window) gets the sink
+      // alone, o = 0, from workgroup 0 (no run and no combine writes it)
+      if (blockIdx.x == 0) {
+        for (int nq = 0; nq < a.Nq; ++nq) {
+          if (s_rpref[nq + 1] != s_rpref[nq]) continue;       // uniform
+          __bf16* o = reinterpret_cast<__bf16*>(a.o) + (int64_t)nq * a.H * kD;
+          for (int i = tid; i < a.H * kD; i += kThreads) o[i] = (__bf16)0.0f;
+          if (a.lse && tid < a.H) a.lse[(int64_t)nq * a.H + tid] = a.sink[tid];
+        }
+      }
     } else {
       int per = (total + gridDim.x - 1) / gridDim.x;
       if (per < HCA_ATTN_MIN_CHUNKS) per = HCA_ATTN_MIN_CHUNKS;
@@ -829,6 +839,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   size_t slot0;
   const int cnt = a.split_runs > 0 ? (query_info(a, n).n_set + KC - 1) / KC : pp.pref[n + 1] - pp.pref[n];
   if (cnt == 0) {                          // empty set (no window, nothing visible): the sink alone, o = 0
+    if (a.split_runs > 0) return;          // written by the attention kernel
     *reinterpret_cast<uint4*>(out + 8 * lane) = (uint4){0u, 0u, 0u, 0u};
     if (a.lse && lane == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
     return;

@@ -72,3 +72,28 @@ def test_window_only_empty_set(gpu, split):
     _print(f"window-only with n_win=0, split_chunks={split}")
     ref, _, err = run_and_compare(lay, g, dev=dev)
     assert np.all(ref["o"] == 0) and err == 0.0
+
+
+@pytest.mark.parametrize("split", [0, 1, 2])
+def test_hca_empty_and_nonempty_sets_mixed(gpu, split):
+    """An HCA layer with no window (n_win = 0) whose queries at t < m - 1 see no entry
+    (empty set: o = 0, lse = the sink) next to queries that see a few entries.  With
+    split_chunks 1 or 2 every non-empty set is one run (split_runs = 1, so no combine
+    is launched): the empty sets must still be written."""
+    from long_context_attention_softmax_amd.layer import DeviceLayer
+    from synth.gen import _decode_layer
+    g = replace(synth.FULL_GEOMETRY, n_win=0)
+    lens = np.array([100, 1000, 127, 5000, 1, 3000], np.int64)       # V = 0, 7, 0, 39, 0, 23
+    lay = _decode_layer(np.random.default_rng(66), g, "hca", lens, 128, 1.0)
+    dev = DeviceLayer.from_host(lay, g)
+    dev.split_chunks = split
+    _print(f"HCA n_win=0, mixed empty sets, split_chunks={split} (one 64-entry chunk per set at most)")
+    dev.o.fill_(1.0)                        # stale contents must be overwritten
+    dev.lse.fill_(-7.0)
+    ref, _, err = run_and_compare(lay, g, dev=dev)
+    empty = (lens - 1 + 1) // g.m_hca == 0
+    assert np.all(ref["o"][empty] == 0)
+    got_o = dev.o.float().cpu().numpy()
+    assert np.all(got_o[empty] == 0)
+    got_lse = dev.lse.cpu().numpy()
+    assert np.array_equal(got_lse[empty], np.broadcast_to(lay.sink.astype(np.float32), got_lse[empty].shape))
