@@ -132,17 +132,23 @@ class Timed:
         for a, b in evs.values():  # create the handles before passing them to the library
             a.record()
             b.record()
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # step-time distribution: an event between consecutive blocks of `block` steps
+        block = max(1, steps // 20)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range((steps + block - 1) // block + 1)]
         torch.cuda.synchronize()
-        start.record()
+        marks[0].record()
         for i in range(steps):
             for li, lay in enumerate(self.sets[i % R]):
                 p = evs.get(i) if li == prof_layer else None
                 lay.step(prefill=self.prefill, prof_select=p if prof_kind == "select" else None,
                          prof_attend=p if prof_kind == "attend" else None)
-        stop.record()
+            if (i + 1) % block == 0 or i + 1 == steps:
+                marks[(i + block) // block].record()
         torch.cuda.synchronize()
-        total_ms = start.elapsed_time(stop)
+        total_ms = marks[0].elapsed_time(marks[-1])
+        per = [marks[j].elapsed_time(marks[j + 1]) / min(block, steps - j * block) for j in range(len(marks) - 1)]
+        self.dist = {"median": round(float(np.median(per)), 4), "p10": round(float(np.percentile(per, 10)), 4),
+                     "p90": round(float(np.percentile(per, 90)), 4), "block_steps": block, "blocks": len(per)}
         kern_ms = np.array([a.elapsed_time(b) for a, b in evs.values()])
         return total_ms / steps, kern_ms
 
@@ -244,11 +250,13 @@ def main():
         log(f"[bench] ragged pair: generated in {time.time() - t0:.1f}s, {cb / 1e6:.1f} + {hb / 1e6:.1f} MB/step")
         sets = replicate(device_layers(w5), cb + hb)
         log(f"[bench] ragged pair: {len(sets)} replicas resident")
-        ms, kern = Timed("ragged", sets).run(args.steps, args.warmup, prof_layer=0, prof_kind="select")
+        tm = Timed("ragged", sets)
+        ms, kern = tm.run(args.steps, args.warmup, prof_layer=0, prof_kind="select")
         kern_avg = float(kern.mean())
         step_bytes = cb + hb
         out.update(dict(
             value=round(w5.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+            step_ms=tm.dist,
             hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1), bytes_per_step=step_bytes,
             config={"workload": "ragged_pair_32", "batch": w5.B, "context_lengths": L,
                     "layers": "CSA (m=4, FP8 indexer 64x128, top-512) + HCA (m=128)",
@@ -269,13 +277,15 @@ def main():
             L2 = [int(x) for x in w2.lengths]
             cb2, ck2 = csa_bytes(L2)
             sets = replicate(device_layers(w2), cb2)
-            ms2, k2 = Timed("csa", sets).run(args.steps, args.warmup, prof_kind="select")
+            tm_csa = Timed("csa", sets)
+            ms2, k2 = tm_csa.run(args.steps, args.warmup, prof_kind="select")
             secondary["csa_decode_128k"] = dict(
                 tokens_per_s=round(w2.B / (ms2 * 1e-3), 1), ms_per_step=round(ms2, 4),
                 hbm_gbps=round(cb2 / (ms2 * 1e-3) / 1e9, 1),
                 hbm_frac=round(cb2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), bytes_per_step=cb2,
                 scoring_kernel_ms=round(float(k2.mean()), 5),
-                scoring_kernel_gbps=round(ck2 / (float(k2.mean()) * 1e-3) / 1e9, 1), replicas=len(sets))
+                scoring_kernel_gbps=round(ck2 / (float(k2.mean()) * 1e-3) / 1e9, 1), replicas=len(sets),
+                step_ms=tm_csa.dist)
             log(f"[bench] csa 128k: {ms2:.4f} ms/step")
             del sets
             torch.cuda.empty_cache()
@@ -406,12 +416,13 @@ def main():
             L3 = [int(x) for x in w3.lengths]
             hb3, _ = hca_bytes(L3)
             sets = replicate(device_layers(w3), hb3)
-            ms3, k3 = Timed("hca", sets).run(args.steps, args.warmup, prof_kind="attend")
+            tm_hca = Timed("hca", sets)
+            ms3, k3 = tm_hca.run(args.steps, args.warmup, prof_kind="attend")
             secondary["hca_decode_1m"] = dict(
                 tokens_per_s=round(w3.B / (ms3 * 1e-3), 1), ms_per_step=round(ms3, 4),
                 hbm_gbps=round(hb3 / (ms3 * 1e-3) / 1e9, 1),
                 hbm_frac=round(hb3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), bytes_per_step=hb3,
-                attention_kernel_ms=round(float(k3.mean()), 5), replicas=len(sets))
+                attention_kernel_ms=round(float(k3.mean()), 5), replicas=len(sets), step_ms=tm_hca.dist)
             log(f"[bench] hca 1m: {ms3:.4f} ms/step")
             del sets
             torch.cuda.empty_cache()

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 5
+#define HCA_ABI_VERSION 6
 
 /* status codes */
 #define HCA_OK             0
@@ -203,10 +203,6 @@ typedef struct hca_indexer_topk_desc {
   void*          score;             /* [Nq, k] or NULL */
   void*          workspace;
   size_t         workspace_bytes;
-  /* optional hipEvent_t pair (as void*) recorded on the stream immediately before
-     and after the scoring kernel, for timing it in isolation; NULL = none */
-  void*          prof_begin;
-  void*          prof_end;
   /* Paged compressed cache (optional; NULL = contiguous rows from cache_row_start,
      which is then required).  "DeepSeek V4 infrastructure" (volanea.com), "Compression
      only works if the attention path is engineered end to end", asks for a cache
@@ -246,7 +242,8 @@ typedef struct hca_indexer_topk_desc {
  *   o = sum_a e^(l_a - M) kappa_a / (e^(sigma_h - M) + sum_a e^(l_a - M))
  *   lse = M + log(e^(sigma_h - M) + sum_a e^(l_a - M))        (optional output)
  * io_fmt HCA_F32 needs cache fmt HCA_F32 (fp64 arithmetic, any D <= 1024, at most
- * 8192 keys per query); io_fmt HCA_BF16 needs cache fmt HCA_FP8_E4M3, D = 512,
+ * 4096 keys per query: k (CSA) or max_visible (HCA), plus n_win; HCA_E_UNSUPPORTED
+ * beyond); io_fmt HCA_BF16 needs cache fmt HCA_FP8_E4M3, D = 512,
  * D_r = 64, H a multiple of 16 up to 64 (BF16 MFMA, fp32 softmax), with q, o, the
  * ring and the cache rows 16-byte aligned (HCA_E_ALIGN otherwise).
  * The ring must hold every window token of every query: win_cap >= n_win plus the
@@ -273,10 +270,6 @@ typedef struct hca_attn_desc {
   float*         lse;               /* [Nq, H] or NULL */
   void*          workspace;
   size_t         workspace_bytes;
-  /* optional hipEvent_t pair recorded immediately before and after the attention
-     kernel (the split combine excluded); NULL = none */
-  void*          prof_begin;
-  void*          prof_end;
   /* Paged compressed cache (optional; NULL = contiguous rows from cache_row_start,
      which is then required).  "DeepSeek V4 infrastructure" (volanea.com), "Compression
      only works if the attention path is engineered end to end", asks for a cache
@@ -378,11 +371,30 @@ typedef struct hca_out_proj_desc {
   void*       y;  int64_t y_pitch;
 } hca_out_proj_desc;
 
+/*
+ * Timing hook for benchmarks (not part of the computation): hca_profiled runs the
+ * call (op, desc) exactly as its own entry point does and records the event `begin`
+ * on the stream immediately before, and `end` immediately after, that call's main
+ * kernel: the scoring kernel of HCA_OP_INDEXER_TOPK (top-k selection excluded), the
+ * attention kernel of HCA_OP_ATTN_DECODE / HCA_OP_ATTN_PREFILL (the combine of split
+ * decode queries excluded).  begin and end are hipEvent_t values passed as void*
+ * (either may be NULL).  Other ops: HCA_E_UNSUPPORTED.
+ */
+typedef struct hca_profile_events {
+  uint32_t struct_size;
+  int32_t  reserved;
+  void*    begin;
+  void*    end;
+} hca_profile_events;
+#define HCA_STRUCT_PROFILE_EVENTS 102
+
 int         hca_abi_version(void);
 const char* hca_last_error(void);
 /* sizeof the descriptor of an HCA_OP_* id, or of an HCA_STRUCT_* plane struct; 0 if unknown */
 size_t      hca_struct_size(int which);
-/* workspace bytes the call described by (op, desc) needs; validates desc like the call */
+/* workspace bytes the call described by (op, desc) needs.  For the indexer and
+   attention only the shapes that decide the size are checked (the buffers may not
+   exist yet); the other operations are validated like the call. */
 int         hca_workspace_bytes(int op, const void* desc, size_t* bytes);
 
 int hca_kv_compress(const hca_kv_compress_desc* desc, void* stream);
@@ -391,6 +403,7 @@ int hca_attn_decode(const hca_attn_desc* desc, void* stream);
 int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
 int hca_qkv_prologue(const hca_qkv_prologue_desc* desc, void* stream);
 int hca_out_proj(const hca_out_proj_desc* desc, void* stream);
+int hca_profiled(int op, const void* desc, const hca_profile_events* events, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,11 +19,11 @@ ERRORS = {-1: "HCA_E_NULL", -2: "HCA_E_SHAPE", -3: "HCA_E_ALIGN", -4: "HCA_E_DTY
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
 OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE, OP_OUT_PROJ = 0, 1, 2, 3, 4, 5
-STRUCT_KV_PLANES, STRUCT_IDX_PLANES = 100, 101
+STRUCT_KV_PLANES, STRUCT_IDX_PLANES, STRUCT_PROFILE_EVENTS = 100, 101, 102
 
 EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes",
            "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_qkv_prologue",
-           "hca_out_proj"]
+           "hca_out_proj", "hca_profiled"]
 
 
 class KvPlanes(ctypes.Structure):
@@ -58,7 +58,6 @@ class IndexerTopkDesc(ctypes.Structure):
                 ("cache_row_start", c_void_p), ("seq_id", c_void_p), ("q_pos", c_void_p),
                 ("idx", c_void_p), ("score", c_void_p),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-                ("prof_begin", c_void_p), ("prof_end", c_void_p),
                 ("page_table", c_void_p), ("page_table_pitch", c_int64), ("page_rows", c_int32),
                 ("reserved_page", c_int32)]
 
@@ -72,7 +71,6 @@ class AttnDesc(ctypes.Structure):
                 ("idx", c_void_p), ("win", c_void_p), ("win_pitch", c_int64), ("sink", c_void_p),
                 ("seq_id", c_void_p), ("q_pos", c_void_p), ("o", c_void_p), ("lse", c_void_p),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-                ("prof_begin", c_void_p), ("prof_end", c_void_p),
                 ("page_table", c_void_p), ("page_table_pitch", c_int64), ("page_rows", c_int32),
                 ("split_chunks", c_int32)]
 
@@ -91,6 +89,10 @@ class OutProjDesc(ctypes.Structure):
     _fields_ = [("struct_size", c_uint32), ("out_fmt", c_int32), ("Nq", c_int32), ("H", c_int32),
                 ("D", c_int32), ("G", c_int32), ("d_g", c_int32), ("o", c_void_p), ("o_pitch", c_int64),
                 ("w", c_void_p), ("w_pitch", c_int64), ("y", c_void_p), ("y_pitch", c_int64)]
+
+
+class ProfileEvents(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("reserved", c_int32), ("begin", c_void_p), ("end", c_void_p)]
 
 
 class HcaError(RuntimeError):
@@ -120,6 +122,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [ctypes.POINTER(dt), c_void_p]
+    lib.hca_profiled.restype = c_int
+    lib.hca_profiled.argtypes = [c_int, c_void_p, ctypes.POINTER(ProfileEvents), c_void_p]
     return lib
 
 

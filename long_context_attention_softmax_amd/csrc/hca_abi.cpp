@@ -316,7 +316,7 @@ int validate_prologue(const hca_qkv_prologue_desc* d) {
   return HCA_OK;
 }
 
-int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
+int attn_call(const hca_attn_desc* d, void* stream, int prefill, const hca_profile_events* ev = nullptr) {
   size_t ws = 0;
   int rc = validate_attn(d, prefill, &ws);
   if (rc) return rc;
@@ -342,7 +342,7 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill) {
   a.workspace = d->workspace; a.prefill = prefill;
   a.split_chunks = prefill || a.io_f32 ? 0 : d->split_chunks;
   a.split_runs = (int)hca::attention_split_runs(a.mode, a.k, a.n_win, a.max_visible, a.split_chunks);
-  a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
+  if (ev) { a.prof_begin = static_cast<hipEvent_t>(ev->begin); a.prof_end = static_cast<hipEvent_t>(ev->end); }
   return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -364,6 +364,7 @@ size_t hca_struct_size(int which) {
     case HCA_OP_OUT_PROJ: return sizeof(hca_out_proj_desc);
     case HCA_STRUCT_KV_PLANES: return sizeof(hca_kv_planes);
     case HCA_STRUCT_IDX_PLANES: return sizeof(hca_idx_planes);
+    case HCA_STRUCT_PROFILE_EVENTS: return sizeof(hca_profile_events);
     default: return 0;
   }
 }
@@ -438,7 +439,8 @@ int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
   return launched(hca::launch_pool(a, static_cast<hipStream_t>(stream)));
 }
 
-int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
+namespace {
+int indexer_call(const hca_indexer_topk_desc* d, void* stream, const hca_profile_events* ev) {
   size_t ws = 0;
   int rc = validate_indexer(d, &ws);
   if (rc) return rc;
@@ -458,8 +460,23 @@ int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) {
   a.idx = d->idx; a.score_out = d->score;
   a.scores = d->workspace;             // the workspace layout is laid out by the launcher
   a.hist = nullptr;
-  a.prof_begin = static_cast<hipEvent_t>(d->prof_begin); a.prof_end = static_cast<hipEvent_t>(d->prof_end);
+  if (ev) { a.prof_begin = static_cast<hipEvent_t>(ev->begin); a.prof_end = static_cast<hipEvent_t>(ev->end); }
   return launched(hca::launch_indexer_topk(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int hca_indexer_topk(const hca_indexer_topk_desc* d, void* stream) { return indexer_call(d, stream, nullptr); }
+
+int hca_profiled(int op, const void* desc, const hca_profile_events* ev, void* stream) {
+  REQUIRE(ev, HCA_E_NULL, "events is NULL");
+  REQUIRE(ev->struct_size == sizeof(hca_profile_events), HCA_E_VERSION, "events struct_size %u != %zu",
+          ev->struct_size, sizeof(hca_profile_events));
+  switch (op) {
+    case HCA_OP_INDEXER_TOPK: return indexer_call(static_cast<const hca_indexer_topk_desc*>(desc), stream, ev);
+    case HCA_OP_ATTN_DECODE: return attn_call(static_cast<const hca_attn_desc*>(desc), stream, 0, ev);
+    case HCA_OP_ATTN_PREFILL: return attn_call(static_cast<const hca_attn_desc*>(desc), stream, 1, ev);
+    default: return fail(HCA_E_UNSUPPORTED, "op %d has no profiled form", op);
+  }
 }
 
 int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }

@@ -3,8 +3,8 @@
 Each function checks dtypes, devices and layouts of PyTorch tensors, fills the
 descriptor with raw device pointers and row pitches, and calls the library on the
 current HIP stream.  Outputs are written into caller tensors (or allocated here);
-workspaces are allocated once per (device, op) and reused (the library needs no
-particular contents in them).  There is no fallback: every result comes from the
+workspaces are allocated once per (op, device, stream) and reused (the library needs
+no particular contents in them).  There is no fallback: every result comes from the
 HIP kernels.
 """
 from __future__ import annotations
@@ -63,9 +63,13 @@ def _i64(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
 
 
 def _workspace(op: int, nbytes: int, device) -> Optional[torch.Tensor]:
+    """The scratch buffer of ``op`` for the current stream of ``device``.  Calls that
+    share a workspace must be ordered on one stream, so each (op, device, stream)
+    gets its own buffer: calls on different streams never share scratch."""
     if nbytes == 0:
         return None
-    key = (op, device.index if device.index is not None else torch.cuda.current_device())
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (op, dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
@@ -76,6 +80,13 @@ def _workspace(op: int, nbytes: int, device) -> Optional[torch.Tensor]:
 
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
+
+
+def _events(prof) -> "ctypes._Pointer":
+    """The timing hook's event pair: prof = (begin, end) torch.cuda.Event objects."""
+    ev = A.new_desc(A.ProfileEvents)
+    ev.begin, ev.end = prof[0].cuda_event, prof[1].cuda_event
+    return ctypes.byref(ev)
 
 
 @dataclass
@@ -202,8 +213,9 @@ def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_sta
     ws = _workspace(A.OP_INDEXER_TOPK, nb, w.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
     if prof is not None:
-        d.prof_begin, d.prof_end = prof[0].cuda_event, prof[1].cuda_event
-    A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
+        A.check(A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), _events(prof), _stream()))
+    else:
+        A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
     return idx
 
 
@@ -250,9 +262,10 @@ def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_st
     ws = _workspace(op, nb, q.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
     if prof is not None:
-        d.prof_begin, d.prof_end = prof[0].cuda_event, prof[1].cuda_event
-    fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
-    A.check(fn(ctypes.byref(d), _stream()))
+        A.check(A.lib.hca_profiled(op, ctypes.byref(d), _events(prof), _stream()))
+    else:
+        fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
+        A.check(fn(ctypes.byref(d), _stream()))
     return o
 
 

@@ -44,11 +44,12 @@ def test_constants_match_the_header():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 5
+    assert A.lib.hca_abi_version() == 6
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
                     (A.OP_QKV_PROLOGUE, A.QkvPrologueDesc), (A.OP_OUT_PROJ, A.OutProjDesc),
-                    (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes)]:
+                    (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes),
+                    (A.STRUCT_PROFILE_EVENTS, A.ProfileEvents)]:
         assert A.lib.hca_struct_size(op) == ctypes.sizeof(cls), cls
     assert A.lib.hca_struct_size(12345) == 0
 
@@ -375,3 +376,38 @@ def test_struct_field_offsets_match_the_header(tmp_path):
         assert int(off) == want, f"{cname}.{field}: C {off}, ctypes {want}"
         n += 1
     assert n == sum(len(c._fields_) + 1 for c in structs.values())
+
+
+@pytest.mark.parametrize("mode,k,max_visible,n_win", [(1, 0, 4000, 96), (0, 3968, 100000, 128), (2, 0, 0, 4096)])
+def test_f32_attention_key_limit_boundary(mode, k, max_visible, n_win):
+    """The f32 attention path takes at most 4096 keys per query (k for CSA or
+    max_visible for HCA, plus the window): 4096 passes validation, 4097 is
+    HCA_E_UNSUPPORTED.  With Nq = 0 a call that passes validation returns HCA_OK
+    without launching anything."""
+    for extra, want in [(0, 0), (1, -5)]:
+        d = attn_desc(mode=mode, k=k, max_visible=max_visible, n_win=n_win + extra, win_cap=n_win + extra,
+                      io_fmt=A.F32, D=128, D_r=32, H=8, win_pitch=512, Nq=0)
+        d.cache.fmt = A.F32
+        d.cache.f32, d.cache.f32_pitch = FAKE, 512
+        assert call("hca_attn_decode", d) == want, extra
+        if want:
+            assert b"4096" in A.lib.hca_last_error()
+
+
+def test_profiled_hook_validation():
+    """The timing hook takes an event pair and runs only the indexer and attention
+    calls; its validation happens before anything is launched."""
+    ev = A.new_desc(A.ProfileEvents)
+    d = idx_desc(Nq=0)
+    assert A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), None, None) == -1
+    bad = A.new_desc(A.ProfileEvents)
+    bad.struct_size = 4
+    assert A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), ctypes.byref(bad), None) == -8
+    assert A.lib.hca_profiled(A.OP_OUT_PROJ, ctypes.byref(d), ctypes.byref(ev), None) == -5
+    # the profiled call validates like the plain one (here: Nq = 0, nothing to do)
+    assert A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), ctypes.byref(ev), None) == 0
+    a = attn_desc(Nq=0)
+    assert A.lib.hca_profiled(A.OP_ATTN_DECODE, ctypes.byref(a), ctypes.byref(ev), None) == 0
+    a = attn_desc(H=20)
+    assert A.lib.hca_profiled(A.OP_ATTN_DECODE, ctypes.byref(a), ctypes.byref(ev), None) == \
+        call("hca_attn_decode", a)
