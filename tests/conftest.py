@@ -23,3 +23,12 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Report the largest parity errors the GPU tests measured (output per-row
+    relative error and lse absolute error, per path)."""
+    mod = sys.modules.get("gpu_helpers")
+    if mod is not None and any(v[0] or v[1] for v in mod.MAX_ERR.values()):
+        for path, (o, l) in mod.MAX_ERR.items():
+            print(f"\nlargest parity errors ({path}): output {o:.3e}, lse {l:.3e}", flush=True)

@@ -9,6 +9,7 @@ from oracle import step as ostep
 
 TOL_QUANT = 2e-2     # per-row relative error, BF16/FP8 paths
 TOL_F32 = 1e-5       # per-row relative error, f32 path
+TOL_LSE = 2e-2       # absolute lse error, BF16/FP8 paths
 
 
 def row_rel_err(o: np.ndarray, ref: np.ndarray) -> float:
@@ -78,8 +79,31 @@ def check_pool(dev, pooled, lay):
             assert_codes_equal(hi_g, hi_w, fr[:, 1::2], "pooled MXFP4 key (odd)")
 
 
+def oracle_layer(lay, g, queries=None, threads=1):
+    """The oracle's step of one layer; with ``threads`` > 1 the queries are split
+    over a thread pool (the layer is pooled once; numpy releases the GIL inside its
+    large array operations) and the per-query results are joined in query order."""
+    if threads <= 1 or queries is None or len(queries) < 2:
+        return ostep.run_layer(lay, g, queries=queries)
+    from concurrent.futures import ThreadPoolExecutor
+    pooled = None if lay.mode == "swa" else ostep.pool_layer(lay, g)
+    qs = [int(q) for q in queries]
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda q: ostep.run_layer(lay, g, queries=[q], pooled=pooled), qs))
+    ref = dict(parts[0])
+    for key in ("idx", "sel_scores", "o", "lse", "queries"):
+        if ref[key] is not None:
+            ref[key] = np.concatenate([p[key] for p in parts])
+    ref["kth_gaps"] = [x for p in parts for x in p["kth_gaps"]]
+    return ref
+
+
+# the largest errors seen by run_and_compare in this process: (output, lse) per path
+MAX_ERR = {"quant": [0.0, 0.0], "f32": [0.0, 0.0]}
+
+
 def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, check_scores=True,
-                    page_rows=None):
+                    page_rows=None, oracle_threads=1):
     """Run the layer's step on the GPU and compare every stage with the oracle.
     ``page_rows`` lays the compressed cache out in shuffled pages of that size.
 
@@ -95,7 +119,7 @@ def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, che
         dev.select(score=score)
     o = dev.attend(prefill=prefill)
     torch.cuda.synchronize()
-    ref = ostep.run_layer(lay, g, queries=queries)
+    ref = oracle_layer(lay, g, queries=queries, threads=oracle_threads)
     qs = ref["queries"]
     check_pool(dev, ref["pooled"], lay)
     if dev.mode == 0:
@@ -118,10 +142,15 @@ def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, che
     err = row_rel_err(got_o, ref["o"])
     assert err <= tol, f"output rel err {err:.3e} > {tol}"
     lse = to_np(dev.lse)[qs]
-    # lse: float32 storage on the f32 path; on the BF16 path a relative error r of the
-    # softmax normalizer is an absolute error ~r of its log, so the output bar applies
+    lse_err = float(np.abs(lse - ref["lse"]).max()) if lse.size else 0.0
+    path = "f32" if dev.f32 else "quant"
+    MAX_ERR[path] = [max(MAX_ERR[path][0], err), max(MAX_ERR[path][1], lse_err)]
+    print(f"  parity ({path}): output rel err {err:.3e}, lse abs err {lse_err:.3e}", flush=True)
+    # lse: float32 storage on the f32 path; on the BF16 path the logits are exact
+    # products of BF16 operands summed in binary32 and the normalizer a binary32 sum
+    # of BF16-rounded probabilities, so lse carries ~1e-4 absolute error (TOL_LSE)
     if dev.f32:
         assert np.allclose(lse, ref["lse"], rtol=1e-6, atol=1e-6)
     else:
-        assert np.abs(lse - ref["lse"]).max() <= TOL_QUANT, np.abs(lse - ref["lse"]).max()
+        assert lse_err <= TOL_LSE, f"lse abs err {lse_err:.3e} > {TOL_LSE}"
     return ref, dev, err

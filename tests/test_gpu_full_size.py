@@ -3,9 +3,10 @@ launches that bench.py times (DeviceLayer pool -> select -> attend, one call eac
 
 Decode workloads are checked on every query (a decode step has one per sequence, so
 the oracle still finishes in seconds); the 4096-token prefill chunk is checked on a
-seeded sample of queries that covers the first and last positions, both ends of
-each 8-query group the MXFP4 scoring grid interleaves over the XCDs, and queries in
-different key chunks.  Bars are those of the small parity tests: pooled codes and
+seeded sample of 128 queries that covers both ends of every 512-query block, both
+ends of the first and last 8-query groups of each block (the MXFP4 scoring grid
+interleaves 8-query groups over the XCDs), the first and last eight queries of the
+chunk, and random ones (the oracle runs them on a thread pool).  Bars are those of the small parity tests: pooled codes and
 top-k sets and selected scores bit-exact, output per-row relative error <= 2e-2.
 """
 import numpy as np
@@ -35,21 +36,30 @@ def test_full_size_decode_every_query(gpu, name, over, page_rows):
         _print(f"  rel err {err:.2e}")
 
 
-def _prefill_sample(nq, seed=7):
-    fixed = [0, 1, 7, 8, 255, 256, 2047, nq - 8, nq - 1]
+def _prefill_sample(nq, seed=7, n=128):
+    """At least ``n`` seeded queries of the chunk: the first and last query of every
+    512-query block (the first and last 8-query group of each block at both ends),
+    the eight queries the XCD-major scoring order spreads over the eight XCDs at
+    each end of the chunk, then random ones."""
+    fixed = []
+    for b0 in range(0, nq, 512):
+        fixed += [b0, b0 + 7, b0 + 8, b0 + 504, b0 + 511]
+    fixed += list(range(8)) + list(range(nq - 8, nq)) + [255, 256, 2047, 2048]
+    got = set(q for q in fixed if 0 <= q < nq)
     rng = np.random.default_rng(seed)
-    extra = rng.choice(nq, size=3, replace=False).tolist()
-    return sorted(set(int(q) for q in fixed + extra if 0 <= q < nq))
+    while len(got) < min(n, nq):
+        got.add(int(rng.integers(0, nq)))
+    return sorted(got)
 
 
 def test_full_size_prefill_sampled_queries(gpu):
     w = synth.make("csa_prefill_1m")
     csa, hca = w.layers
     qs = _prefill_sample(len(csa.q_pos))
-    _print(f"csa_prefill_1m CSA layer (MXFP4 indexer) prefix={w.prefix} T={w.T} queries={qs}")
-    ref, dev, err = run_and_compare(csa, w.g, queries=qs, prefill=True)
+    _print(f"csa_prefill_1m CSA layer (MXFP4 indexer) prefix={w.prefix} T={w.T} {len(qs)} queries: {qs}")
+    ref, dev, err = run_and_compare(csa, w.g, queries=qs, prefill=True, oracle_threads=16)
     _print(f"  rel err {err:.2e}")
     qh = _prefill_sample(len(hca.q_pos), seed=8)
-    _print(f"csa_prefill_1m HCA layer queries={qh}")
-    ref, dev, err = run_and_compare(hca, w.g, queries=qh, prefill=True)
+    _print(f"csa_prefill_1m HCA layer {len(qh)} queries: {qh}")
+    ref, dev, err = run_and_compare(hca, w.g, queries=qh, prefill=True, oracle_threads=16)
     _print(f"  rel err {err:.2e}")
