@@ -9,7 +9,12 @@ from oracle import step as ostep
 
 TOL_QUANT = 2e-2     # per-row relative error, BF16/FP8 paths
 TOL_F32 = 1e-5       # per-row relative error, f32 path
-TOL_LSE = 2e-2       # absolute lse error, BF16/FP8 paths
+# absolute lse error, BF16/FP8 paths.  lse moves by at most the largest logit error,
+# and a logit errs by the BF16 rounding (2^-9 relative) of the rotated RoPE slice of
+# q and of window keys: |dl| <= 2^-8 sum_rope |q_i k_i|, about 5e-3 for queries
+# N(0,1)/sqrt(512) and N(0,1) keys.  Measured: at most 2.5e-3 (sets of a few keys,
+# where one logit decides lse); 2e-4 .. 5e-4 for long sets.
+TOL_LSE = 5e-3
 
 
 def row_rel_err(o: np.ndarray, ref: np.ndarray) -> float:
@@ -146,9 +151,7 @@ def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, che
     path = "f32" if dev.f32 else "quant"
     MAX_ERR[path] = [max(MAX_ERR[path][0], err), max(MAX_ERR[path][1], lse_err)]
     print(f"  parity ({path}): output rel err {err:.3e}, lse abs err {lse_err:.3e}", flush=True)
-    # lse: float32 storage on the f32 path; on the BF16 path the logits are exact
-    # products of BF16 operands summed in binary32 and the normalizer a binary32 sum
-    # of BF16-rounded probabilities, so lse carries ~1e-4 absolute error (TOL_LSE)
+    # lse: float32 storage on the f32 path; TOL_LSE on the BF16 path
     if dev.f32:
         assert np.allclose(lse, ref["lse"], rtol=1e-6, atol=1e-6)
     else:
