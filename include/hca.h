@@ -401,6 +401,22 @@ int hca_kv_compress(const hca_kv_compress_desc* desc, void* stream);
 int hca_indexer_topk(const hca_indexer_topk_desc* desc, void* stream);
 int hca_attn_decode(const hca_attn_desc* desc, void* stream);
 int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
+/*
+ * hca_attn_decode_noalloc: hca_attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same descriptor, same kernels and the same results bit for bit;
+ * desc->workspace and desc->workspace_bytes are ignored: the scratch is a static
+ * device array of 40 MiB per GPU inside the library, held from the library's load
+ * until the process ends (its address is looked up once per device, on the first
+ * call made with that device current; the stream must belong to the current
+ * device).  The call allocates and frees nothing.  A call needing more scratch than
+ * that (hca_workspace_bytes reports the need) fails with HCA_E_WORKSPACE before
+ * anything is launched; decode calls of up to 256 queries and 64 heads without a
+ * fixed split always fit.  Every call on one GPU shares that GPU's array, and the
+ * kernels need none of its previous contents: calls that overlap on one GPU (on
+ * different streams, unordered) race on it and must not be issued.
+ */
+int hca_attn_decode_noalloc(const hca_attn_desc* desc, void* stream);
 int hca_qkv_prologue(const hca_qkv_prologue_desc* desc, void* stream);
 int hca_out_proj(const hca_out_proj_desc* desc, void* stream);
 int hca_profiled(int op, const void* desc, const hca_profile_events* events, void* stream);

@@ -22,7 +22,8 @@ OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGU
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES, STRUCT_PROFILE_EVENTS = 100, 101, 102
 
 EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes",
-           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_qkv_prologue",
+           "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_attn_decode_noalloc",
+           "hca_qkv_prologue",
            "hca_out_proj", "hca_profiled"]
 
 
@@ -118,6 +119,7 @@ def _load():
     lib.hca_workspace_bytes.argtypes = [c_int, c_void_p, ctypes.POINTER(c_size_t)]
     for name, dt in [("hca_kv_compress", KvCompressDesc), ("hca_indexer_topk", IndexerTopkDesc),
                      ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc),
+                     ("hca_attn_decode_noalloc", AttnDesc),
                      ("hca_qkv_prologue", QkvPrologueDesc), ("hca_out_proj", OutProjDesc)]:
         f = getattr(lib, name)
         f.restype = c_int

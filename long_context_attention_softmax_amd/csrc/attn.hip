@@ -18,6 +18,8 @@
 // them row-wise, P.V reads them transposed with ds_read_b64_tr_b16, so one copy of
 // the tile serves both products.  Each slice leaves (max, sum, unnormalized o) and a
 // combine kernel merges the slices in a fixed order with the sink.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "hca_internal.hpp"
 #include "../../include/hca.h"
@@ -922,6 +924,38 @@ int64_t attention_split_runs(int mode, int k, int n_win, int64_t max_visible, in
 }
 
 int attention_max_runs() { return kMaxRuns; }
+
+// ---------------------------------------------------------------- static scratch
+// The scratch memory of the allocation-free decode entry point: one array per GPU,
+// held from the library's load until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address comes
+// from hipGetSymbolAddress, once per device with that device current, and only that
+// address is handed to kernels.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+size_t attention_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t attention_static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
                                  int64_t max_visible, int io_f32, int prefill, int split_chunks) {

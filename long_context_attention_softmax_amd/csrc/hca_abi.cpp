@@ -174,7 +174,7 @@ int validate_indexer(const hca_indexer_topk_desc* d, size_t* ws) {
 }
 
 // ---------------------------------------------------------------------- attention
-int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
+int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws, bool skip_workspace = false) {
   REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
   REQUIRE(d->struct_size == sizeof(hca_attn_desc), HCA_E_VERSION, "struct_size %u != %zu",
           d->struct_size, sizeof(hca_attn_desc));
@@ -237,7 +237,7 @@ int validate_attn(const hca_attn_desc* d, int prefill, size_t* ws) {
   }
   REQUIRE(aligned(d->sink, 4) && aligned(d->seq_id, 4) && aligned(d->q_pos, 8) && aligned(d->cache_row_start, 8) &&
           (!d->idx || aligned(d->idx, 4)) && (!d->lse || aligned(d->lse, 4)), HCA_E_ALIGN, "index arrays misaligned");
-  if (*ws) {
+  if (*ws && !skip_workspace) {
     REQUIRE(d->workspace && d->workspace_bytes >= *ws, HCA_E_WORKSPACE, "workspace needs %zu bytes, got %zu",
             *ws, d->workspace_bytes);
     REQUIRE(aligned(d->workspace, 256), HCA_E_ALIGN, "workspace must be 256-byte aligned");
@@ -482,6 +482,26 @@ int hca_profiled(int op, const void* desc, const hca_profile_events* ev, void* s
 int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }
 
 int hca_attn_prefill(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 1); }
+
+int hca_attn_decode_noalloc(const hca_attn_desc* d, void* stream) {
+  size_t ws = 0;
+  int rc = validate_attn(d, 0, &ws, true);
+  if (rc) return rc;
+  if (d->Nq == 0) return HCA_OK;
+  const size_t cap = hca::attention_static_scratch_bytes();
+  REQUIRE(ws <= cap, HCA_E_WORKSPACE,
+          "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu (use hca_attn_decode "
+          "with a workspace)", ws, cap);
+  hca_attn_desc c = *d;
+  c.workspace = nullptr;
+  c.workspace_bytes = 0;
+  if (ws) {
+    hipError_t e = hca::attention_static_scratch(&c.workspace);
+    if (e != hipSuccess) return fail(HCA_E_LAUNCH, "static scratch lookup failed: %s", hipGetErrorString(e));
+    c.workspace_bytes = cap;
+  }
+  return attn_call(&c, stream, 0);
+}
 
 int hca_out_proj(const hca_out_proj_desc* d, void* stream) {
   int rc = validate_out_proj(d);

@@ -78,6 +78,10 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
 // most runs of one query under a fixed split of split_chunks chunks (0 when split_chunks <= 0)
 int64_t attention_split_runs(int mode, int k, int n_win, int64_t max_visible, int split_chunks);
 int attention_max_runs();
+// the allocation-free decode entry point's scratch: its size, and its device address
+// on the current device (looked up once per device)
+size_t attention_static_scratch_bytes();
+hipError_t attention_static_scratch(void** ptr);
 
 struct PrologueArgs {
   int Nq, H, D, Nt, W_cap, B, d_I, f32;

@@ -224,7 +224,7 @@ def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_st
           mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
           idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
           o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None,
-          pages=None, split_chunks: int = 0) -> torch.Tensor:
+          pages=None, split_chunks: int = 0, noalloc: bool = False) -> torch.Tensor:
     Nq, H, D = q.shape
     _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
     io = A.F32 if q.dtype == torch.float32 else A.BF16
@@ -258,6 +258,11 @@ def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_st
     d.o = _ptr(o)
     d.lse = _ptr(lse)
     op = A.OP_ATTN_PREFILL if prefill else A.OP_ATTN_DECODE
+    if noalloc:                           # the library's static scratch; no workspace
+        if prof is not None:
+            raise ValueError("the allocation-free entry point has no timing hook")
+        A.check(A.lib.hca_attn_decode_noalloc(ctypes.byref(d), _stream()))
+        return o
     nb = A.workspace_bytes(op, d)
     ws = _workspace(op, nb, q.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
@@ -272,6 +277,13 @@ def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_st
 def hca_attn_decode(*args, **kw) -> torch.Tensor:
     """One-softmax attention of decode queries (see include/hca.h)."""
     return _attn(False, *args, **kw)
+
+
+def hca_attn_decode_noalloc(*args, **kw) -> torch.Tensor:
+    """hca_attn_decode through the allocation-free entry point: the library's static
+    scratch instead of a workspace (pass ``o`` and ``lse`` to allocate nothing here
+    either; see include/hca.h for the size limit and the one-call-at-a-time rule)."""
+    return _attn(False, *args, noalloc=True, **kw)
 
 
 def hca_attn_prefill(*args, **kw) -> torch.Tensor:

@@ -411,3 +411,20 @@ def test_profiled_hook_validation():
     a = attn_desc(H=20)
     assert A.lib.hca_profiled(A.OP_ATTN_DECODE, ctypes.byref(a), ctypes.byref(ev), None) == \
         call("hca_attn_decode", a)
+
+
+def test_noalloc_decode_validation_before_any_launch():
+    """The allocation-free decode entry validates like hca_attn_decode (the workspace
+    fields are ignored), and refuses a call whose scratch need exceeds its static
+    array before touching the device."""
+    d = attn_desc(H=20)
+    assert call("hca_attn_decode_noalloc", d) == call("hca_attn_decode", d) == -5
+    d = attn_desc(Nq=0)
+    assert call("hca_attn_decode_noalloc", d) == 0
+    # HCA, 200 queries, a fixed split of one chunk per run over 4096 visible entries and
+    # the window: 66 runs of partials per query (64 heads x 1 KiB each), far beyond the
+    # static scratch
+    d = attn_desc(Nq=200, mode=1, k=0, max_visible=4096, split_chunks=1)
+    d.workspace, d.workspace_bytes = FAKE, 1 << 40       # ignored by the no-alloc entry
+    assert call("hca_attn_decode_noalloc", d) == -6
+    assert b"scratch" in A.lib.hca_last_error()
