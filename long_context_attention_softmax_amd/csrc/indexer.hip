@@ -486,6 +486,7 @@ struct SelectWs {
   uint32_t* d1;           // [Nq] first digit found once per query (many queries), else null
   uint32_t* cand_count;   // [Nq] (cleared with the histogram, as the next)
   uint32_t* above_count;  // [Nq]  merged selection: keys above the first digit
+  uint32_t* done;         // [Nq]  fused decode select: chunks of the query collected
   uint32_t* above_key;    // [Nq, k]
   int32_t* above_idx;     // [Nq, k]
   uint32_t* cand_key;     // [Nq, kCandCap2]
@@ -678,8 +679,191 @@ __device__ uint32_t emit_ordered(const IndexerArgs& a, int n, const uint32_t (&k
   return tot;
 }
 
+// Position of this lane's item in a list appended to through *counter (LDS or
+// global): one atomic per wave for the lanes with pred set, in lane order.  Called
+// by every active lane of the wave; the result is meaningful where pred is set.
+__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
+  const uint64_t m = __ballot(pred);
+  if (!m) return 0;
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(m);
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(m));
+  base = __shfl(base, leader, 64);
+  return base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+}
+
+// Device-coherent word access (relaxed, device scope): what one workgroup stores
+// this way is seen by another's loads once the store has completed, with no cache
+// write-back or invalidation (those make a device-scope fence cost microseconds).
+__device__ __forceinline__ uint32_t ld_dev(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float key_float(uint32_t k) {        // inverse of float_key (no -0 arises)
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Digits 2 and 3 of the k-th largest key T (digit 1 = d1; *need = its rank inside d1
+// on entry, the number of keys equal to T to keep on return), from the candidate
+// list (key_at(i), i < n1: every key whose first digit is d1) or, when the list
+// overflowed (!have), from the query's scores.  *n_eq: candidates equal to T.
+template <int NT, class KeyAt>
+__device__ uint32_t resolve_threshold(const float* sc, int64_t V, uint32_t d1, uint32_t* need, bool have, KeyAt key_at,
+                                      uint32_t n1, uint32_t* s_hist, uint32_t* s_wave, int* s_found, uint32_t* s_need,
+                                      uint32_t* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = d1;
+  for (int round = 0; round < 2; ++round) {
+    const int shift = round == 0 ? 10 : 0;
+    const int nbits = round == 0 ? 11 : 10;
+    const int nb = 1 << nbits;
+    for (int i = tid; i < kBins; i += NT) s_hist[i] = 0;
+    __syncthreads();
+    if (have) {
+      for (uint32_t i = tid; i < n1; i += NT) {
+        const uint32_t key = key_at(i);
+        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
+      }
+    } else {
+      for (int64_t j = tid; j < V; j += NT) {
+        const uint32_t key = float_key(sc[j]);
+        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    const int dd = find_digit<NT>(s_hist, nb, need, s_wave, s_found, s_need);
+    if (round == 1) *n_eq = s_hist[dd];
+    prefix = (prefix << nbits) | (uint32_t)dd;
+  }
+  __syncthreads();                                       // every thread has read n_eq before s_hist is reused
+  return prefix;
+}
+
+// The selection of one query from its threshold T: every key above d1 (ws.above_*),
+// the candidates above T and the take_eq lowest-index candidates equal to T, each
+// written at the rank of its index (ascending); or, when the candidate list
+// overflowed (!have), one ordered pass over the scores.  The lists are read with
+// device-coherent loads (they may have been written by other workgroups of the
+// same launch).
+template <int NT, class KeyAt, class IdxAt>
+__device__ void emit_merged(const IndexerArgs& a, const SelectWs& ws, int n, int64_t V, int64_t K, uint32_t T,
+                            uint32_t take_eq, uint32_t n_eq, bool have, KeyAt key_at, IdxAt idx_at, uint32_t n1,
+                            const float* sc, uint32_t* s_hist, uint32_t* s_sk, int32_t* s_sj, uint32_t* s_fill,
+                            uint32_t* s_tk, int32_t* s_tj, uint32_t* s_wave, int* s_found, uint32_t* s_need,
+                            uint32_t* s_ns) {
+  const int tid = threadIdx.x;
+  int32_t* const out = a.idx + (int64_t)n * a.k;
+  float* const so = reinterpret_cast<float*>(a.score_out);
+  if (!have) {
+    uint32_t sel_before = 0, eq_seen = 0;
+    constexpr int64_t kStretch = (int64_t)NT * kPerThread1;
+    for (int64_t b0 = 0; b0 < V; b0 += kStretch) {
+      const int64_t b1 = b0 + kStretch < V ? b0 + kStretch : V;
+      const int64_t bt = b0 + (int64_t)kPerThread1 * tid;
+      uint32_t kk[kPerThread1];
+      load_chunk_keys(sc, bt, b1, kk);
+      const uint32_t tt = emit_ordered<NT>(a, n, kk, bt, b1, T, take_eq, sel_before, eq_seen, K, sc, s_wave);
+      const uint32_t gt = tt & 0xFFFF, eq = tt >> 16;
+      const uint32_t took = (eq_seen + eq < take_eq ? eq_seen + eq : take_eq) - (eq_seen < take_eq ? eq_seen : take_eq);
+      sel_before += gt + took;
+      eq_seen += eq;
+    }
+    return;
+  }
+  // equal keys: the take_eq lowest indices, i.e. the take_eq largest of 2^30 - 1 - j
+  // (three 10-bit digits)
+  uint32_t inv_min = 0;
+  if (take_eq < n_eq) {
+    uint32_t need_i = take_eq, pre = 0;
+    for (int round = 0; round < 3; ++round) {
+      const int shift = 20 - 10 * round;
+      for (int i = tid; i < 1024; i += NT) s_hist[i] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < n1; i += NT) {
+        if (key_at(i) != T) continue;
+        const uint32_t inv = 0x3FFFFFFFu - (uint32_t)idx_at(i);
+        if ((inv >> (shift + 10)) == pre) atomicAdd(&s_hist[(inv >> shift) & 1023], 1u);
+      }
+      __syncthreads();
+      const int dd = find_digit<NT>(s_hist, 1024, &need_i, s_wave, s_found, s_need);
+      pre = (pre << 10) | (uint32_t)dd;
+    }
+    inv_min = pre;
+  }
+  // the selected entries (exactly K; the checks below only guard the LDS bounds),
+  // then each one's output position is the rank of its index
+  if (tid == 0) *s_ns = 0;
+  __syncthreads();
+  const uint32_t na = min(ld_dev(&ws.above_count[n]), (uint32_t)a.k);
+  for (uint32_t i0 = 0; i0 < na; i0 += NT) {
+    const uint32_t i = i0 + tid;
+    const bool in = i < na;
+    const uint32_t p = wave_append(s_ns, in);
+    if (in && p < (uint32_t)kMergedMaxK) {
+      s_sk[p] = ld_dev(&ws.above_key[(int64_t)n * a.k + i]);
+      s_sj[p] = (int32_t)ld_dev(reinterpret_cast<uint32_t*>(&ws.above_idx[(int64_t)n * a.k + i]));
+    }
+  }
+  for (uint32_t i0 = 0; i0 < n1; i0 += NT) {
+    const uint32_t i = i0 + tid;
+    uint32_t k2 = 0;
+    int32_t j = 0;
+    bool take = false;
+    if (i < n1) {
+      k2 = key_at(i);
+      j = idx_at(i);
+      take = k2 > T || (k2 == T && 0x3FFFFFFFu - (uint32_t)j >= inv_min);
+    }
+    const uint32_t p = wave_append(s_ns, take);
+    if (take && p < (uint32_t)kMergedMaxK) {
+      s_sk[p] = k2;
+      s_sj[p] = j;
+    }
+  }
+  __syncthreads();
+  const uint32_t ns = min(*s_ns, (uint32_t)kMergedMaxK);  // == K <= kMergedMaxK
+  // ---- order by index: counting sort on the index's high bits (at most kBins
+  // buckets), then each entry's rank among the entries of its bucket
+  int shift = 0;
+  while (((V - 1) >> shift) >= kBins) ++shift;
+  for (int b = tid; b < kBins; b += NT) { s_hist[b] = 0; s_fill[b] = 0; }
+  __syncthreads();
+  for (uint32_t e = tid; e < ns; e += NT) atomicAdd(&s_hist[s_sj[e] >> shift], 1u);
+  __syncthreads();
+  {
+    constexpr int kPerB = kBins / NT;
+    uint32_t c[kPerB], sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPerB; ++q) { c[q] = s_hist[kPerB * tid + q]; sum += c[q]; }
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan<NT>(sum, s_wave, &tot);
+#pragma unroll
+    for (int q = 0; q < kPerB; ++q) { s_hist[kPerB * tid + q] = off; off += c[q]; }
+  }
+  __syncthreads();
+  for (uint32_t e = tid; e < ns; e += NT) {
+    const int32_t j = s_sj[e];
+    const int b = j >> shift;
+    const uint32_t p = s_hist[b] + atomicAdd(&s_fill[b], 1u);
+    s_tj[p] = j;
+    s_tk[p] = s_sk[e];
+  }
+  __syncthreads();
+  for (uint32_t p = tid; p < ns; p += NT) {
+    const int32_t j = s_tj[p];
+    const int b = j >> shift;
+    const uint32_t b0 = s_hist[b], b1 = b0 + s_fill[b];
+    uint32_t r = b0;
+    for (uint32_t q = b0; q < b1; ++q) r += (uint32_t)(s_tj[q] < j);
+    if (r < (uint32_t)K) {
+      out[r] = j;
+      if (so) so[(int64_t)n * a.k + r] = key_float(s_tk[p]);
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(IndexerArgs a, SelectWs ws) {
@@ -731,131 +915,15 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
     }
   }
   __syncthreads();
-  uint32_t prefix = d1;
   uint32_t n_eq = 0;                                     // candidates equal to T (in the list)
-  for (int round = 0; round < 2; ++round) {
-    const int shift = round == 0 ? 10 : 0;
-    const int nbits = round == 0 ? 11 : 10;
-    const int nb = 1 << nbits;
-    for (int i = tid; i < kBins; i += kSelectThreads) s_hist[i] = 0;
-    __syncthreads();
-    if (in_lds) {
-      for (uint32_t i = tid; i < n1; i += kSelectThreads) {
-        const uint32_t key = s_ck[i];
-        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
-      }
-    } else {
-      for (int64_t j = tid; j < V; j += kSelectThreads) {
-        const uint32_t key = float_key(sc[j]);
-        if ((key >> (shift + nbits)) == prefix) atomicAdd(&s_hist[(key >> shift) & (nb - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    const int dd = find_digit<kSelectThreads>(s_hist, nb, &need, s_wave, &s_found, &s_need);
-    if (round == 1) n_eq = s_hist[dd];
-    prefix = (prefix << nbits) | (uint32_t)dd;
-  }
-  const uint32_t T = prefix, take_eq = need;
+  auto lds_key = [&](uint32_t i) { return s_ck[i]; };
+  auto lds_idx = [&](uint32_t i) { return s_cj[i]; };
+  const uint32_t T = resolve_threshold<kSelectThreads>(sc, V, d1, &need, in_lds, lds_key, n1, s_hist, s_wave, &s_found,
+                                                       &s_need, &n_eq);
+  const uint32_t take_eq = need;
   if (merged) {
-    __syncthreads();                                     // every thread has read n_eq before s_hist is reused
-    if (!in_lds) {
-      // the candidates overflowed their list: one ordered pass over the scores
-      uint32_t sel_before = 0, eq_seen = 0;
-      constexpr int64_t kStretch = (int64_t)kSelectThreads * kPerThread1;
-      for (int64_t b0 = 0; b0 < V; b0 += kStretch) {
-        const int64_t b1 = b0 + kStretch < V ? b0 + kStretch : V;
-        const int64_t bt = b0 + (int64_t)kPerThread1 * tid;
-        uint32_t kk[kPerThread1];
-        load_chunk_keys(sc, bt, b1, kk);
-        const uint32_t tt = emit_ordered<kSelectThreads>(a, n, kk, bt, b1, T, take_eq, sel_before, eq_seen, K, sc, s_wave);
-        const uint32_t gt = tt & 0xFFFF, eq = tt >> 16;
-        const uint32_t took = (eq_seen + eq < take_eq ? eq_seen + eq : take_eq) - (eq_seen < take_eq ? eq_seen : take_eq);
-        sel_before += gt + took;
-        eq_seen += eq;
-      }
-      return;
-    }
-    // equal keys: the take_eq lowest indices, i.e. the take_eq largest of 2^30 - 1 - j
-    // (three 10-bit digits)
-    uint32_t inv_min = 0;
-    if (take_eq < n_eq) {
-      uint32_t need_i = take_eq, pre = 0;
-      for (int round = 0; round < 3; ++round) {
-        const int shift = 20 - 10 * round;
-        for (int i = tid; i < 1024; i += kSelectThreads) s_hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = tid; i < n1; i += kSelectThreads) {
-          if (s_ck[i] != T) continue;
-          const uint32_t inv = 0x3FFFFFFFu - (uint32_t)s_cj[i];
-          if ((inv >> (shift + 10)) == pre) atomicAdd(&s_hist[(inv >> shift) & 1023], 1u);
-        }
-        __syncthreads();
-        const int dd = find_digit<kSelectThreads>(s_hist, 1024, &need_i, s_wave, &s_found, &s_need);
-        pre = (pre << 10) | (uint32_t)dd;
-      }
-      inv_min = pre;
-    }
-    // the selected entries: every key above d1, the candidates above T and the equal
-    // keys taken (exactly K; the checks below only guard the LDS bounds); then each
-    // one's output position is the rank of its index
-    if (tid == 0) s_ns = 0;
-    __syncthreads();
-    const uint32_t na = min(ws.above_count[n], (uint32_t)a.k);
-    for (uint32_t i = tid; i < na; i += kSelectThreads) {
-      const uint32_t p = atomicAdd(&s_ns, 1u);
-      if (p < (uint32_t)kMergedMaxK) {
-        s_sk[p] = ws.above_key[(int64_t)n * a.k + i];
-        s_sj[p] = ws.above_idx[(int64_t)n * a.k + i];
-      }
-    }
-    for (uint32_t i = tid; i < n1; i += kSelectThreads) {
-      const uint32_t k2 = s_ck[i];
-      const int32_t j = s_cj[i];
-      if (k2 > T || (k2 == T && 0x3FFFFFFFu - (uint32_t)j >= inv_min)) {
-        const uint32_t p = atomicAdd(&s_ns, 1u);
-        if (p < (uint32_t)kMergedMaxK) {
-          s_sk[p] = k2;
-          s_sj[p] = j;
-        }
-      }
-    }
-    __syncthreads();
-    const uint32_t ns = min(s_ns, (uint32_t)kMergedMaxK);   // == K <= kMergedMaxK
-    const uint32_t ns32 = (ns + 31) & ~31u;
-    if (tid < ns32 - ns) s_sj[ns + tid] = 0x7FFFFFFF;    // pads to a multiple of 32 (never below an index)
-    __syncthreads();
-    constexpr int kPer = kMergedMaxK / kSelectThreads;
-    int32_t mine[kPer];
-    uint32_t rank[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      mine[r] = tid + (uint32_t)kSelectThreads * r < ns ? s_sj[tid + kSelectThreads * r] : 0x7FFFFFFF;
-      rank[r] = 0;
-    }
-    // waves without an entry skip the pass; eight 16-byte reads in flight per step
-    const uint32_t wave_first = tid & ~63u;
-    if (wave_first < ns || (kPer > 1 && wave_first + kSelectThreads < ns)) {
-      const int4* c4 = reinterpret_cast<const int4*>(s_sj);
-      for (uint32_t f = 0; f < ns32 / 4; f += 8) {
-        int4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = c4[f + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int r = 0; r < kPer; ++r)
-            rank[r] += (uint32_t)(v[u].x < mine[r]) + (uint32_t)(v[u].y < mine[r]) + (uint32_t)(v[u].z < mine[r]) +
-                       (uint32_t)(v[u].w < mine[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const uint32_t e = tid + (uint32_t)kSelectThreads * r;
-      if (e < ns && rank[r] < (uint32_t)K) {
-        out[rank[r]] = mine[r];
-        if (so) so[(int64_t)n * a.k + rank[r]] = key_float(s_sk[e]);
-      }
-    }
+    emit_merged<kSelectThreads>(a, ws, n, V, K, T, take_eq, n_eq, in_lds, lds_key, lds_idx, n1, sc, s_hist, s_sk, s_sj,
+                                s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
     return;
   }
   // per-chunk counts of the candidates above T and equal to T
@@ -938,6 +1006,157 @@ __global__ void __launch_bounds__(256) select_emit_kernel(IndexerArgs a, SelectW
   emit_ordered<256>(a, n, key, jt, j1, T, take_eq, pos_base, eqb, K, sc, s_wave);
 }
 
+// Decode (fewer than kDigitMinQ queries, k <= kMergedMaxK): the whole selection in one
+// launch.  The (query, 4096-entry chunk) items are spread over the workgroups; each
+// finds d1 from the scoring kernel's histogram, appends its chunk's candidates (first
+// digit d1) and its keys above d1 to the query's lists, then counts itself done.  The
+// workgroup that completes a query's count resolves T and writes the selection.  The
+// lists pass between workgroups through device-coherent stores and loads, each store
+// complete before its workgroup's count is raised.  No workgroup waits for another.
+constexpr int kFusedThreads = 512;
+constexpr int kFusedPer = kChunk1 / kFusedThreads;     // scores per thread of a chunk
+constexpr int kFusedCandLds = 4096;                      // candidates the finisher holds in LDS
+#ifndef HCA_SELECT_FUSED_GRID
+#define HCA_SELECT_FUSED_GRID 512
+#endif
+__global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4))) select_fused_kernel(IndexerArgs a, SelectWs ws) {
+  __shared__ uint32_t s_hist[kBins];
+  // collect: a chunk's candidates from the front, its keys above d1 from the back;
+  // finish: the query's candidates (kChunk1 <= kFusedCandLds)
+  __shared__ __attribute__((aligned(16))) uint32_t s_ck[kFusedCandLds];
+  __shared__ int32_t s_cj[kFusedCandLds];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sk[kMergedMaxK];
+  __shared__ __attribute__((aligned(16))) int32_t s_sj[kMergedMaxK + 32];
+  __shared__ int s_pref[kDigitMinQ + 1];
+  __shared__ uint32_t s_wave[kFusedThreads / 64 + 1];
+  __shared__ int s_found;
+  __shared__ uint32_t s_need, s_ns, s_n, s_na, s_base, s_abase, s_last;
+  static_assert(kChunk1 <= kFusedCandLds, "a chunk's appends fit the candidate arrays");
+  static_assert(kFusedCandLds >= kBins + kMergedMaxK && kFusedCandLds >= kMergedMaxK, "ordering scratch fits");
+  const int tid = threadIdx.x;
+  // items of query t: one per chunk of its visible entries (one when it keeps them all)
+  {
+    int items = 0;
+    if (tid < a.Nq) {
+      const int64_t V = visible(a, tid);
+      items = V <= (int64_t)a.k ? 1 : (int)((V + kChunk1 - 1) / kChunk1);
+    }
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan<kFusedThreads>((uint32_t)items, s_wave, &tot);
+    if (tid < a.Nq) s_pref[tid] = (int)pre;
+    if (tid == 0) s_pref[a.Nq] = (int)tot;
+    __syncthreads();
+  }
+  const int total = s_pref[a.Nq];
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = a.Nq - 1;                           // the query whose items hold `item`
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo, c = item - s_pref[n];
+    const int nitems = s_pref[n + 1] - s_pref[n];
+    const int64_t V = visible(a, n);
+    const int64_t K = V < a.k ? V : a.k;
+    const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
+    int32_t* const out = a.idx + (int64_t)n * a.k;
+    float* const so = reinterpret_cast<float*>(a.score_out);
+    if (V <= K) {                                        // every visible entry, at its own position
+      for (int64_t p = tid; p < a.k; p += kFusedThreads) {
+        out[p] = p < V ? (int32_t)p : -1;
+        if (so) so[(int64_t)n * a.k + p] = p < V ? sc[p] : 0.0f;
+      }
+      continue;
+    }
+    // ---- collect: this chunk's scores (requested first), the first digit d1
+    const int64_t j0 = (int64_t)c * kChunk1;
+    const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
+    const int64_t jt = j0 + (int64_t)kFusedPer * tid;
+    uint32_t key[kFusedPer];
+#pragma unroll
+    for (int v = 0; v < kFusedPer / 4; ++v) {
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (jt + 4 * v < j1) f = *reinterpret_cast<const float4*>(sc + jt + 4 * v);   // rows padded to 64
+      key[4 * v] = float_key(f.x); key[4 * v + 1] = float_key(f.y);
+      key[4 * v + 2] = float_key(f.z); key[4 * v + 3] = float_key(f.w);
+    }
+    const uint32_t* gh = a.hist + (int64_t)n * kBins;
+    for (int i = tid; i < kBins; i += kFusedThreads) s_hist[i] = gh[i];
+    if (tid == 0) { s_n = 0; s_na = 0; }
+    __syncthreads();
+    uint32_t need = (uint32_t)K;
+    const uint32_t d1 = (uint32_t)find_digit<kFusedThreads>(s_hist, kBins, &need, s_wave, &s_found, &s_need);
+#pragma unroll
+    for (int e = 0; e < kFusedPer; ++e) {
+      const bool in = jt + e < j1;
+      const uint32_t dg = key[e] >> 21;
+      const bool cand = in && dg == d1, above = in && dg > d1;
+      const uint32_t pc = wave_append(&s_n, cand);
+      const uint32_t pa = wave_append(&s_na, above);
+      if (cand || above) {
+        const uint32_t p = cand ? pc : kChunk1 - 1 - pa;
+        s_ck[p] = key[e];
+        s_cj[p] = (int32_t)(jt + e);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      s_base = s_n ? atomicAdd(&ws.cand_count[n], s_n) : 0;
+      s_abase = s_na ? atomicAdd(&ws.above_count[n], s_na) : 0;
+    }
+    __syncthreads();
+    const uint32_t cnt = s_n, base = s_base, na = s_na, abase = s_abase;
+    uint32_t* const gk = ws.cand_key + (int64_t)n * kCandCap2;
+    uint32_t* const gj = reinterpret_cast<uint32_t*>(ws.cand_idx + (int64_t)n * kCandCap2);
+    for (uint32_t i = tid; i < cnt; i += kFusedThreads) {
+      const uint32_t p = base + i;
+      if (p < (uint32_t)kCandCap2) {
+        st_dev(gk + p, s_ck[i]);
+        st_dev(gj + p, (uint32_t)s_cj[i]);
+      }
+    }
+    for (uint32_t i = tid; i < na; i += kFusedThreads) {
+      const uint32_t p = abase + i;                      // < k: fewer than k keys lie above d1
+      if (p < (uint32_t)a.k) {
+        st_dev(ws.above_key + (int64_t)n * a.k + p, s_ck[kChunk1 - 1 - i]);
+        st_dev(reinterpret_cast<uint32_t*>(ws.above_idx + (int64_t)n * a.k + p), (uint32_t)s_cj[kChunk1 - 1 - i]);
+      }
+    }
+    // ---- count this chunk done; the last of the query's chunks finishes it.  Every
+    // thread's device-coherent stores have completed (the wait) before the count is
+    // raised, and the finisher reads the lists with device-coherent loads.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&ws.done[n], 1u) == (uint32_t)(nitems - 1);
+    __syncthreads();
+    if (!s_last) continue;                               // uniform
+    const uint32_t n1 = ld_dev(&ws.cand_count[n]);
+    uint32_t n_eq = 0;
+    if (n1 <= (uint32_t)kFusedCandLds) {
+      for (uint32_t i = tid; i < n1; i += kFusedThreads) {
+        s_ck[i] = ld_dev(gk + i);
+        s_cj[i] = (int32_t)ld_dev(gj + i);
+      }
+      __syncthreads();
+      auto key_at = [&](uint32_t i) { return s_ck[i]; };
+      auto idx_at = [&](uint32_t i) { return s_cj[i]; };
+      const uint32_t T = resolve_threshold<kFusedThreads>(sc, V, d1, &need, true, key_at, n1, s_hist, s_wave, &s_found,
+                                                          &s_need, &n_eq);
+      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, true, key_at, idx_at, n1, sc, s_hist, s_sk, s_sj,
+                                 s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
+    } else {                                             // in place (or, past kCandCap2, from the scores)
+      const bool have = n1 <= (uint32_t)kCandCap2;
+      auto key_at = [&](uint32_t i) { return ld_dev(gk + i); };
+      auto idx_at = [&](uint32_t i) { return (int32_t)ld_dev(gj + i); };
+      const uint32_t T = resolve_threshold<kFusedThreads>(sc, V, d1, &need, have, key_at, n1, s_hist, s_wave, &s_found,
+                                                          &s_need, &n_eq);
+      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, have, key_at, idx_at, n1, sc, s_hist, s_sk, s_sj,
+                                 s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
+    }
+    __syncthreads();                                     // LDS reused by the next item
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -956,7 +1175,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
   if (fmt == HCA_F32) return L;
   L.nch = (int)((max_visible + kChunk1 - 1) / kChunk1);
   if (L.nch < 1) L.nch = 1;
-  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 2) * 4);        // histogram, candidate and above counts
+  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 3) * 4);        // histogram; candidate, above and done counts
   L.cand_key = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.cand_idx = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.chunk_gt = o; o = up(o + (size_t)Nq * L.nch * 4);
@@ -964,7 +1183,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
   L.eq_before = o; o = up(o + (size_t)Nq * L.nch * 4);
   L.state = o; o = up(o + (size_t)Nq * 2 * 4);
   L.d1 = o; o = up(o + (size_t)Nq * 4);
-  L.merged = Nq >= kDigitMinQ && k >= 1 && k <= kMergedMaxK;
+  L.merged = k >= 1 && k <= kMergedMaxK;
   const size_t kf = L.merged ? (size_t)k : 0;           // keys above the first digit
   L.above_key = o; o = up(o + (size_t)Nq * kf * 4);
   L.above_idx = o; o = up(o + (size_t)Nq * kf * 4);
@@ -1011,6 +1230,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   sw.d1 = a.Nq >= kDigitMinQ ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
   sw.above_count = sw.cand_count + a.Nq;
+  sw.done = sw.above_count + a.Nq;
   sw.above_key = L.merged ? reinterpret_cast<uint32_t*>(wsb + L.above_key) : nullptr;
   sw.above_idx = L.merged ? reinterpret_cast<int32_t*>(wsb + L.above_idx) : nullptr;
   sw.cand_key = reinterpret_cast<uint32_t*>(wsb + L.cand_key);
@@ -1023,7 +1243,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   {
     // the scoring kernel histograms the first digit and the collect phase counts
     // candidates and keys above the first digit: clear them first (they are adjacent)
-    const int64_t n16 = ((int64_t)a.Nq * (kBins + 2) * 4 + 15) / 16;
+    const int64_t n16 = ((int64_t)a.Nq * (kBins + 3) * 4 + 15) / 16;
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
@@ -1043,6 +1263,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
   dim3 cgrid((unsigned)L.nch, a.Nq);
+  if (L.merged && !sw.d1) {                              // few queries: one launch
+    hipLaunchKernelGGL(select_fused_kernel, dim3(HCA_SELECT_FUSED_GRID), dim3(kFusedThreads), 0, s, a, sw);
+    return hipGetLastError();
+  }
   if (sw.d1) {
     hipLaunchKernelGGL(select_digit_kernel, dim3(a.Nq), dim3(256), 0, s, a, sw);
     hipLaunchKernelGGL(select_collect_kernel<true>, cgrid, dim3(256), 0, s, a, sw);
