@@ -108,6 +108,42 @@ def committed_traffic(summary="profiles/hbm_counters.ragged_pair_32.md"):
         return None
 
 
+# ------------------------------------------------------- rocprofv3 summaries
+def rocprof_summary(path):
+    """Markdown table of a rocprofv3 CSV: a ``*_kernel_stats.csv`` (--kernel-trace
+    --stats) gives calls and durations per kernel; a ``*_counter_collection.csv``
+    (--pmc) gives each counter's mean per dispatch, per kernel."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(path)))
+    lines = []
+    if path.endswith("kernel_stats.csv"):
+        tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+        lines += ["| kernel | calls | avg us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+    elif path.endswith("counter_collection.csv"):
+        val = defaultdict(lambda: defaultdict(float))
+        disp = defaultdict(set)
+        counters = []
+        for r in rows:
+            k, c = r["Kernel_Name"], r["Counter_Name"]
+            val[k][c] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+            if c not in counters:
+                counters.append(c)
+        lines += ["| kernel | dispatches | " + " | ".join(counters) + " |",
+                  "|---|---:|" + "---:|" * len(counters)]
+        for k, v in val.items():
+            n = len(disp[k])
+            lines.append(f"| `{k}` | {n} | " + " | ".join(f"{v[c] / n:,.0f}" for c in counters) + " |")
+    else:
+        raise SystemExit(f"{path}: expected a rocprofv3 *_kernel_stats.csv or *_counter_collection.csv")
+    return "\n".join(lines)
+
+
 # ---------------------------------------------------------------- GPU timing
 PROF_EVERY = 8     # steps of the timed region whose profiled kernel gets its own event pair
 
@@ -209,8 +245,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy a 1 GiB buffer a few times (reference for HBM byte counters) and exit")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV",
+                    help="print markdown tables of rocprofv3 CSV output (kernel stats or counters) and exit")
     ap.add_argument("--only", default=None, help="debug: run one workload (ragged|csa|ragged4|paged|invariant|prologue|outproj|hca|prefill)")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        for path in args.rocprof_summary:
+            print(f"{os.path.basename(path)}:\n\n{rocprof_summary(path)}\n")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(sequences are independent, so more GPUs shard the batch with no exchange).",
