@@ -39,6 +39,7 @@ METRIC = "decode attn tokens/s and HBM GB/s at 1M ctx (CSA+HCA); prefill indexer
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0
+PREFILL_GROUP = 824        # the library's query group for the 4096-query chunk (workspace within 896 MiB)
 ENTRY_BYTES = 448 + 128 + 4          # FP8 nope + BF16 rope + f32 scale
 TOKEN_BYTES = 512 * 2                # raw BF16 window token
 KEY_BYTES = 128                      # FP8 indexer key
@@ -475,32 +476,48 @@ def main():
             lays = device_layers(w4)
             csa4 = lays[0]
             steps4 = max(3, min(10, args.steps // 10))
-            for _ in range(2):
-                csa4.pool()
+            for _ in range(2):                # warm-up: every kernel of the chunk loaded and run once
+                for lay in lays:
+                    lay.pool()
                 csa4.select()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps4)]
-            for a, b in evs:
-                a.record()
-                b.record()
+                csa4.attend(prefill=True)
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             s0.record()
             for i in range(steps4):
                 for lay in lays:
                     lay.pool()
-                csa4.select(prof=evs[i])
+                csa4.select()
                 csa4.attend(prefill=True)
             s1.record()
             torch.cuda.synchronize()
             chunk_ms = s0.elapsed_time(s1) / steps4
-            kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+            from long_context_attention_softmax_amd import _abi as A, ops
+            idx_ws = max(v.numel() for key, v in ops._WS.items() if key[0] == A.OP_INDEXER_TOPK)
+            # the scoring kernel alone: the library scores many queries in groups (its
+            # workspace holds one group), so the chunk's queries are passed here in
+            # groups of the same size, with events around each group's scoring kernel
+            G = PREFILL_GROUP
+            groups = [slice(g0, min(g0 + G, csa4.Nq)) for g0 in range(0, csa4.Nq, G)]
+            evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+                   for _ in range(steps4)]
+            for e in evs:                     # create the events (torch makes them on first record)
+                for a, b in e:
+                    a.record()
+                    b.record()
+            for i in range(steps4):
+                for sl, ev in zip(groups, evs[i]):
+                    csa4.select(prof=ev, queries=sl)
+            torch.cuda.synchronize()
+            kms = float(np.mean([sum(a.elapsed_time(b) for a, b in e) for e in evs]))
             secondary["csa_prefill_1m"] = dict(
                 indexer_scoring_tflops=round(flops / (kms * 1e-3) / 1e12, 1),
                 indexer_scoring_ms=round(kms, 3),
                 fp8_peak_frac=round(flops / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                 fp4_peak_frac=round(flops / (kms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
                 scoring_flop=flops, visible_pairs=pairs, chunk_ms=round(chunk_ms, 3),
-                chunk_tokens_per_s=round(w4.T / (chunk_ms * 1e-3), 1))
+                chunk_tokens_per_s=round(w4.T / (chunk_ms * 1e-3), 1), indexer_workspace_bytes=idx_ws,
+                scoring_groups=len(groups))
             log(f"[bench] prefill: chunk {chunk_ms:.3f} ms, scoring {kms:.3f} ms")
             del lays, csa4
             torch.cuda.empty_cache()

@@ -187,6 +187,13 @@ typedef struct hca_kv_compress_desc {
  * Quantized keys: max_visible <= 2^23, key (and, for MXFP4, key-scale) pitches
  * below 2^24 bytes, and max_visible times each such pitch (page_rows times it,
  * with a page table) below 2^32 bytes; otherwise HCA_E_UNSUPPORTED.
+ * Workspace (quantized operands): the call keeps one f32 score row per query of a
+ * query group (ceil(max_visible / 64) * 256 bytes each) plus the selection's
+ * lists (about 75 KB per query); a call with more than 256 queries runs in
+ * near-equal groups of a multiple of 8 queries (at least 256) whose workspace fits
+ * in 896 MiB, one group after the other on the stream, so the workspace stays
+ * within that whatever Nq (at least 256 queries' worth; the results are those of
+ * one group holding every query).
  */
 typedef struct hca_indexer_topk_desc {
   uint32_t struct_size;
@@ -375,7 +382,8 @@ typedef struct hca_out_proj_desc {
  * Timing hook for benchmarks (not part of the computation): hca_profiled runs the
  * call (op, desc) exactly as its own entry point does and records the event `begin`
  * on the stream immediately before, and `end` immediately after, that call's main
- * kernel: the scoring kernel of HCA_OP_INDEXER_TOPK (top-k selection excluded), the
+ * kernel: the scoring kernel of HCA_OP_INDEXER_TOPK (top-k selection excluded; of
+ * the first query group when the call runs in several), the
  * attention kernel of HCA_OP_ATTN_DECODE / HCA_OP_ATTN_PREFILL (the combine of split
  * decode queries excluded).  begin and end are hipEvent_t values passed as void*
  * (either may be NULL).  Other ops: HCA_E_UNSUPPORTED.

@@ -47,9 +47,12 @@ struct IndexerArgs {
   uint32_t* hist;                     // workspace: [Nq, 2048] (quantized only)
   hipEvent_t prof_begin, prof_end;    // optional, around the scoring kernel
   const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged keys (page_shift >= 0)
+  int many;                           // set per group of a grouped call: the many-query plan
 };
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k);
+// queries per launch group of a call with Nq queries (its workspace holds one group)
+int indexer_group(int Nq, int64_t max_visible, int fmt, int k);
 
 struct AttnArgs {
   int Nq, H, D, D_r, mode, m, k, n_win, win_cap, io_f32;

@@ -1205,13 +1205,55 @@ void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
-  return ws_layout(Nq, max_visible, fmt, k).total;
+// Queries per launch group: the quantized path materializes one f32 score row per
+// query, so a call with many queries is processed in near-equal groups (a multiple
+// of 8 queries, at least kDigitMinQ) whose workspace - score rows and selection
+// lists - fits in HCA_INDEXER_WS_BUDGET bytes: each group is scored and selected
+// before the next, and every group takes the many-query plan (the same scores and
+// the same selection as one launch over all queries).
+#ifndef HCA_INDEXER_WS_BUDGET
+#define HCA_INDEXER_WS_BUDGET (896ull << 20)
+#endif
+int indexer_group(int Nq, int64_t max_visible, int fmt, int k) {
+  if (fmt == HCA_F32 || Nq <= kDigitMinQ) return Nq;
+  const size_t per_q = ws_layout(kDigitMinQ, max_visible, fmt, k).total / kDigitMinQ + 1;
+  int64_t gmax = (int64_t)(HCA_INDEXER_WS_BUDGET / per_q) / 8 * 8;
+  if (gmax < kDigitMinQ) gmax = kDigitMinQ;
+  if (gmax >= Nq) return Nq;
+  const int64_t ng = (Nq + gmax - 1) / gmax;
+  const int64_t g = ((Nq + ng - 1) / ng + 7) / 8 * 8;
+  return g < Nq ? (int)g : Nq;
 }
 
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
+  return ws_layout(indexer_group(Nq, max_visible, fmt, k), max_visible, fmt, k).total;
+}
+
+hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s);
+
 hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
+  if (a0.Nq == 0) return hipSuccess;
+  const int G = indexer_group(a0.Nq, a0.max_visible, a0.fmt, a0.k);
+  for (int g0 = 0; g0 < a0.Nq; g0 += G) {
+    IndexerArgs a = a0;
+    a.Nq = a0.Nq - g0 < G ? a0.Nq - g0 : G;
+    a.q = a0.q + (int64_t)g0 * a0.H_I * a0.q_pitch;
+    if (a0.q_scales) a.q_scales = a0.q_scales + (int64_t)g0 * a0.H_I * a0.q_scale_pitch;
+    a.w = a0.w + (int64_t)g0 * a0.H_I;
+    a.seq_id = a0.seq_id + g0;
+    a.q_pos = a0.q_pos + g0;
+    a.idx = a0.idx + (int64_t)g0 * a0.k;
+    if (a0.score_out) a.score_out = static_cast<float*>(a0.score_out) + (int64_t)g0 * a0.k;
+    if (g0 > 0) a.prof_begin = a.prof_end = nullptr;     // the events bracket the first group's scoring
+    a.many = G < a0.Nq;                                  // several groups: the many-query plan for each
+    const hipError_t e = launch_indexer_group(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
   IndexerArgs a = a0;
-  if (a.Nq == 0) return hipSuccess;
   const int64_t chunks_f64 = (a.max_visible + 255) / 256;
   if (a.fmt == HCA_F32) {
     if (a.prof_begin) hipEventRecord(a.prof_begin, s);
@@ -1226,8 +1268,9 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   const WsLayout L = ws_layout(a.Nq, a.max_visible, a.fmt, a.k);
   char* wsb = static_cast<char*>(a.scores);
   a.hist = reinterpret_cast<uint32_t*>(wsb + L.hist);
+  const bool many = a.Nq >= kDigitMinQ || a.many;
   SelectWs sw;
-  sw.d1 = a.Nq >= kDigitMinQ ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
+  sw.d1 = many ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
   sw.above_count = sw.cand_count + a.Nq;
   sw.done = sw.above_count + a.Nq;
@@ -1248,7 +1291,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
   // MXFP4 with few queries takes the decode tiling (chunk-major, HCA_SCORE_TPW4D tiles)
-  const bool few4 = a.fmt == HCA_MXFP4 && a.Nq < kFewQ;
+  const bool few4 = a.fmt == HCA_MXFP4 && a.Nq < kFewQ && !many;
   const int tpw = a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : few4 ? HCA_SCORE_TPW4D : HCA_SCORE_TPW4;
   const int64_t epw = entries_per_wg_t(tpw);
   const int64_t chunks = (a.max_visible + epw - 1) / epw;

@@ -184,11 +184,14 @@ class DeviceLayer:
                         raw_idx=self.win_idx if self.mode == A.MODE_CSA else None,
                         out_idx=self.keys if self.mode == A.MODE_CSA else None, debug=debug)
 
-    def select(self, score: Optional[torch.Tensor] = None, prof=None):
+    def select(self, score: Optional[torch.Tensor] = None, prof=None, queries: Optional[slice] = None):
+        """Indexer top-k of every query, or of the queries in ``queries`` (a slice)."""
         g = self.g
-        return hca_indexer_topk(self.qI, self.w, self.keys, self.cache_row_start, self.seq_id, self.q_pos,
-                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx, score=score,
-                                prof=prof, pages=self.pages)
+        qs = queries if queries is not None else slice(None)
+        qI = IdxCache(self.qI.data[qs], self.qI.fmt, None if self.qI.scales is None else self.qI.scales[qs])
+        return hca_indexer_topk(qI, self.w[qs], self.keys, self.cache_row_start, self.seq_id[qs], self.q_pos[qs],
+                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx[qs],
+                                score=None if score is None else score[qs], prof=prof, pages=self.pages)
 
     def attend(self, prefill: bool = False, prof=None):
         g = self.g

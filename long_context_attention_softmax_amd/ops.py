@@ -84,6 +84,9 @@ def _stream() -> int:
 
 def _events(prof) -> "ctypes._Pointer":
     """The timing hook's event pair: prof = (begin, end) torch.cuda.Event objects."""
+    for e in prof:
+        if e.cuda_event == 0:             # torch creates an event on its first record
+            e.record()
     ev = A.new_desc(A.ProfileEvents)
     ev.begin, ev.end = prof[0].cuda_event, prof[1].cuda_event
     return ctypes.byref(ev)
