@@ -885,14 +885,23 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const __bf16* po = pp.o + slot0 * kD + 8 * lane;
   const size_t ostride = sstride * kD;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sidx = 0; sidx < S; ++sidx) {
-    const uint4 v = *reinterpret_cast<const uint4*>(po + sidx * ostride);
-    const float w = s_w[wave][sidx];
-    const uint32_t* vw = &v.x;
+  // eight runs' rows requested at once, then added in run order
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    uint4 v[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_to_f32((uint16_t)vw[e]) * w;
-      acc[2 * e + 1] += bf16_to_f32((uint16_t)(vw[e] >> 16)) * w;
+    for (int u = 0; u < 8; ++u)
+      v[u] = s0 + u < S ? *reinterpret_cast<const uint4*>(po + (size_t)(s0 + u) * ostride) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < S) {
+        const float w = s_w[wave][s0 + u];
+        const uint32_t* vw = &v[u].x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_to_f32((uint16_t)vw[e]) * w;
+          acc[2 * e + 1] += bf16_to_f32((uint16_t)(vw[e] >> 16)) * w;
+        }
+      }
     }
   }
   uint4 o4;
