@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(NT) pool_d512_kernel(PoolArgs a) {
   constexpr int PER = kFastD / NT > 0 ? kFastD / NT : 1;          // dims per thread in the final stage
   constexpr int RW = (448 % NT) / 64;                            // the wave holding dims 448 .. 511
   constexpr int RK = 448 / NT;                                   // ... in its slot RK
-  __shared__ double s_z[NW * TOK];
+  __shared__ double s_z[NW * TOK], s_e[NW * TOK];     // gate logits, e^(z_t - max)
   __shared__ double s_part[NW][kFastD];
   __shared__ double s_party[Y ? NW : 1][Y ? kFastMaxDI : 1];
   __shared__ double s_red[NW];
@@ -316,30 +316,47 @@ __global__ void __launch_bounds__(NT) pool_d512_kernel(PoolArgs a) {
     }
     zt[j] = acc;
   }
+  // the TOK partial dots summed over the wave at once: a reduce-scatter over lane
+  // bits 5, 4, ... (each step halves the values a lane keeps), then a butterfly over
+  // the remaining bits; lane L ends with the sum of token j = L >> (6 - log2 TOK)
+  constexpr int kLogT = TOK >= 16 ? 4 : TOK >= 8 ? 3 : TOK >= 4 ? 2 : TOK >= 2 ? 1 : 0;
+  static_assert((1 << kLogT) == TOK, "TOK is a power of two");
 #pragma unroll
-  for (int j = 0; j < TOK; ++j) zt[j] = wave_sum(zt[j]);
-  if (lane == 0) {
+  for (int st = 0; st < kLogT; ++st) {
+    const int o = 32 >> st, half = TOK >> (st + 1);
+    const bool upper = (lane & o) != 0;
 #pragma unroll
-    for (int j = 0; j < TOK; ++j) {
-      const int t = wave + NW * j;
-      if (t < m) s_z[t] = zt[j] + (double)a.gate_b[t];
+    for (int i = 0; i < half; ++i) {
+      const double mine = upper ? zt[i + half] : zt[i];
+      const double give = upper ? zt[i] : zt[i + half];
+      zt[i] = mine + __shfl_xor(give, o, 64);
     }
   }
+  double zs = zt[0];
+#pragma unroll
+  for (int o = 32 >> kLogT; o >= 1; o >>= 1) zs += __shfl_xor(zs, o, 64);
+  {
+    const int t = wave + NW * (lane >> (6 - kLogT));
+    if ((lane & ((64 >> kLogT) - 1)) == 0 && t < m) s_z[t] = zs + (double)a.gate_b[t];
+  }
   __syncthreads();
-  // softmax over the block, formed by every wave: alpha_t = e^(z_t - max) / sum
+  // softmax over the block: alpha_t = e^(z_t - max) / sum; each exponential formed
+  // once (thread t), the max and the sum by every wave from LDS in one order
   double mx = -INFINITY;
   for (int i = lane; i < m; i += 64) mx = fmax(mx, s_z[i]);
   mx = wave_max(mx);
-  double sum = 0.0;
-  for (int i = lane; i < m; i += 64) sum += exp(s_z[i] - mx);
-  sum = wave_sum(sum);
+  if (tid < m) s_e[tid] = exp(s_z[tid] - mx);
+  __syncthreads();
+  double sm = 0.0;
+  for (int i = lane; i < m; i += 64) sm += s_e[i];
+  const double inv = 1.0 / wave_sum(sm);
   // weighted sums of this wave's tokens
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, accy[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < TOK; ++j) {
     const int t = wave + NW * j;
     if (t < m) {
-      const double al = exp(s_z[t] - mx) / sum;
+      const double al = s_e[t] * inv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += al * el(xr[j], e);
       if (Y && lane < ngi) {
