@@ -40,11 +40,16 @@ def _prefill_sample(nq, seed=7, n=128):
     """At least ``n`` seeded queries of the chunk: the first and last query of every
     512-query block (the first and last 8-query group of each block at both ends),
     the eight queries the XCD-major scoring order spreads over the eight XCDs at
-    each end of the chunk, then random ones."""
+    each end of the chunk, both sides of the indexer's query-group boundaries, then
+    random ones."""
     fixed = []
     for b0 in range(0, nq, 512):
         fixed += [b0, b0 + 7, b0 + 8, b0 + 504, b0 + 511]
     fixed += list(range(8)) + list(range(nq - 8, nq)) + [255, 256, 2047, 2048]
+    # both sides of each query-group boundary of the indexer at this size (the
+    # 4096-query call over a 1M prefix runs in five groups of 824 queries)
+    for g0 in range(824, nq, 824):
+        fixed += [g0 - 1, g0]
     got = set(q for q in fixed if 0 <= q < nq)
     rng = np.random.default_rng(seed)
     while len(got) < min(n, nq):
