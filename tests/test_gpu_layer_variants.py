@@ -62,7 +62,10 @@ def test_window_only_fixed_split_invariant(gpu):
 @pytest.mark.parametrize("split", [0, 1])
 def test_window_only_empty_set(gpu, split):
     """n_win = 0 in the window-only mode: every set is empty, so o = 0 and lse = the
-    sink (the oracle's attention over no keys); default plan and fixed split."""
+    sink (the oracle's attention over no keys).  split_chunks = 1 asks for the fixed
+    split, but with every set empty no query has a run and the launch takes the
+    default plan; test_hca_empty_and_nonempty_sets_mixed runs the split itself with
+    empty sets beside non-empty ones."""
     from long_context_attention_softmax_amd.layer import DeviceLayer
     g = replace(synth.FULL_GEOMETRY, n_win=0)
     lens = np.array([1, 300, 5000], np.int64)
