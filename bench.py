@@ -39,7 +39,7 @@ METRIC = "decode attn tokens/s and HBM GB/s at 1M ctx (CSA+HCA); prefill indexer
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0
-PREFILL_GROUP = 824        # the library's query group for the 4096-query chunk (workspace within 896 MiB)
+PREFILL_GROUP = 416        # the library's query group for the 4096-query chunk (two groups' workspace within 896 MiB)
 ENTRY_BYTES = 448 + 128 + 4          # FP8 nope + BF16 rope + f32 scale
 TOKEN_BYTES = 512 * 2                # raw BF16 window token
 KEY_BYTES = 128                      # FP8 indexer key

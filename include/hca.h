@@ -187,13 +187,16 @@ typedef struct hca_kv_compress_desc {
  * Quantized keys: max_visible <= 2^23, key (and, for MXFP4, key-scale) pitches
  * below 2^24 bytes, and max_visible times each such pitch (page_rows times it,
  * with a page table) below 2^32 bytes; otherwise HCA_E_UNSUPPORTED.
- * Workspace (quantized operands): the call keeps one f32 score row per query of a
- * query group (ceil(max_visible / 64) * 256 bytes each) plus the selection's
- * lists (about 75 KB per query); a call with more than 256 queries runs in
- * near-equal groups of a multiple of 8 queries (at least 256) whose workspace fits
- * in 896 MiB, one group after the other on the stream, so the workspace stays
- * within that whatever Nq (at least 256 queries' worth; the results are those of
- * one group holding every query).
+ * Workspace (quantized operands): one f32 score row per query of a query group
+ * (ceil(max_visible / 64) * 256 bytes each) plus the selection's lists (about
+ * 75 KB per query).  A call whose whole workspace would exceed 896 MiB runs in
+ * near-equal query groups (a multiple of 8 queries, at least 256) and keeps two
+ * groups: group g is scored on `stream` while the selection of group g - 1 runs
+ * on a second stream the library creates once per device (default priority),
+ * joined back to `stream` through events before the call returns, so work queued
+ * on `stream` afterwards sees every result.  The workspace stays within 896 MiB
+ * whatever Nq (at least two groups of 256 queries' worth), and the results are
+ * those of one group holding every query.
  */
 typedef struct hca_indexer_topk_desc {
   uint32_t struct_size;

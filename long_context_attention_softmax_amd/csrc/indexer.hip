@@ -26,6 +26,8 @@
 //
 // Selection: exact radix select on the orderable 32-bit key of each score, lower
 // index first among equal scores, output in ascending index order.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "hca_internal.hpp"
 #include "../../include/hca.h"
@@ -1205,71 +1207,26 @@ void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-// Queries per launch group: the quantized path materializes one f32 score row per
-// query, so a call with many queries is processed in near-equal groups (a multiple
-// of 8 queries, at least kDigitMinQ) whose workspace - score rows and selection
-// lists - fits in HCA_INDEXER_WS_BUDGET bytes: each group is scored and selected
-// before the next, and every group takes the many-query plan (the same scores and
-// the same selection as one launch over all queries).
-#ifndef HCA_INDEXER_WS_BUDGET
-#define HCA_INDEXER_WS_BUDGET (896ull << 20)
-#endif
-int indexer_group(int Nq, int64_t max_visible, int fmt, int k) {
-  if (fmt == HCA_F32 || Nq <= kDigitMinQ) return Nq;
-  const size_t per_q = ws_layout(kDigitMinQ, max_visible, fmt, k).total / kDigitMinQ + 1;
-  int64_t gmax = (int64_t)(HCA_INDEXER_WS_BUDGET / per_q) / 8 * 8;
-  if (gmax < kDigitMinQ) gmax = kDigitMinQ;
-  if (gmax >= Nq) return Nq;
-  const int64_t ng = (Nq + gmax - 1) / gmax;
-  const int64_t g = ((Nq + ng - 1) / ng + 7) / 8 * 8;
-  return g < Nq ? (int)g : Nq;
-}
+namespace {
 
-size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
-  return ws_layout(indexer_group(Nq, max_visible, fmt, k), max_visible, fmt, k).total;
-}
+// The launches of one query group: the score phase (clear the counters, score) and
+// the select phase, each on its own stream.
+struct GroupPlan {
+  IndexerArgs a;
+  WsLayout L;
+  SelectWs sw;
+};
 
-hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s);
-
-hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
-  if (a0.Nq == 0) return hipSuccess;
-  const int G = indexer_group(a0.Nq, a0.max_visible, a0.fmt, a0.k);
-  for (int g0 = 0; g0 < a0.Nq; g0 += G) {
-    IndexerArgs a = a0;
-    a.Nq = a0.Nq - g0 < G ? a0.Nq - g0 : G;
-    a.q = a0.q + (int64_t)g0 * a0.H_I * a0.q_pitch;
-    if (a0.q_scales) a.q_scales = a0.q_scales + (int64_t)g0 * a0.H_I * a0.q_scale_pitch;
-    a.w = a0.w + (int64_t)g0 * a0.H_I;
-    a.seq_id = a0.seq_id + g0;
-    a.q_pos = a0.q_pos + g0;
-    a.idx = a0.idx + (int64_t)g0 * a0.k;
-    if (a0.score_out) a.score_out = static_cast<float*>(a0.score_out) + (int64_t)g0 * a0.k;
-    if (g0 > 0) a.prof_begin = a.prof_end = nullptr;     // the events bracket the first group's scoring
-    a.many = G < a0.Nq;                                  // several groups: the many-query plan for each
-    const hipError_t e = launch_indexer_group(a, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
-  IndexerArgs a = a0;
-  const int64_t chunks_f64 = (a.max_visible + 255) / 256;
-  if (a.fmt == HCA_F32) {
-    if (a.prof_begin) hipEventRecord(a.prof_begin, s);
-    if (a.max_visible > 0) {
-      size_t lds = (size_t)a.H_I * a.d_I * sizeof(float);
-      hipLaunchKernelGGL(score_f64_kernel, dim3((unsigned)chunks_f64, a.Nq), dim3(256), lds, s, a);
-    }
-    if (a.prof_end) hipEventRecord(a.prof_end, s);
-    hipLaunchKernelGGL(select_small_f64_kernel, dim3(a.Nq), dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
-  const WsLayout L = ws_layout(a.Nq, a.max_visible, a.fmt, a.k);
+GroupPlan plan_group(const IndexerArgs& a0) {
+  GroupPlan p;
+  p.a = a0;
+  IndexerArgs& a = p.a;
+  p.L = ws_layout(a.Nq, a.max_visible, a.fmt, a.k);
+  const WsLayout& L = p.L;
   char* wsb = static_cast<char*>(a.scores);
   a.hist = reinterpret_cast<uint32_t*>(wsb + L.hist);
   const bool many = a.Nq >= kDigitMinQ || a.many;
-  SelectWs sw;
+  SelectWs& sw = p.sw;
   sw.d1 = many ? reinterpret_cast<uint32_t*>(wsb + L.d1) : nullptr;
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
   sw.above_count = sw.cand_count + a.Nq;
@@ -1283,6 +1240,11 @@ hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
   sw.eq_before = reinterpret_cast<uint32_t*>(wsb + L.eq_before);
   sw.state = reinterpret_cast<uint32_t*>(wsb + L.state);
   sw.nch = L.nch;
+  return p;
+}
+
+void launch_score_phase(const GroupPlan& p, hipStream_t s) {
+  const IndexerArgs& a = p.a;
   {
     // the scoring kernel histograms the first digit and the collect phase counts
     // candidates and keys above the first digit: clear them first (they are adjacent)
@@ -1291,7 +1253,7 @@ hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
   // MXFP4 with few queries takes the decode tiling (chunk-major, HCA_SCORE_TPW4D tiles)
-  const bool few4 = a.fmt == HCA_MXFP4 && a.Nq < kFewQ && !many;
+  const bool few4 = a.fmt == HCA_MXFP4 && a.Nq < kFewQ && !p.sw.d1;
   const int tpw = a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : few4 ? HCA_SCORE_TPW4D : HCA_SCORE_TPW4;
   const int64_t epw = entries_per_wg_t(tpw);
   const int64_t chunks = (a.max_visible + epw - 1) / epw;
@@ -1305,10 +1267,16 @@ hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
     else launch_score<HCA_MXFP4, false, T4>(a, g2, s);
   }
   if (a.prof_end) hipEventRecord(a.prof_end, s);
+}
+
+void launch_select_phase(const GroupPlan& p, hipStream_t s) {
+  const IndexerArgs& a = p.a;
+  const WsLayout& L = p.L;
+  const SelectWs& sw = p.sw;
   dim3 cgrid((unsigned)L.nch, a.Nq);
   if (L.merged && !sw.d1) {                              // few queries: one launch
     hipLaunchKernelGGL(select_fused_kernel, dim3(HCA_SELECT_FUSED_GRID), dim3(kFusedThreads), 0, s, a, sw);
-    return hipGetLastError();
+    return;
   }
   if (sw.d1) {
     hipLaunchKernelGGL(select_digit_kernel, dim3(a.Nq), dim3(256), 0, s, a, sw);
@@ -1318,6 +1286,125 @@ hipError_t launch_indexer_group(const IndexerArgs& a0, hipStream_t s) {
   }
   hipLaunchKernelGGL(select_threshold_kernel, dim3(a.Nq), dim3(kSelectThreads), 0, s, a, sw);
   if (!L.merged) hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
+}
+
+// Per device, created on first use: the stream the select phases of a grouped call
+// run on (default priority), and one "scored" and one "selected" event per
+// workspace half.
+constexpr int kMaxDev = 64;
+struct AuxStreams {
+  hipStream_t st = nullptr;
+  hipEvent_t scored[2] = {nullptr, nullptr}, selected[2] = {nullptr, nullptr}, start = nullptr;
+};
+std::mutex g_aux_mu;
+AuxStreams g_aux[kMaxDev];
+
+hipError_t aux_streams(AuxStreams** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  AuxStreams& x = g_aux[dev];
+  if (!x.st) {
+    if ((e = hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking)) != hipSuccess) return e;
+    for (int h = 0; h < 2; ++h) {
+      if ((e = hipEventCreateWithFlags(&x.scored[h], hipEventDisableTiming)) != hipSuccess) return e;
+      if ((e = hipEventCreateWithFlags(&x.selected[h], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    if ((e = hipEventCreateWithFlags(&x.start, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &x;
+  return hipSuccess;
+}
+
+}  // namespace
+
+// Queries per launch group: the quantized path materializes one f32 score row per
+// query, so a call with many queries is processed in near-equal groups (a multiple
+// of 8 queries, at least kDigitMinQ).  The workspace holds two groups: group g is
+// scored on the caller's stream into half g mod 2 while the select phase of group
+// g - 1 runs on a second stream (scoring is bound by the vector ALU, the select by
+// memory, so the two overlap); each half - score rows and selection lists - fits in
+// HCA_INDEXER_WS_BUDGET / 2 bytes.  Every group takes the many-query plan: the same
+// scores and the same selection as one launch over all queries.
+#ifndef HCA_INDEXER_WS_BUDGET
+#define HCA_INDEXER_WS_BUDGET (896ull << 20)
+#endif
+int indexer_group(int Nq, int64_t max_visible, int fmt, int k) {
+  if (fmt == HCA_F32 || Nq <= kDigitMinQ) return Nq;
+  const size_t per_q = ws_layout(kDigitMinQ, max_visible, fmt, k).total / kDigitMinQ + 1;
+  const size_t budget = ws_layout(Nq, max_visible, fmt, k).total <= HCA_INDEXER_WS_BUDGET ? HCA_INDEXER_WS_BUDGET
+                                                                                        : HCA_INDEXER_WS_BUDGET / 2;
+  if (budget == HCA_INDEXER_WS_BUDGET) return Nq;                  // one group fits whole
+  int64_t gmax = (int64_t)(budget / per_q) / 8 * 8;
+  if (gmax < kDigitMinQ) gmax = kDigitMinQ;
+  if (gmax >= Nq) return Nq;
+  const int64_t ng = (Nq + gmax - 1) / gmax;
+  const int64_t g = ((Nq + ng - 1) / ng + 7) / 8 * 8;
+  return g < Nq ? (int)g : Nq;
+}
+
+size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
+  const int G = indexer_group(Nq, max_visible, fmt, k);
+  const size_t half = ws_layout(G, max_visible, fmt, k).total;
+  return G < Nq ? 2 * half : half;
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
+  if (a0.Nq == 0) return hipSuccess;
+  if (a0.fmt == HCA_F32) {
+    const int64_t chunks_f64 = (a0.max_visible + 255) / 256;
+    if (a0.prof_begin) hipEventRecord(a0.prof_begin, s);
+    if (a0.max_visible > 0) {
+      size_t lds = (size_t)a0.H_I * a0.d_I * sizeof(float);
+      hipLaunchKernelGGL(score_f64_kernel, dim3((unsigned)chunks_f64, a0.Nq), dim3(256), lds, s, a0);
+    }
+    if (a0.prof_end) hipEventRecord(a0.prof_end, s);
+    hipLaunchKernelGGL(select_small_f64_kernel, dim3(a0.Nq), dim3(256), 0, s, a0);
+    return hipGetLastError();
+  }
+  const int G = indexer_group(a0.Nq, a0.max_visible, a0.fmt, a0.k);
+  if (G >= a0.Nq) {                                      // one group, one stream
+    const GroupPlan p = plan_group(a0);
+    launch_score_phase(p, s);
+    launch_select_phase(p, s);
+    return hipGetLastError();
+  }
+  AuxStreams* x = nullptr;
+  hipError_t e = aux_streams(&x);
+  if (e != hipSuccess) return e;
+  const size_t half = ws_layout(G, a0.max_visible, a0.fmt, a0.k).total;
+  // the second stream starts after everything the caller enqueued before this call
+  if ((e = hipEventRecord(x->start, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(x->st, x->start, 0)) != hipSuccess) return e;
+  int ng = 0;
+  for (int g0 = 0; g0 < a0.Nq; g0 += G, ++ng) {
+    const int h = ng & 1;
+    IndexerArgs a = a0;
+    a.Nq = a0.Nq - g0 < G ? a0.Nq - g0 : G;
+    a.q = a0.q + (int64_t)g0 * a0.H_I * a0.q_pitch;
+    if (a0.q_scales) a.q_scales = a0.q_scales + (int64_t)g0 * a0.H_I * a0.q_scale_pitch;
+    a.w = a0.w + (int64_t)g0 * a0.H_I;
+    a.seq_id = a0.seq_id + g0;
+    a.q_pos = a0.q_pos + g0;
+    a.idx = a0.idx + (int64_t)g0 * a0.k;
+    if (a0.score_out) a.score_out = static_cast<float*>(a0.score_out) + (int64_t)g0 * a0.k;
+    if (g0 > 0) a.prof_begin = a.prof_end = nullptr;     // the events bracket the first group's scoring
+    a.many = 1;                                          // several groups: the many-query plan for each
+    a.scores = static_cast<char*>(a0.scores) + h * half;
+    const GroupPlan p = plan_group(a);
+    // half h is free once the select phase of group ng - 2 is done
+    if (ng >= 2 && (e = hipStreamWaitEvent(s, x->selected[h], 0)) != hipSuccess) return e;
+    launch_score_phase(p, s);
+    if ((e = hipEventRecord(x->scored[h], s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(x->st, x->scored[h], 0)) != hipSuccess) return e;
+    launch_select_phase(p, x->st);
+    if ((e = hipEventRecord(x->selected[h], x->st)) != hipSuccess) return e;
+  }
+  // the caller's stream continues after every group's selection
+  for (int h = 0; h < 2 && h < ng; ++h)
+    if ((e = hipStreamWaitEvent(s, x->selected[h], 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@ def _prefill_sample(nq, seed=7, n=128):
         fixed += [b0, b0 + 7, b0 + 8, b0 + 504, b0 + 511]
     fixed += list(range(8)) + list(range(nq - 8, nq)) + [255, 256, 2047, 2048]
     # both sides of each query-group boundary of the indexer at this size (the
-    # 4096-query call over a 1M prefix runs in five groups of 824 queries)
-    for g0 in range(824, nq, 824):
+    # 4096-query call over a 1M prefix runs in ten groups of 416 queries)
+    for g0 in range(416, nq, 416):
         fixed += [g0 - 1, g0]
     got = set(q for q in fixed if 0 <= q < nq)
     rng = np.random.default_rng(seed)
