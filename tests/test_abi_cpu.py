@@ -428,3 +428,32 @@ def test_noalloc_decode_validation_before_any_launch():
     d.workspace, d.workspace_bytes = FAKE, 1 << 40       # ignored by the no-alloc entry
     assert call("hca_attn_decode_noalloc", d) == -6
     assert b"scratch" in A.lib.hca_last_error()
+
+
+def _idx_ws(Nq, max_visible, fmt=None):
+    d = idx_desc(Nq=Nq, max_visible=max_visible)
+    if fmt is not None:
+        d.q.fmt = d.keys.fmt = fmt
+        if fmt == A.MXFP4:
+            d.q.pitch = d.keys.pitch = 64
+    n = ctypes.c_size_t(0)
+    assert A.lib.hca_workspace_bytes(A.OP_INDEXER_TOPK, ctypes.byref(d), ctypes.byref(n)) == 0
+    return n.value
+
+
+@pytest.mark.parametrize("fmt", [A.FP8_E4M3, A.MXFP4])
+def test_indexer_workspace_is_bounded_by_query_groups(fmt):
+    """A quantized indexer call keeps f32 score rows for at most two query groups:
+    whatever Nq, its workspace stays within 896 MiB once one group of every query
+    would not; below that it grows with Nq (one group, per-query rows)."""
+    budget = 896 << 20
+    row = 263168 * 4                                     # one score row at a 1M-token prefix
+    small = _idx_ws(64, 263168, fmt)
+    assert 64 * row <= small < budget
+    assert _idx_ws(128, 263168, fmt) > small             # one group: grows with the queries
+    for nq in (1024, 4096, 16384, 65536):
+        ws = _idx_ws(nq, 263168, fmt)
+        assert nq * row > budget                         # one group would not fit
+        assert 2 * 256 * row <= ws <= budget             # two groups of at least 256 queries
+    # short prefixes: every query in one group, no split
+    assert _idx_ws(4096, 4096, fmt) == pytest.approx(4096 * _idx_ws(1, 4096, fmt), rel=0.05)
