@@ -745,15 +745,15 @@ __device__ uint32_t resolve_threshold(const float* sc, int64_t V, uint32_t d1, u
   return prefix;
 }
 
-// The selection of one query from its threshold T: every key above d1 (ws.above_*),
-// the candidates above T and the take_eq lowest-index candidates equal to T, each
-// written at the rank of its index (ascending); or, when the candidate list
-// overflowed (!have), one ordered pass over the scores.  The lists are read with
-// device-coherent loads (they may have been written by other workgroups of the
-// same launch).
+// The selection of one query from its threshold T: every key above d1 (the caller
+// has put the na of them in s_sk/s_sj[0, na)), the candidates above T and the
+// take_eq lowest-index candidates equal to T, each written at the rank of its index
+// (ascending); or, when the candidate list overflowed (!have), one ordered pass over
+// the scores.
 template <int NT, class KeyAt, class IdxAt>
 __device__ void emit_merged(const IndexerArgs& a, const SelectWs& ws, int n, int64_t V, int64_t K, uint32_t T,
                             uint32_t take_eq, uint32_t n_eq, bool have, KeyAt key_at, IdxAt idx_at, uint32_t n1,
+                            uint32_t na,
                             const float* sc, uint32_t* s_hist, uint32_t* s_sk, int32_t* s_sj, uint32_t* s_fill,
                             uint32_t* s_tk, int32_t* s_tj, uint32_t* s_wave, int* s_found, uint32_t* s_need,
                             uint32_t* s_ns) {
@@ -798,18 +798,8 @@ __device__ void emit_merged(const IndexerArgs& a, const SelectWs& ws, int n, int
   }
   // the selected entries (exactly K; the checks below only guard the LDS bounds),
   // then each one's output position is the rank of its index
-  if (tid == 0) *s_ns = 0;
+  if (tid == 0) *s_ns = na;                              // the keys above d1: s_sk/s_sj[0, na), placed by the caller
   __syncthreads();
-  const uint32_t na = min(ld_dev(&ws.above_count[n]), (uint32_t)a.k);
-  for (uint32_t i0 = 0; i0 < na; i0 += NT) {
-    const uint32_t i = i0 + tid;
-    const bool in = i < na;
-    const uint32_t p = wave_append(s_ns, in);
-    if (in && p < (uint32_t)kMergedMaxK) {
-      s_sk[p] = ld_dev(&ws.above_key[(int64_t)n * a.k + i]);
-      s_sj[p] = (int32_t)ld_dev(reinterpret_cast<uint32_t*>(&ws.above_idx[(int64_t)n * a.k + i]));
-    }
-  }
   for (uint32_t i0 = 0; i0 < n1; i0 += NT) {
     const uint32_t i = i0 + tid;
     uint32_t k2 = 0;
@@ -916,6 +906,11 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
       s_cj[i] = ws.cand_idx[(int64_t)n * kCandCap2 + i];
     }
   }
+  const uint32_t na = merged ? min(ws.above_count[n], (uint32_t)a.k) : 0;
+  for (uint32_t i = tid; i < na && i < (uint32_t)kMergedMaxK; i += kSelectThreads) {
+    s_sk[i] = ws.above_key[(int64_t)n * a.k + i];
+    s_sj[i] = ws.above_idx[(int64_t)n * a.k + i];
+  }
   __syncthreads();
   uint32_t n_eq = 0;                                     // candidates equal to T (in the list)
   auto lds_key = [&](uint32_t i) { return s_ck[i]; };
@@ -924,7 +919,7 @@ __global__ void __launch_bounds__(kSelectThreads) select_threshold_kernel(Indexe
                                                        &s_need, &n_eq);
   const uint32_t take_eq = need;
   if (merged) {
-    emit_merged<kSelectThreads>(a, ws, n, V, K, T, take_eq, n_eq, in_lds, lds_key, lds_idx, n1, sc, s_hist, s_sk, s_sj,
+    emit_merged<kSelectThreads>(a, ws, n, V, K, T, take_eq, n_eq, in_lds, lds_key, lds_idx, n1, na, sc, s_hist, s_sk, s_sj,
                                 s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
     return;
   }
@@ -1107,7 +1102,7 @@ __global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per
       s_abase = s_na ? atomicAdd(&ws.above_count[n], s_na) : 0;
     }
     __syncthreads();
-    const uint32_t cnt = s_n, base = s_base, na = s_na, abase = s_abase;
+    const uint32_t cnt = s_n, base = s_base, cna = s_na, abase = s_abase;
     uint32_t* const gk = ws.cand_key + (int64_t)n * kCandCap2;
     uint32_t* const gj = reinterpret_cast<uint32_t*>(ws.cand_idx + (int64_t)n * kCandCap2);
     for (uint32_t i = tid; i < cnt; i += kFusedThreads) {
@@ -1117,7 +1112,7 @@ __global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per
         st_dev(gj + p, (uint32_t)s_cj[i]);
       }
     }
-    for (uint32_t i = tid; i < na; i += kFusedThreads) {
+    for (uint32_t i = tid; i < cna; i += kFusedThreads) {
       const uint32_t p = abase + i;                      // < k: fewer than k keys lie above d1
       if (p < (uint32_t)a.k) {
         st_dev(ws.above_key + (int64_t)n * a.k + p, s_ck[kChunk1 - 1 - i]);
@@ -1133,18 +1128,44 @@ __global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per
     __syncthreads();
     if (!s_last) continue;                               // uniform
     const uint32_t n1 = ld_dev(&ws.cand_count[n]);
+    const uint32_t na = min(ld_dev(&ws.above_count[n]), (uint32_t)a.k);
     uint32_t n_eq = 0;
-    if (n1 <= (uint32_t)kFusedCandLds) {
-      for (uint32_t i = tid; i < n1; i += kFusedThreads) {
-        s_ck[i] = ld_dev(gk + i);
-        s_cj[i] = (int32_t)ld_dev(gj + i);
+    {
+      // the keys above d1 (at most kMergedMaxK) and, when they fit in LDS, the
+      // candidates: every load requested before any is stored
+      constexpr int kPerC = kFusedCandLds / kFusedThreads, kPerA = kMergedMaxK / kFusedThreads;
+      const bool cand_lds = n1 <= (uint32_t)kFusedCandLds;
+      uint32_t* const ak = ws.above_key + (int64_t)n * a.k;
+      uint32_t* const aj = reinterpret_cast<uint32_t*>(ws.above_idx + (int64_t)n * a.k);
+      uint32_t vk[kPerC], vj[kPerC], wk[kPerA], wj[kPerA];
+#pragma unroll
+      for (int u = 0; u < kPerC; ++u) {
+        const uint32_t i = tid + (uint32_t)kFusedThreads * u;
+        if (cand_lds && i < n1) { vk[u] = ld_dev(gk + i); vj[u] = ld_dev(gj + i); }
       }
+#pragma unroll
+      for (int u = 0; u < kPerA; ++u) {
+        const uint32_t i = tid + (uint32_t)kFusedThreads * u;
+        if (i < na) { wk[u] = ld_dev(ak + i); wj[u] = ld_dev(aj + i); }
+      }
+#pragma unroll
+      for (int u = 0; u < kPerC; ++u) {
+        const uint32_t i = tid + (uint32_t)kFusedThreads * u;
+        if (cand_lds && i < n1) { s_ck[i] = vk[u]; s_cj[i] = (int32_t)vj[u]; }
+      }
+#pragma unroll
+      for (int u = 0; u < kPerA; ++u) {
+        const uint32_t i = tid + (uint32_t)kFusedThreads * u;
+        if (i < na) { s_sk[i] = wk[u]; s_sj[i] = (int32_t)wj[u]; }
+      }
+    }
+    if (n1 <= (uint32_t)kFusedCandLds) {
       __syncthreads();
       auto key_at = [&](uint32_t i) { return s_ck[i]; };
       auto idx_at = [&](uint32_t i) { return s_cj[i]; };
       const uint32_t T = resolve_threshold<kFusedThreads>(sc, V, d1, &need, true, key_at, n1, s_hist, s_wave, &s_found,
                                                           &s_need, &n_eq);
-      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, true, key_at, idx_at, n1, sc, s_hist, s_sk, s_sj,
+      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, true, key_at, idx_at, n1, na, sc, s_hist, s_sk, s_sj,
                                  s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
     } else {                                             // in place (or, past kCandCap2, from the scores)
       const bool have = n1 <= (uint32_t)kCandCap2;
@@ -1152,7 +1173,7 @@ __global__ void __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per
       auto idx_at = [&](uint32_t i) { return (int32_t)ld_dev(gj + i); };
       const uint32_t T = resolve_threshold<kFusedThreads>(sc, V, d1, &need, have, key_at, n1, s_hist, s_wave, &s_found,
                                                           &s_need, &n_eq);
-      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, have, key_at, idx_at, n1, sc, s_hist, s_sk, s_sj,
+      emit_merged<kFusedThreads>(a, ws, n, V, K, T, need, n_eq, have, key_at, idx_at, n1, na, sc, s_hist, s_sk, s_sj,
                                  s_ck, s_ck + kBins, s_cj, s_wave, &s_found, &s_need, &s_ns);
     }
     __syncthreads();                                     // LDS reused by the next item
