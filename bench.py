@@ -39,7 +39,6 @@ METRIC = "decode attn tokens/s and HBM GB/s at 1M ctx (CSA+HCA); prefill indexer
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0
-PREFILL_GROUP = 416        # the library's query group for the 4096-query chunk (two groups' workspace within 896 MiB)
 ENTRY_BYTES = 448 + 128 + 4          # FP8 nope + BF16 rope + f32 scale
 TOKEN_BYTES = 512 * 2                # raw BF16 window token
 KEY_BYTES = 128                      # FP8 indexer key
@@ -495,9 +494,9 @@ def main():
             from long_context_attention_softmax_amd import _abi as A, ops
             idx_ws = max(v.numel() for key, v in ops._WS.items() if key[0] == A.OP_INDEXER_TOPK)
             # the scoring kernel alone: the library scores many queries in groups (its
-            # workspace holds one group), so the chunk's queries are passed here in
-            # groups of the same size, with events around each group's scoring kernel
-            G = PREFILL_GROUP
+            # workspace holds two), so the chunk's queries are passed here in groups
+            # of the same size, with events around each group's scoring kernel
+            G = ops.hca_indexer_query_group(csa4.Nq, csa4.max_visible, csa4.qI.fmt, csa4.g.topk)
             groups = [slice(g0, min(g0 + G, csa4.Nq)) for g0 in range(0, csa4.Nq, G)]
             evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
                    for _ in range(steps4)]
@@ -517,7 +516,7 @@ def main():
                 fp4_peak_frac=round(flops / (kms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
                 scoring_flop=flops, visible_pairs=pairs, chunk_ms=round(chunk_ms, 3),
                 chunk_tokens_per_s=round(w4.T / (chunk_ms * 1e-3), 1), indexer_workspace_bytes=idx_ws,
-                scoring_groups=len(groups))
+                scoring_groups=len(groups), scoring_group_queries=G)
             log(f"[bench] prefill: chunk {chunk_ms:.3f} ms, scoring {kms:.3f} ms")
             del lays, csa4
             torch.cuda.empty_cache()

@@ -407,6 +407,10 @@ size_t      hca_struct_size(int which);
    attention only the shapes that decide the size are checked (the buffers may not
    exist yet); the other operations are validated like the call. */
 int         hca_workspace_bytes(int op, const void* desc, size_t* bytes);
+/* queries per group of the indexer call described by desc (only its shapes are
+   read): desc->Nq when the call runs as one group, else the size of each group but
+   the last, which holds the rest (see hca_indexer_topk_desc) */
+int         hca_indexer_query_group(const hca_indexer_topk_desc* desc, int32_t* group);
 
 int hca_kv_compress(const hca_kv_compress_desc* desc, void* stream);
 int hca_indexer_topk(const hca_indexer_topk_desc* desc, void* stream);

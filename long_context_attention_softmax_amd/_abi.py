@@ -21,7 +21,7 @@ MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
 OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE, OP_OUT_PROJ = 0, 1, 2, 3, 4, 5
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES, STRUCT_PROFILE_EVENTS = 100, 101, 102
 
-EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes",
+EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes", "hca_indexer_query_group",
            "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_attn_decode_noalloc",
            "hca_qkv_prologue",
            "hca_out_proj", "hca_profiled"]
@@ -117,6 +117,8 @@ def _load():
     lib.hca_struct_size.argtypes = [c_int]
     lib.hca_workspace_bytes.restype = c_int
     lib.hca_workspace_bytes.argtypes = [c_int, c_void_p, ctypes.POINTER(c_size_t)]
+    lib.hca_indexer_query_group.restype = c_int
+    lib.hca_indexer_query_group.argtypes = [c_void_p, ctypes.POINTER(c_int32)]
     for name, dt in [("hca_kv_compress", KvCompressDesc), ("hca_indexer_topk", IndexerTopkDesc),
                      ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc),
                      ("hca_attn_decode_noalloc", AttnDesc),
@@ -141,6 +143,12 @@ def new_desc(cls):
     d = cls()
     d.struct_size = ctypes.sizeof(cls)
     return d
+
+
+def indexer_query_group(desc) -> int:
+    g = c_int32(0)
+    check(lib.hca_indexer_query_group(ctypes.byref(desc), ctypes.byref(g)))
+    return g.value
 
 
 def workspace_bytes(op: int, desc) -> int:

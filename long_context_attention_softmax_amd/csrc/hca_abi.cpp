@@ -369,6 +369,16 @@ size_t hca_struct_size(int which) {
   }
 }
 
+int hca_indexer_query_group(const hca_indexer_topk_desc* d, int32_t* group) {
+  REQUIRE(group, HCA_E_NULL, "group is NULL");
+  *group = 0;
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_indexer_topk_desc), HCA_E_VERSION, "struct_size mismatch");
+  REQUIRE(d->Nq >= 0 && d->max_visible >= 0, HCA_E_SHAPE, "Nq and max_visible must be >= 0");
+  *group = hca::indexer_group(d->Nq, d->max_visible, d->q.fmt, d->k);
+  return HCA_OK;
+}
+
 int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
   REQUIRE(bytes, HCA_E_NULL, "bytes is NULL");
   *bytes = 0;

@@ -183,6 +183,15 @@ def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch
     A.check(A.lib.hca_kv_compress(ctypes.byref(d), _stream()))
 
 
+def hca_indexer_query_group(Nq: int, max_visible: int, fmt: int, k: int) -> int:
+    """Queries per group of an indexer call of these shapes (Nq when it runs as one
+    group; the last group holds the rest)."""
+    d = A.new_desc(A.IndexerTopkDesc)
+    d.Nq, d.k, d.max_visible = Nq, k, max_visible
+    d.q.fmt = d.keys.fmt = fmt
+    return A.indexer_query_group(d)
+
+
 def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: Optional[torch.Tensor],
                      seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
                      max_visible: int, idx: Optional[torch.Tensor] = None,

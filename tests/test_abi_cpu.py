@@ -457,3 +457,29 @@ def test_indexer_workspace_is_bounded_by_query_groups(fmt):
         assert 2 * 256 * row <= ws <= budget             # two groups of at least 256 queries
     # short prefixes: every query in one group, no split
     assert _idx_ws(4096, 4096, fmt) == pytest.approx(4096 * _idx_ws(1, 4096, fmt), rel=0.05)
+
+
+@pytest.mark.parametrize("fmt", [A.FP8_E4M3, A.MXFP4])
+def test_indexer_query_group_matches_the_workspace(fmt):
+    """hca_indexer_query_group names the group the workspace is sized for: the whole
+    call when it fits one group, else near-equal groups (multiples of 8, at least
+    256, the last holding the rest) whose two-group workspace is what
+    hca_workspace_bytes reports."""
+    def group(nq, vis):
+        d = idx_desc(Nq=nq, max_visible=vis)
+        d.q.fmt = d.keys.fmt = fmt
+        if fmt == A.MXFP4:
+            d.q.pitch = d.keys.pitch = 64
+        return A.indexer_query_group(d)
+    assert group(0, 263168) == 0
+    assert group(64, 263168) == 64
+    assert group(4096, 4096) == 4096                     # short prefix: one group
+    for nq in (1024, 4096, 16384):
+        g = group(nq, 263168)
+        assert 256 <= g < nq and g % 8 == 0
+        ng = -(-nq // g)
+        assert nq - (ng - 1) * g <= g                    # the last group holds the rest
+        assert ng * g - nq < 8 * ng                      # near-equal: at most 7 spare per group
+        assert _idx_ws(nq, 263168, fmt) == 2 * _idx_ws(g, 263168, fmt)
+    rc = A.lib.hca_indexer_query_group(None, ctypes.byref(ctypes.c_int32()))
+    assert rc == -1                                      # HCA_E_NULL

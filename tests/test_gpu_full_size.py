@@ -36,7 +36,7 @@ def test_full_size_decode_every_query(gpu, name, over, page_rows):
         _print(f"  rel err {err:.2e}")
 
 
-def _prefill_sample(nq, seed=7, n=128):
+def _prefill_sample(nq, group, seed=7, n=128):
     """At least ``n`` seeded queries of the chunk: the first and last query of every
     512-query block (the first and last 8-query group of each block at both ends),
     the eight queries the XCD-major scoring order spreads over the eight XCDs at
@@ -46,9 +46,8 @@ def _prefill_sample(nq, seed=7, n=128):
     for b0 in range(0, nq, 512):
         fixed += [b0, b0 + 7, b0 + 8, b0 + 504, b0 + 511]
     fixed += list(range(8)) + list(range(nq - 8, nq)) + [255, 256, 2047, 2048]
-    # both sides of each query-group boundary of the indexer at this size (the
-    # 4096-query call over a 1M prefix runs in ten groups of 416 queries)
-    for g0 in range(416, nq, 416):
+    # both sides of each query-group boundary of the indexer at this size
+    for g0 in range(group, nq, group):
         fixed += [g0 - 1, g0]
     got = set(q for q in fixed if 0 <= q < nq)
     rng = np.random.default_rng(seed)
@@ -60,11 +59,17 @@ def _prefill_sample(nq, seed=7, n=128):
 def test_full_size_prefill_sampled_queries(gpu):
     w = synth.make("csa_prefill_1m")
     csa, hca = w.layers
-    qs = _prefill_sample(len(csa.q_pos))
-    _print(f"csa_prefill_1m CSA layer (MXFP4 indexer) prefix={w.prefix} T={w.T} {len(qs)} queries: {qs}")
+    from long_context_attention_softmax_amd import _abi as A
+    from long_context_attention_softmax_amd.ops import hca_indexer_query_group
+    nq = len(csa.q_pos)
+    group = hca_indexer_query_group(nq, int(((csa.q_pos + 1) // csa.m).max()), A.MXFP4, w.g.topk)
+    assert 256 <= group < nq                             # the call runs in several groups
+    qs = _prefill_sample(nq, group)
+    _print(f"csa_prefill_1m CSA layer (MXFP4 indexer) prefix={w.prefix} T={w.T} group={group} "
+           f"{len(qs)} queries: {qs}")
     ref, dev, err = run_and_compare(csa, w.g, queries=qs, prefill=True, oracle_threads=16)
     _print(f"  rel err {err:.2e}")
-    qh = _prefill_sample(len(hca.q_pos), seed=8)
+    qh = _prefill_sample(len(hca.q_pos), group, seed=8)
     _print(f"csa_prefill_1m HCA layer {len(qh)} queries: {qh}")
     ref, dev, err = run_and_compare(hca, w.g, queries=qh, prefill=True, oracle_threads=16)
     _print(f"  rel err {err:.2e}")
