@@ -23,8 +23,12 @@
  *     (a hipStream_t passed as void*; NULL = the default stream).
  *   - Every buffer pointer inside a descriptor is a DEVICE pointer owned by the
  *     caller; rows are addressed with explicit pitches in BYTES.  The library
- *     allocates nothing, frees nothing, never synchronizes and keeps no state
- *     between calls other than the thread-local error message.
+ *     allocates no device memory, frees nothing and never waits on the host.  It
+ *     keeps no state between calls other than the thread-local error message and
+ *     two things made once per device and held until the process ends: the
+ *     second stream and events of an indexer call that runs in query groups
+ *     (hca_indexer_topk), and the static scratch array of
+ *     hca_attn_decode_noalloc.
  *   - Scratch memory comes from a caller-owned workspace of at least
  *     hca_workspace_bytes() bytes, 256-byte aligned; its contents on entry do not
  *     matter (the library clears what it needs).  Calls that share one workspace
