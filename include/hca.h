@@ -25,10 +25,10 @@
  *     caller; rows are addressed with explicit pitches in BYTES.  The library
  *     allocates no device memory, frees nothing and never waits on the host.  It
  *     keeps no state between calls other than the thread-local error message and
- *     two things made once per device and held until the process ends: the
- *     second stream and events of an indexer call that runs in query groups
- *     (hca_indexer_topk), and the static scratch array of
- *     hca_attn_decode_noalloc.
+ *     two things made on first use and held until the process ends: the second
+ *     stream and events of indexer calls that run in query groups
+ *     (hca_indexer_topk; one set per device and caller stream), and the static
+ *     scratch array of hca_attn_decode_noalloc (one per device).
  *   - Scratch memory comes from a caller-owned workspace of at least
  *     hca_workspace_bytes() bytes, 256-byte aligned; its contents on entry do not
  *     matter (the library clears what it needs).  Calls that share one workspace
@@ -196,7 +196,8 @@ typedef struct hca_kv_compress_desc {
  * 75 KB per query).  A call whose whole workspace would exceed 896 MiB runs in
  * near-equal query groups (a multiple of 8 queries, at least 256) and keeps two
  * groups: group g is scored on `stream` while the selection of group g - 1 runs
- * on a second stream the library creates once per device (default priority),
+ * on a second stream the library creates once per device and caller stream
+ * (default priority),
  * joined back to `stream` through events before the call returns, so work queued
  * on `stream` afterwards sees every result.  The workspace stays within 896 MiB
  * whatever Nq (at least two groups of 256 queries' worth), and the results are

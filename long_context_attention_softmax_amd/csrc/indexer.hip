@@ -26,7 +26,9 @@
 //
 // Selection: exact radix select on the orderable 32-bit key of each score, lower
 // index first among equal scores, output in ascending index order.
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "device_common.hpp"
 #include "hca_internal.hpp"
@@ -1309,31 +1311,39 @@ void launch_select_phase(const GroupPlan& p, hipStream_t s) {
   if (!L.merged) hipLaunchKernelGGL(select_emit_kernel, cgrid, dim3(256), 0, s, a, sw);
 }
 
-// Per device, created on first use: the stream the select phases of a grouped call
-// run on (default priority), and one "scored" and one "selected" event per
-// workspace half.
-constexpr int kMaxDev = 64;
+// Per (device, caller stream), created on first use and kept until the process
+// ends: the stream the select phases of a grouped call run on (default priority),
+// and one "scored" and one "selected" event per workspace half.  Calls on one
+// caller stream are ordered, so they can share these; calls on different caller
+// streams get their own, so their event records never interleave.
 struct AuxStreams {
   hipStream_t st = nullptr;
   hipEvent_t scored[2] = {nullptr, nullptr}, selected[2] = {nullptr, nullptr}, start = nullptr;
 };
 std::mutex g_aux_mu;
-AuxStreams g_aux[kMaxDev];
+std::map<std::pair<int, hipStream_t>, AuxStreams> g_aux;   // node-based: entries never move
 
-hipError_t aux_streams(AuxStreams** out) {
+hipError_t aux_streams(hipStream_t caller, AuxStreams** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_aux_mu);
-  AuxStreams& x = g_aux[dev];
-  if (!x.st) {
-    if ((e = hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking)) != hipSuccess) return e;
-    for (int h = 0; h < 2; ++h) {
-      if ((e = hipEventCreateWithFlags(&x.scored[h], hipEventDisableTiming)) != hipSuccess) return e;
-      if ((e = hipEventCreateWithFlags(&x.selected[h], hipEventDisableTiming)) != hipSuccess) return e;
+  AuxStreams& x = g_aux[std::make_pair(dev, caller)];
+  if (!x.st) {                                           // all made, or none kept
+    AuxStreams y;
+    e = hipStreamCreateWithFlags(&y.st, hipStreamNonBlocking);
+    for (int h = 0; h < 2 && e == hipSuccess; ++h) {
+      e = hipEventCreateWithFlags(&y.scored[h], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&y.selected[h], hipEventDisableTiming);
     }
-    if ((e = hipEventCreateWithFlags(&x.start, hipEventDisableTiming)) != hipSuccess) return e;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&y.start, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (hipEvent_t ev : {y.scored[0], y.scored[1], y.selected[0], y.selected[1], y.start})
+        if (ev) (void)hipEventDestroy(ev);
+      if (y.st) (void)hipStreamDestroy(y.st);
+      return e;
+    }
+    x = y;
   }
   *out = &x;
   return hipSuccess;
@@ -1393,7 +1403,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
     return hipGetLastError();
   }
   AuxStreams* x = nullptr;
-  hipError_t e = aux_streams(&x);
+  hipError_t e = aux_streams(s, &x);
   if (e != hipSuccess) return e;
   const size_t half = ws_layout(G, a0.max_visible, a0.fmt, a0.k).total;
   // the second stream starts after everything the caller enqueued before this call
