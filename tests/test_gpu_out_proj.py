@@ -34,9 +34,10 @@ def _dev(bits, gpu):
 
 
 # (rows, units per group): up to 64 rows the K-split kernel; more rows with units a
-# multiple of 128 the tiled kernel (ragged last row tile included)
+# multiple of 128 the 128-wide tiled kernel, more than 128 rows with units a multiple
+# of 256 the 256-wide one (ragged last row tiles included)
 @pytest.mark.parametrize("Nq,d_g", [(1, 64), (5, 64), (32, 64), (33, 64), (100, 64), (65, 128), (100, 128),
-                                    (300, 256)])
+                                    (300, 128), (128, 256), (129, 256), (300, 256), (600, 512)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_out_proj_parity(gpu, Nq, d_g, out):
     from long_context_attention_softmax_amd.ops import hca_out_proj
@@ -54,7 +55,7 @@ def test_out_proj_parity(gpu, Nq, d_g, out):
 
 def test_out_proj_full_size_sampled(gpu):
     """The prefill-chunk size (4096 rows, G = 8 groups of 1024 outputs): every row
-    is computed, 64 seeded rows (first and last of the 64-row tiles included) are
+    is computed, 66 rows (rows on both sides of the 64- and 256-row tile edges included) are
     checked against the oracle; the decode size (32 rows) in full."""
     from long_context_attention_softmax_amd.ops import hca_out_proj
     d_g = 1024
@@ -63,7 +64,7 @@ def test_out_proj_full_size_sampled(gpu):
         y = hca_out_proj(_dev(o, gpu), _dev(w, gpu), G=G)
         torch.cuda.synchronize()
         rows = np.arange(Nq) if Nq <= 64 else np.unique(np.concatenate(
-            [[0, 63, 64, Nq - 1], np.random.default_rng(9).choice(Nq, 60, replace=False)]))
+            [[0, 63, 64, 255, 256, Nq - 1], np.random.default_rng(9).choice(Nq, 60, replace=False)]))
         ref = project.grouped_out_proj(quant.bf16_decode(o[rows]), quant.bf16_decode(w))
         got = to_np(y)[rows].astype(np.float64)
         err = row_rel_err(got.reshape(len(rows), -1), ref.reshape(len(rows), -1))
