@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 6
+#define HCA_ABI_VERSION 7
 
 /* status codes */
 #define HCA_OK             0
@@ -88,6 +88,7 @@ extern "C" {
 #define HCA_OP_ATTN_PREFILL 3
 #define HCA_OP_QKV_PROLOGUE 4
 #define HCA_OP_OUT_PROJ     5
+#define HCA_OP_DECODE_LAYER 6
 #define HCA_STRUCT_KV_PLANES  100
 #define HCA_STRUCT_IDX_PLANES 101
 
@@ -387,13 +388,52 @@ typedef struct hca_out_proj_desc {
 } hca_out_proj_desc;
 
 /*
+ * hca_decode_layer: one decode step of one layer, the three calls above in one:
+ * pooling of the blocks that the step's new tokens complete (`pool`; NULL or
+ * n_blocks = 0: nothing to pool), then, for a CSA layer (attn->mode ==
+ * HCA_MODE_CSA), the indexer top-k (`indexer`, required there and NULL otherwise;
+ * attention reads the idx it writes), then decode attention (`attn`).  The results
+ * are bit for bit those of hca_kv_compress, hca_indexer_topk and hca_attn_decode
+ * called in that order on `stream`.  "DeepSeek V4 infrastructure" (volanea.com),
+ * "MegaMoE targets the real bottleneck in sparse models", counts the idle time
+ * between kernel launches as a cost of its own: here the pooling needs no launch of
+ * its own where the launch plan allows, and workgroups that do not read a new entry
+ * never wait for it.
+ *
+ * Decode precondition: a pooled block's entry is the newest entry that the queries
+ * of its sequence see (entry floor((t + 1) / m) - 1 for a query at t; in decode the
+ * token at t completes that block exactly when (t + 1) mod m = 0).  Pooling any
+ * other entry that a query of this call reads leaves its scores and output
+ * undefined (every access stays inside the buffers: no fault, no hang).
+ * Under it, a CSA step with FP8 keys (or MXFP4 keys and fewer than 256 queries)
+ * whose blocks hold at most 16 BF16 rows of 512 dims with an index stream pools
+ * inside the scoring launch: the pooling workgroups lead the grid, and only the
+ * workgroup that scores a query's newest entry waits for them, inside the device
+ * and for a bounded time.  Any other combination launches the pooling first.
+ *
+ * The descriptors are validated as their own calls validate them, before any
+ * launch, and must agree: m of each equal to attn->m; for CSA, indexer->Nq, k and
+ * idx equal to attn's.  The indexer and attention keep their own workspaces;
+ * hca_workspace_bytes(HCA_OP_DECODE_LAYER, ...) gives 0.
+ */
+typedef struct hca_decode_layer_desc {
+  uint32_t struct_size;
+  int32_t  reserved;
+  const hca_kv_compress_desc*  pool;      /* optional */
+  const hca_indexer_topk_desc* indexer;   /* CSA only */
+  const hca_attn_desc*         attn;      /* required */
+} hca_decode_layer_desc;
+
+/*
  * Timing hook for benchmarks (not part of the computation): hca_profiled runs the
  * call (op, desc) exactly as its own entry point does and records the event `begin`
  * on the stream immediately before, and `end` immediately after, that call's main
  * kernel: the scoring kernel of HCA_OP_INDEXER_TOPK (top-k selection excluded; of
  * the first query group when the call runs in several), the
  * attention kernel of HCA_OP_ATTN_DECODE / HCA_OP_ATTN_PREFILL (the combine of split
- * decode queries excluded).  begin and end are hipEvent_t values passed as void*
+ * decode queries excluded), and of HCA_OP_DECODE_LAYER the scoring launch of a CSA
+ * layer (with the pooling when it rides there) or the attention kernel of an HCA or
+ * sliding-window layer.  begin and end are hipEvent_t values passed as void*
  * (either may be NULL).  Other ops: HCA_E_UNSUPPORTED.
  */
 typedef struct hca_profile_events {
@@ -439,6 +479,7 @@ int hca_attn_prefill(const hca_attn_desc* desc, void* stream);
 int hca_attn_decode_noalloc(const hca_attn_desc* desc, void* stream);
 int hca_qkv_prologue(const hca_qkv_prologue_desc* desc, void* stream);
 int hca_out_proj(const hca_out_proj_desc* desc, void* stream);
+int hca_decode_layer(const hca_decode_layer_desc* desc, void* stream);
 int hca_profiled(int op, const void* desc, const hca_profile_events* events, void* stream);
 
 #ifdef __cplusplus

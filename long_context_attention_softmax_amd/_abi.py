@@ -19,12 +19,13 @@ ERRORS = {-1: "HCA_E_NULL", -2: "HCA_E_SHAPE", -3: "HCA_E_ALIGN", -4: "HCA_E_DTY
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 MODE_CSA, MODE_HCA, MODE_SWA = 0, 1, 2
 OP_KV_COMPRESS, OP_INDEXER_TOPK, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_QKV_PROLOGUE, OP_OUT_PROJ = 0, 1, 2, 3, 4, 5
+OP_DECODE_LAYER = 6
 STRUCT_KV_PLANES, STRUCT_IDX_PLANES, STRUCT_PROFILE_EVENTS = 100, 101, 102
 
 EXPORTS = ["hca_abi_version", "hca_last_error", "hca_struct_size", "hca_workspace_bytes", "hca_indexer_query_group",
            "hca_kv_compress", "hca_indexer_topk", "hca_attn_decode", "hca_attn_prefill", "hca_attn_decode_noalloc",
            "hca_qkv_prologue",
-           "hca_out_proj", "hca_profiled"]
+           "hca_out_proj", "hca_decode_layer", "hca_profiled"]
 
 
 class KvPlanes(ctypes.Structure):
@@ -76,6 +77,12 @@ class AttnDesc(ctypes.Structure):
                 ("split_chunks", c_int32)]
 
 
+class DecodeLayerDesc(ctypes.Structure):
+    _fields_ = [("struct_size", c_uint32), ("reserved", c_int32),
+                ("pool", ctypes.POINTER(KvCompressDesc)), ("indexer", ctypes.POINTER(IndexerTopkDesc)),
+                ("attn", ctypes.POINTER(AttnDesc))]
+
+
 class QkvPrologueDesc(ctypes.Structure):
     _fields_ = [("struct_size", c_uint32), ("io_fmt", c_int32), ("Nq", c_int32), ("H", c_int32),
                 ("D", c_int32), ("Nt", c_int32), ("B", c_int32), ("W_cap", c_int32), ("d_I", c_int32),
@@ -122,7 +129,8 @@ def _load():
     for name, dt in [("hca_kv_compress", KvCompressDesc), ("hca_indexer_topk", IndexerTopkDesc),
                      ("hca_attn_decode", AttnDesc), ("hca_attn_prefill", AttnDesc),
                      ("hca_attn_decode_noalloc", AttnDesc),
-                     ("hca_qkv_prologue", QkvPrologueDesc), ("hca_out_proj", OutProjDesc)]:
+                     ("hca_qkv_prologue", QkvPrologueDesc), ("hca_out_proj", OutProjDesc),
+                     ("hca_decode_layer", DecodeLayerDesc)]:
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [ctypes.POINTER(dt), c_void_p]

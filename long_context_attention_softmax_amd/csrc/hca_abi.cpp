@@ -316,12 +316,13 @@ int validate_prologue(const hca_qkv_prologue_desc* d) {
   return HCA_OK;
 }
 
-int attn_call(const hca_attn_desc* d, void* stream, int prefill, const hca_profile_events* ev = nullptr) {
+// validate an attention call and fill its launch arguments (a.Nq = 0: nothing to launch)
+int build_attn(const hca_attn_desc* d, int prefill, const hca_profile_events* ev, hca::AttnArgs& a) {
   size_t ws = 0;
   int rc = validate_attn(d, prefill, &ws);
   if (rc) return rc;
+  a = hca::AttnArgs{};
   if (d->Nq == 0) return HCA_OK;
-  hca::AttnArgs a{};
   const bool swa = d->mode == HCA_MODE_SWA;   // runs as HCA with no visible entry: no cache read
   a.Nq = d->Nq; a.H = d->H; a.D = d->D; a.D_r = d->D_r; a.mode = swa ? HCA_MODE_HCA : d->mode;
   a.m = swa ? 1 : d->m;
@@ -343,6 +344,13 @@ int attn_call(const hca_attn_desc* d, void* stream, int prefill, const hca_profi
   a.split_chunks = prefill || a.io_f32 ? 0 : d->split_chunks;
   a.split_runs = (int)hca::attention_split_runs(a.mode, a.k, a.n_win, a.max_visible, a.split_chunks);
   if (ev) { a.prof_begin = static_cast<hipEvent_t>(ev->begin); a.prof_end = static_cast<hipEvent_t>(ev->end); }
+  return HCA_OK;
+}
+
+int attn_call(const hca_attn_desc* d, void* stream, int prefill, const hca_profile_events* ev = nullptr) {
+  hca::AttnArgs a;
+  const int rc = build_attn(d, prefill, ev, a);
+  if (rc || a.Nq == 0) return rc;
   return launched(hca::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -362,6 +370,7 @@ size_t hca_struct_size(int which) {
     case HCA_OP_ATTN_PREFILL: return sizeof(hca_attn_desc);
     case HCA_OP_QKV_PROLOGUE: return sizeof(hca_qkv_prologue_desc);
     case HCA_OP_OUT_PROJ: return sizeof(hca_out_proj_desc);
+    case HCA_OP_DECODE_LAYER: return sizeof(hca_decode_layer_desc);
     case HCA_STRUCT_KV_PLANES: return sizeof(hca_kv_planes);
     case HCA_STRUCT_IDX_PLANES: return sizeof(hca_idx_planes);
     case HCA_STRUCT_PROFILE_EVENTS: return sizeof(hca_profile_events);
@@ -418,6 +427,14 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
       rc = validate_out_proj(static_cast<const hca_out_proj_desc*>(desc));
       ws = 0;
       break;
+    case HCA_OP_DECODE_LAYER: {           // the indexer and attention keep their own workspaces
+      const hca_decode_layer_desc* d = static_cast<const hca_decode_layer_desc*>(desc);
+      REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+      REQUIRE(d->struct_size == sizeof(hca_decode_layer_desc), HCA_E_VERSION, "struct_size mismatch");
+      rc = HCA_OK;
+      ws = 0;
+      break;
+    }
     default: return fail(HCA_E_SHAPE, "unknown op %d", op);
   }
   if (rc) return rc;
@@ -425,11 +442,13 @@ int hca_workspace_bytes(int op, const void* desc, size_t* bytes) {
   return HCA_OK;
 }
 
-int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
+namespace {
+// validate a pooling call and fill its launch arguments (a.n_blocks = 0: nothing to launch)
+int build_pool(const hca_kv_compress_desc* d, hca::PoolArgs& a) {
   int rc = validate_kv_compress(d);
   if (rc) return rc;
+  a = hca::PoolArgs{};
   if (d->n_blocks == 0) return HCA_OK;
-  hca::PoolArgs a{};
   a.m = d->m; a.D = d->D; a.D_r = d->D_r; a.d_I = d->raw_idx ? d->d_I : 0; a.n_blocks = d->n_blocks;
   a.rope_base = d->rope_base; a.raw_is_f32 = d->raw_fmt == HCA_F32;
   if (d->D_r / 2 <= 64)
@@ -446,16 +465,25 @@ int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
   a.out_idx = static_cast<char*>(d->out_idx.data); a.idx_pitch = d->out_idx.pitch;
   a.out_idx_scales = static_cast<char*>(d->out_idx.scales); a.idx_scale_pitch = d->out_idx.scale_pitch;
   a.debug = d->debug;
+  return HCA_OK;
+}
+}  // namespace
+
+int hca_kv_compress(const hca_kv_compress_desc* d, void* stream) {
+  hca::PoolArgs a;
+  const int rc = build_pool(d, a);
+  if (rc || a.n_blocks == 0) return rc;
   return launched(hca::launch_pool(a, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
-int indexer_call(const hca_indexer_topk_desc* d, void* stream, const hca_profile_events* ev) {
+// validate an indexer call and fill its launch arguments (a.Nq = 0: nothing to launch)
+int build_indexer(const hca_indexer_topk_desc* d, const hca_profile_events* ev, hca::IndexerArgs& a) {
   size_t ws = 0;
   int rc = validate_indexer(d, &ws);
   if (rc) return rc;
+  a = hca::IndexerArgs{};
   if (d->Nq == 0) return HCA_OK;
-  hca::IndexerArgs a{};
   a.Nq = d->Nq; a.H_I = d->H_I; a.d_I = d->d_I; a.k = d->k; a.m = d->m; a.fmt = d->q.fmt;
   a.max_visible = d->max_visible;
   a.score_pitch = (d->max_visible + 63) / 64 * 64;
@@ -471,7 +499,53 @@ int indexer_call(const hca_indexer_topk_desc* d, void* stream, const hca_profile
   a.scores = d->workspace;             // the workspace layout is laid out by the launcher
   a.hist = nullptr;
   if (ev) { a.prof_begin = static_cast<hipEvent_t>(ev->begin); a.prof_end = static_cast<hipEvent_t>(ev->end); }
+  return HCA_OK;
+}
+
+int indexer_call(const hca_indexer_topk_desc* d, void* stream, const hca_profile_events* ev) {
+  hca::IndexerArgs a;
+  const int rc = build_indexer(d, ev, a);
+  if (rc || a.Nq == 0) return rc;
   return launched(hca::launch_indexer_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- decode layer step
+int decode_layer_call(const hca_decode_layer_desc* d, void* stream, const hca_profile_events* ev) {
+  REQUIRE(d, HCA_E_NULL, "descriptor is NULL");
+  REQUIRE(d->struct_size == sizeof(hca_decode_layer_desc), HCA_E_VERSION,
+          "struct_size %u != %zu", d->struct_size, sizeof(hca_decode_layer_desc));
+  REQUIRE(d->attn, HCA_E_NULL, "attn is NULL");
+  const bool csa = d->attn->mode == HCA_MODE_CSA;
+  REQUIRE(csa == (d->indexer != nullptr), HCA_E_SHAPE, "indexer is required for a CSA layer and only there");
+  hca::PoolArgs pa{};
+  if (d->pool) {
+    const int rc = build_pool(d->pool, pa);
+    if (rc) return rc;
+    REQUIRE(pa.n_blocks == 0 || d->pool->m == d->attn->m, HCA_E_SHAPE, "pool m %d != attn m %d",
+            d->pool->m, d->attn->m);
+  }
+  hca::IndexerArgs ia{};
+  if (csa) {
+    const int rc = build_indexer(d->indexer, ev, ia);
+    if (rc) return rc;
+    REQUIRE(d->indexer->m == d->attn->m && d->indexer->Nq == d->attn->Nq && d->indexer->k == d->attn->k &&
+            d->indexer->idx == d->attn->idx, HCA_E_SHAPE, "indexer and attn disagree on m, Nq, k or idx");
+  }
+  hca::AttnArgs aa;
+  {
+    const int rc = build_attn(d->attn, 0, csa ? nullptr : ev, aa);
+    if (rc) return rc;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hca::PoolArgs* pool = pa.n_blocks > 0 ? &pa : nullptr;
+  hipError_t e = hipSuccess;
+  if (csa) {
+    e = hca::launch_indexer_topk(ia, s, pool);           // pools inside the scoring launch where it can
+  } else if (pool) {
+    e = hca::launch_pool(pa, s);
+  }
+  if (e == hipSuccess && aa.Nq > 0) e = hca::launch_attention(aa, s);
+  return launched(e);
 }
 }  // namespace
 
@@ -485,11 +559,14 @@ int hca_profiled(int op, const void* desc, const hca_profile_events* ev, void* s
     case HCA_OP_INDEXER_TOPK: return indexer_call(static_cast<const hca_indexer_topk_desc*>(desc), stream, ev);
     case HCA_OP_ATTN_DECODE: return attn_call(static_cast<const hca_attn_desc*>(desc), stream, 0, ev);
     case HCA_OP_ATTN_PREFILL: return attn_call(static_cast<const hca_attn_desc*>(desc), stream, 1, ev);
+    case HCA_OP_DECODE_LAYER: return decode_layer_call(static_cast<const hca_decode_layer_desc*>(desc), stream, ev);
     default: return fail(HCA_E_UNSUPPORTED, "op %d has no profiled form", op);
   }
 }
 
 int hca_attn_decode(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 0); }
+
+int hca_decode_layer(const hca_decode_layer_desc* d, void* stream) { return decode_layer_call(d, stream, nullptr); }
 
 int hca_attn_prefill(const hca_attn_desc* d, void* stream) { return attn_call(d, stream, 1); }
 

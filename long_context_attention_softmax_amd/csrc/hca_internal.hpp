@@ -48,8 +48,16 @@ struct IndexerArgs {
   hipEvent_t prof_begin, prof_end;    // optional, around the scoring kernel
   const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged keys (page_shift >= 0)
   int many;                           // set per group of a grouped call: the many-query plan
+  // fused decode pooling: grid rows y < pool_rows pool the step's blocks and count
+  // themselves in *pool_done; a workgroup that reads its query's newest entry waits
+  // for pool_target counts first (0: no pooling in this launch)
+  int pool_rows, pool_target;
+  uint32_t* pool_done;
 };
-hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
+// pool (optional, decode): blocks to pool before the scores are formed, in the same
+// call; fused into the scoring launch where the launch plan allows, else launched first
+hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s, const PoolArgs* pool = nullptr);
+bool pool_fast_path(const PoolArgs& a);
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k);
 // queries per launch group of a call with Nq queries (its workspace holds one group)
 int indexer_group(int Nq, int64_t max_visible, int fmt, int k);

@@ -33,6 +33,7 @@
 #include "device_common.hpp"
 #include "hca_internal.hpp"
 #include "../../include/hca.h"
+#include "pool_block.hpp"
 
 namespace hca {
 
@@ -44,6 +45,16 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSmallV = 4096;
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Device-coherent word access (relaxed, device scope): what one workgroup stores
+// this way is seen by another's loads once the store has completed, with no cache
+// write-back or invalidation (those make a device-scope fence cost microseconds).
+__device__ __forceinline__ uint32_t ld_dev(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ int64_t visible(const IndexerArgs& a, int n) {
   int64_t v = (a.q_pos[n] + 1) / a.m;
@@ -245,19 +256,55 @@ __device__ __forceinline__ float head_sum(const v16f (&acc)[2], const float (&wv
 #endif
 // TPW: 32-entry tiles per wave (1024 entries per workgroup at 8).  PAGED: key rows
 // come through the page table, one page per 32-entry tile.
-template <int FMT, bool XQ, int HT, int TPW, bool PAGED>
-__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
-score_quant_kernel(IndexerArgs a) {
+// POOL (decode, chunk-major): the grid's leading pool_rows rows pool the step's
+// blocks (the block's tokens complete its sequence's newest entry) and count
+// themselves; the one workgroup per query whose range holds that query's newest
+// entry V - 1 waits for every count before it loads a key.  The pooling workgroups
+// lead the dispatch order, so they are running whenever a workgroup waits; the wait
+// is bounded all the same.
+typedef PoolSmem<kScoreThreads, 4, true> ScorePoolSmem;     // blocks of m <= 16 tokens
+constexpr uint32_t kPoolSpinMax = 1u << 22;
+
+template <int FMT, bool XQ, int HT, int TPW, bool PAGED, bool POOL>
+__device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const PoolArgs& pool) {
 #pragma clang fp contract(off)
   // scores staged in LDS and written once per wave (whole 16-byte groups per lane)
   constexpr bool kStage = TPW <= 16 && (32 * TPW) % 256 == 0;
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ v8bf s_qa[2][8][64];                        // FP8 path: widened query operands, per lane
-  __shared__ __attribute__((aligned(16))) float s_st[kStage ? kScoreThreads / 64 : 1][kStage ? 32 * TPW : 4];
+  constexpr int kQa = FMT == HCA_FP8_E4M3 ? 8 : 1;       // MXFP4 keeps its query operands in registers
+  struct Lds {
+    uint32_t hist[kBins];
+    v8bf qa[2][kQa][64];                                 // FP8 path: widened query operands, per lane
+    float st[kStage ? kScoreThreads / 64 : 1][kStage ? 32 * TPW : 4];
+  };
+  union Shared {
+    Lds s;
+    char pool[POOL ? sizeof(ScorePoolSmem) : 1];         // a pooling workgroup's LDS
+  };
+  __shared__ __attribute__((aligned(16))) Shared sh;
+  uint32_t* const s_hist = sh.s.hist;
+  v8bf (*const s_qa)[kQa][64] = sh.s.qa;
+  float (*const s_st)[kStage ? 32 * TPW : 4] = sh.s.st;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, u = lane >> 5;
   int n;
   int64_t chunk;
+  if constexpr (POOL) {
+    if ((int)blockIdx.y < a.pool_rows) {
+      const int nb = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+      if (nb < pool.n_blocks) {
+        pool_d512_block<kScoreThreads, 4, true>(pool, nb, *reinterpret_cast<ScorePoolSmem*>(sh.pool));
+        // every thread's stores complete, then the XCD's cache is written back before
+        // the count is raised
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          atomicAdd(a.pool_done, 1u);
+        }
+      }
+      return;                                           // uniform over the workgroup
+    }
+  }
   if (XQ) {
     const int64_t L = blockIdx.x, r = L >> 3;
     const int64_t nper = ((int64_t)a.Nq + 7) >> 3;
@@ -265,7 +312,7 @@ score_quant_kernel(IndexerArgs a) {
     chunk = r / nper;
     if (n >= a.Nq) return;                              // uniform over the workgroup
   } else {
-    n = blockIdx.y;
+    n = (int)blockIdx.y - (POOL ? a.pool_rows : 0);
     chunk = blockIdx.x;
   }
   const int64_t V = visible(a, n);
@@ -358,6 +405,16 @@ score_quant_kernel(IndexerArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (POOL) {
+    if (V - 1 < ebase + entries_per_wg_t(TPW)) {         // uniform: this range holds entry V - 1
+      if (tid == 0) {
+        for (uint32_t it = 0; ld_dev(a.pool_done) < (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
+          __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale copy of the new rows is read
+      }
+      __syncthreads();
+    }
+  }
 #pragma unroll
   for (int t = 0; t < kRing; ++t) {
     if (t < kTilesPerWave) load_tile(t, kr[t], ks[t]);
@@ -461,6 +518,20 @@ score_quant_kernel(IndexerArgs a) {
     uint32_t c = s_hist[i];
     if (c) atomicAdd(&gh[i], c);
   }
+}
+
+template <int FMT, bool XQ, int HT, int TPW, bool PAGED>
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
+score_quant_kernel(IndexerArgs a) {
+  const PoolArgs none{};
+  score_quant_body<FMT, XQ, HT, TPW, PAGED, false>(a, none);
+}
+
+// the same scoring with the step's pooling in the leading grid rows (decode)
+template <int FMT, int HT, int TPW, bool PAGED>
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
+score_pool_kernel(IndexerArgs a, PoolArgs p) {
+  score_quant_body<FMT, false, HT, TPW, PAGED, true>(a, p);
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(uint4* p, int64_t n16) {
@@ -697,15 +768,6 @@ __device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
   return base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
 }
 
-// Device-coherent word access (relaxed, device scope): what one workgroup stores
-// this way is seen by another's loads once the store has completed, with no cache
-// write-back or invalidation (those make a device-scope fence cost microseconds).
-__device__ __forceinline__ uint32_t ld_dev(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ float key_float(uint32_t k) {        // inverse of float_key (no -0 arises)
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -1200,7 +1262,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
   if (fmt == HCA_F32) return L;
   L.nch = (int)((max_visible + kChunk1 - 1) / kChunk1);
   if (L.nch < 1) L.nch = 1;
-  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 3) * 4);        // histogram; candidate, above and done counts
+  L.hist = o;  o = up(o + (size_t)Nq * (kBins + 3) * 4 + 4);    // histogram; candidate, above, done counts; pooling count
   L.cand_key = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.cand_idx = o; o = up(o + (size_t)Nq * kCandCap2 * 4);
   L.chunk_gt = o; o = up(o + (size_t)Nq * L.nch * 4);
@@ -1219,8 +1281,21 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
 
 // one scoring launch; the head-tile count (H_I / 32) and paging are template arguments
 template <int FMT, bool XQ, int TPW>
-void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s, const PoolArgs* pool = nullptr) {
   const bool h2 = a.H_I == 64;
+  if constexpr (!XQ) {
+    if (pool) {                                          // grid rows [0, pool_rows) pool
+      const dim3 gp(grid.x, grid.y + (unsigned)a.pool_rows);
+      if (a.page_shift >= 0) {
+        if (h2) hipLaunchKernelGGL((score_pool_kernel<FMT, 2, TPW, true>), gp, dim3(kScoreThreads), 0, s, a, *pool);
+        else hipLaunchKernelGGL((score_pool_kernel<FMT, 1, TPW, true>), gp, dim3(kScoreThreads), 0, s, a, *pool);
+      } else {
+        if (h2) hipLaunchKernelGGL((score_pool_kernel<FMT, 2, TPW, false>), gp, dim3(kScoreThreads), 0, s, a, *pool);
+        else hipLaunchKernelGGL((score_pool_kernel<FMT, 1, TPW, false>), gp, dim3(kScoreThreads), 0, s, a, *pool);
+      }
+      return;
+    }
+  }
   if (a.page_shift >= 0) {
     if (h2) hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 2, TPW, true>), grid, dim3(kScoreThreads), 0, s, a);
     else hipLaunchKernelGGL((score_quant_kernel<FMT, XQ, 1, TPW, true>), grid, dim3(kScoreThreads), 0, s, a);
@@ -1254,6 +1329,7 @@ GroupPlan plan_group(const IndexerArgs& a0) {
   sw.cand_count = a.hist + (int64_t)a.Nq * kBins;
   sw.above_count = sw.cand_count + a.Nq;
   sw.done = sw.above_count + a.Nq;
+  a.pool_done = sw.done + a.Nq;                          // cleared with the histogram
   sw.above_key = L.merged ? reinterpret_cast<uint32_t*>(wsb + L.above_key) : nullptr;
   sw.above_idx = L.merged ? reinterpret_cast<int32_t*>(wsb + L.above_idx) : nullptr;
   sw.cand_key = reinterpret_cast<uint32_t*>(wsb + L.cand_key);
@@ -1266,12 +1342,14 @@ GroupPlan plan_group(const IndexerArgs& a0) {
   return p;
 }
 
-void launch_score_phase(const GroupPlan& p, hipStream_t s) {
+// pool: the step's pooling, fused into this scoring launch (pool_fusable)
+void launch_score_phase(const GroupPlan& p, hipStream_t s, const PoolArgs* pool = nullptr) {
   const IndexerArgs& a = p.a;
   {
     // the scoring kernel histograms the first digit and the collect phase counts
-    // candidates and keys above the first digit: clear them first (they are adjacent)
-    const int64_t n16 = ((int64_t)a.Nq * (kBins + 3) * 4 + 15) / 16;
+    // candidates and keys above the first digit: clear them first (they are adjacent,
+    // and so is the fused pooling's count)
+    const int64_t n16 = ((int64_t)a.Nq * (kBins + 3) * 4 + 4 + 15) / 16;
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(a.hist), n16);
   }
@@ -1284,8 +1362,8 @@ void launch_score_phase(const GroupPlan& p, hipStream_t s) {
   if (chunks > 0) {
     const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
     constexpr int T8 = HCA_SCORE_TPW, T4 = HCA_SCORE_TPW4, T4D = HCA_SCORE_TPW4D;
-    if (a.fmt == HCA_FP8_E4M3) launch_score<HCA_FP8_E4M3, false, T8>(a, g2, s);
-    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s);
+    if (a.fmt == HCA_FP8_E4M3) launch_score<HCA_FP8_E4M3, false, T8>(a, g2, s, pool);
+    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s, pool);
     else if (HCA_SCORE_XCD_MAJOR) launch_score<HCA_MXFP4, true, T4>(a, gx, s);
     else launch_score<HCA_MXFP4, false, T4>(a, g2, s);
   }
@@ -1382,7 +1460,29 @@ size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
   return G < Nq ? 2 * half : half;
 }
 
-hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
+namespace {
+// tiles per wave of the chunk-major scoring launch a decode call takes
+int kFusedTpw(const IndexerArgs& a) { return a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : HCA_SCORE_TPW4D; }
+
+// The step's pooling can ride in the scoring launch: one query group scored chunk-major
+// (FP8, or MXFP4 with few queries), blocks of at most 16 BF16 rows of 512 dims with an
+// index stream (the fast pooling path at 256 threads), and at least one key to score.
+bool pool_fusable(const IndexerArgs& a, const PoolArgs& p) {
+  if (a.fmt == HCA_F32 || a.max_visible <= 0) return false;
+  if (indexer_group(a.Nq, a.max_visible, a.fmt, a.k) < a.Nq) return false;
+  const bool many = a.Nq >= kDigitMinQ || a.many;
+  if (a.fmt == HCA_MXFP4 && (a.Nq >= kFewQ || many)) return false;
+  return pool_fast_path(p) && p.m <= 16 && p.idx_fmt >= 0;
+}
+}  // namespace
+
+hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s, const PoolArgs* pool) {
+  if (pool && pool->n_blocks == 0) pool = nullptr;
+  if (pool && (a0.Nq == 0 || !pool_fusable(a0, *pool))) {   // pooled by its own launch, first
+    const hipError_t e = launch_pool(*pool, s);
+    if (e != hipSuccess) return e;
+    pool = nullptr;
+  }
   if (a0.Nq == 0) return hipSuccess;
   if (a0.fmt == HCA_F32) {
     const int64_t chunks_f64 = (a0.max_visible + 255) / 256;
@@ -1397,8 +1497,14 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s) {
   }
   const int G = indexer_group(a0.Nq, a0.max_visible, a0.fmt, a0.k);
   if (G >= a0.Nq) {                                      // one group, one stream
-    const GroupPlan p = plan_group(a0);
-    launch_score_phase(p, s);
+    GroupPlan p = plan_group(a0);
+    if (pool) {
+      const int64_t chunks = (p.a.max_visible + entries_per_wg_t(kFusedTpw(p.a)) - 1) / entries_per_wg_t(kFusedTpw(p.a));
+      const int64_t cx = chunks > 0 ? chunks : 1;
+      p.a.pool_rows = (int)((pool->n_blocks + cx - 1) / cx);
+      p.a.pool_target = pool->n_blocks;
+    }
+    launch_score_phase(p, s, pool);
     launch_select_phase(p, s);
     return hipGetLastError();
   }

@@ -29,7 +29,8 @@ import numpy as np
 import torch
 
 from . import _abi as A
-from .ops import IdxCache, KVCache, hca_attn_decode, hca_attn_prefill, hca_indexer_topk, hca_kv_compress
+from .ops import (IdxCache, KVCache, hca_attn_decode, hca_attn_prefill, hca_decode_layer, hca_indexer_topk,
+                  hca_kv_compress)
 
 
 def _page_layout(starts: np.ndarray, n_rows: int, max_visible: int, page_rows: int, seed: int):
@@ -175,40 +176,60 @@ class DeviceLayer:
         return d
 
     # ----------------------------------------------------------------- steps
-    def pool(self, debug: Optional[torch.Tensor] = None):
+    def _pool_kw(self, debug: Optional[torch.Tensor] = None) -> dict:
         g = self.g
-        if self.mode == A.MODE_SWA:
-            return
-        hca_kv_compress(self.win, self.block_row, self.block_pos, self.out_row, self.gate_w, self.gate_b,
-                        self.cache, m=self.m, D_r=g.D_r, rope_base=g.rope_base,
-                        raw_idx=self.win_idx if self.mode == A.MODE_CSA else None,
-                        out_idx=self.keys if self.mode == A.MODE_CSA else None, debug=debug)
+        csa = self.mode == A.MODE_CSA
+        return dict(raw=self.win, block_row=self.block_row, block_pos=self.block_pos, out_row=self.out_row,
+                    gate_w=self.gate_w, gate_b=self.gate_b, out=self.cache, m=self.m, D_r=g.D_r,
+                    rope_base=g.rope_base, raw_idx=self.win_idx if csa else None,
+                    out_idx=self.keys if csa else None, debug=debug)
 
-    def select(self, score: Optional[torch.Tensor] = None, prof=None, queries: Optional[slice] = None):
-        """Indexer top-k of every query, or of the queries in ``queries`` (a slice)."""
+    def _select_kw(self, score: Optional[torch.Tensor] = None, queries: Optional[slice] = None) -> dict:
         g = self.g
         qs = queries if queries is not None else slice(None)
         qI = IdxCache(self.qI.data[qs], self.qI.fmt, None if self.qI.scales is None else self.qI.scales[qs])
-        return hca_indexer_topk(qI, self.w[qs], self.keys, self.cache_row_start, self.seq_id[qs], self.q_pos[qs],
-                                k=g.topk, m=self.m, max_visible=self.max_visible, idx=self.idx[qs],
-                                score=None if score is None else score[qs], prof=prof, pages=self.pages)
+        return dict(q=qI, w=self.w[qs], keys=self.keys, cache_row_start=self.cache_row_start,
+                    seq_id=self.seq_id[qs], q_pos=self.q_pos[qs], k=g.topk, m=self.m,
+                    max_visible=self.max_visible, idx=self.idx[qs],
+                    score=None if score is None else score[qs], pages=self.pages)
+
+    def _attend_kw(self) -> dict:
+        g = self.g
+        csa = self.mode == A.MODE_CSA
+        return dict(q=self.q, cache=self.cache, cache_row_start=self.cache_row_start, win=self.win,
+                    sink=self.sink, seq_id=self.seq_id, q_pos=self.q_pos, mode=self.mode, m=self.m,
+                    n_win=g.n_win, D_r=g.D_r, max_visible=self.max_visible, k=g.topk if csa else 0,
+                    idx=self.idx if csa else None, tau=g.tau, rope_base=g.rope_base, o=self.o,
+                    lse=self.lse, pages=self.pages, split_chunks=self.split_chunks)
+
+    def pool(self, debug: Optional[torch.Tensor] = None):
+        if self.mode == A.MODE_SWA:
+            return
+        hca_kv_compress(**self._pool_kw(debug))
+
+    def select(self, score: Optional[torch.Tensor] = None, prof=None, queries: Optional[slice] = None):
+        """Indexer top-k of every query, or of the queries in ``queries`` (a slice)."""
+        return hca_indexer_topk(**self._select_kw(score, queries), prof=prof)
 
     def attend(self, prefill: bool = False, prof=None):
-        g = self.g
         fn = hca_attn_prefill if prefill else hca_attn_decode
-        return fn(self.q, self.cache, self.cache_row_start, self.win, self.sink, self.seq_id, self.q_pos,
-                  mode=self.mode, m=self.m, n_win=g.n_win, D_r=g.D_r, max_visible=self.max_visible,
-                  k=g.topk if self.mode == A.MODE_CSA else 0,
-                  idx=self.idx if self.mode == A.MODE_CSA else None, tau=g.tau,
-                  rope_base=g.rope_base, o=self.o, lse=self.lse, prof=prof, pages=self.pages,
-                  split_chunks=self.split_chunks)
+        return fn(**self._attend_kw(), prof=prof)
 
-    def step(self, prefill: bool = False, pool: bool = True, prof_select=None, prof_attend=None):
-        if pool:
-            self.pool()
-        if self.mode == A.MODE_CSA:
-            self.select(prof=prof_select)
-        return self.attend(prefill, prof=prof_attend)
+    def step(self, prefill: bool = False, pool: bool = True, prof_select=None, prof_attend=None,
+             fused: bool = True):
+        """pool -> (CSA) select -> attend.  Decode runs as one hca_decode_layer call
+        (``fused`` False: the three calls one after another, the same results)."""
+        csa = self.mode == A.MODE_CSA
+        if prefill or not fused:
+            if pool:
+                self.pool()
+            if csa:
+                self.select(prof=prof_select)
+            return self.attend(prefill, prof=prof_attend)
+        return hca_decode_layer(self._attend_kw(),
+                                pool=self._pool_kw() if pool and self.mode != A.MODE_SWA else None,
+                                indexer=self._select_kw() if csa else None,
+                                prof=prof_select if csa else prof_attend)
 
     def clone(self) -> "DeviceLayer":
         """An independent copy of every device buffer (same shapes and contents)."""

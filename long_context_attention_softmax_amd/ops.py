@@ -1,4 +1,4 @@
-"""Python boundary over the C ABI: the four entry points with the C names.
+"""Python boundary over the C ABI: the entry points with the C names.
 
 Each function checks dtypes, devices and layouts of PyTorch tensors, fills the
 descriptor with raw device pointers and row pitches, and calls the library on the
@@ -151,12 +151,18 @@ def _raw_fmt(t: torch.Tensor) -> int:
     raise ValueError("raw rows must be float32 or bfloat16 (bits)")
 
 
-def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch.Tensor,
-                    out_row: torch.Tensor, gate_w: torch.Tensor, gate_b: torch.Tensor,
-                    out: KVCache, *, m: int, D_r: int, rope_base: float = 10000.0,
-                    raw_idx: Optional[torch.Tensor] = None, out_idx: Optional[IdxCache] = None,
-                    debug: Optional[torch.Tensor] = None) -> None:
+def hca_kv_compress(*args, **kw) -> None:
     """Pool the listed blocks of ``raw`` rows into ``out`` (and ``out_idx``)."""
+    d, _keep = _kv_compress_desc(*args, **kw)
+    A.check(A.lib.hca_kv_compress(ctypes.byref(d), _stream()))
+
+
+def _kv_compress_desc(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch.Tensor,
+                      out_row: torch.Tensor, gate_w: torch.Tensor, gate_b: torch.Tensor,
+                      out: KVCache, *, m: int, D_r: int, rope_base: float = 10000.0,
+                      raw_idx: Optional[torch.Tensor] = None, out_idx: Optional[IdxCache] = None,
+                      debug: Optional[torch.Tensor] = None):
+    """The descriptor of a pooling call, and the tensors it points into."""
     raw2 = raw.reshape(-1, raw.shape[-1])
     n = block_row.numel()
     _need_cuda(raw2, block_row, block_pos, out_row, gate_w, gate_b, raw_idx, debug)
@@ -169,7 +175,8 @@ def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch
     d.out_row = _ptr(_i64(out_row, n, "out_row"))
     if gate_w.dtype != torch.float32 or gate_b.dtype != torch.float32:
         raise ValueError("gate_w and gate_b must be float32")
-    d.gate_w, d.gate_b = _ptr(gate_w.contiguous()), _ptr(gate_b.contiguous())
+    gate_w, gate_b = gate_w.contiguous(), gate_b.contiguous()
+    d.gate_w, d.gate_b = _ptr(gate_w), _ptr(gate_b)
     d.out = out.planes()
     if raw_idx is not None:
         ri = raw_idx.reshape(-1, raw_idx.shape[-1])
@@ -180,7 +187,7 @@ def hca_kv_compress(raw: torch.Tensor, block_row: torch.Tensor, block_pos: torch
         d.out_idx = out_idx.planes()
     if debug is not None:
         d.debug = _ptr(debug)
-    A.check(A.lib.hca_kv_compress(ctypes.byref(d), _stream()))
+    return d, (raw2, gate_w, gate_b)
 
 
 def hca_indexer_query_group(Nq: int, max_visible: int, fmt: int, k: int) -> int:
@@ -192,13 +199,24 @@ def hca_indexer_query_group(Nq: int, max_visible: int, fmt: int, k: int) -> int:
     return A.indexer_query_group(d)
 
 
-def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: Optional[torch.Tensor],
-                     seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
-                     max_visible: int, idx: Optional[torch.Tensor] = None,
-                     score: Optional[torch.Tensor] = None, prof=None, pages=None) -> torch.Tensor:
+def hca_indexer_topk(*args, prof=None, **kw) -> torch.Tensor:
     """Top-k entries per query.  q.data is [Nq, H_I, ...]; returns idx [Nq, k] int32.
     ``pages`` = (page_table, page_rows) addresses a paged key cache instead of
     cache_row_start (see include/hca.h)."""
+    d, idx, _keep = _indexer_desc(*args, **kw)
+    if prof is not None:
+        A.check(A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), _events(prof), _stream()))
+    else:
+        A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
+    return idx
+
+
+def _indexer_desc(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_start: Optional[torch.Tensor],
+                  seq_id: torch.Tensor, q_pos: torch.Tensor, *, k: int, m: int,
+                  max_visible: int, idx: Optional[torch.Tensor] = None,
+                  score: Optional[torch.Tensor] = None, pages=None):
+    """The descriptor of an indexer call (its workspace attached), idx, and the tensors
+    the descriptor points into."""
     Nq, H_I = q.data.shape[0], q.data.shape[1]
     d_I = q.data.shape[-1] * (2 if q.fmt == A.MXFP4 else 1)
     _need_cuda(w, cache_row_start, seq_id, q_pos, idx, score)
@@ -224,19 +242,32 @@ def hca_indexer_topk(q: IdxCache, w: torch.Tensor, keys: IdxCache, cache_row_sta
     nb = A.workspace_bytes(A.OP_INDEXER_TOPK, d)
     ws = _workspace(A.OP_INDEXER_TOPK, nb, w.device)
     d.workspace, d.workspace_bytes = _ptr(ws), nb
-    if prof is not None:
-        A.check(A.lib.hca_profiled(A.OP_INDEXER_TOPK, ctypes.byref(d), _events(prof), _stream()))
+    return d, idx, (ws,)
+
+
+def _attn(prefill: bool, *args, prof=None, noalloc: bool = False, **kw) -> torch.Tensor:
+    d, o, _keep = _attn_desc(prefill, *args, workspace=not noalloc, **kw)
+    op = A.OP_ATTN_PREFILL if prefill else A.OP_ATTN_DECODE
+    if noalloc:                           # the library's static scratch; no workspace
+        if prof is not None:
+            raise ValueError("the allocation-free entry point has no timing hook")
+        A.check(A.lib.hca_attn_decode_noalloc(ctypes.byref(d), _stream()))
+    elif prof is not None:
+        A.check(A.lib.hca_profiled(op, ctypes.byref(d), _events(prof), _stream()))
     else:
-        A.check(A.lib.hca_indexer_topk(ctypes.byref(d), _stream()))
-    return idx
+        fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
+        A.check(fn(ctypes.byref(d), _stream()))
+    return o
 
 
-def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_start: Optional[torch.Tensor],
-          win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
-          mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
-          idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
-          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, prof=None,
-          pages=None, split_chunks: int = 0, noalloc: bool = False) -> torch.Tensor:
+def _attn_desc(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_start: Optional[torch.Tensor],
+               win: torch.Tensor, sink: torch.Tensor, seq_id: torch.Tensor, q_pos: torch.Tensor, *,
+               mode: int, m: int, n_win: int, D_r: int, max_visible: int, k: int = 0,
+               idx: Optional[torch.Tensor] = None, tau: float = 1.0, rope_base: float = 10000.0,
+               o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               pages=None, split_chunks: int = 0, workspace: bool = True):
+    """The descriptor of an attention call (with its workspace unless ``workspace`` is
+    False), the output o, and the tensors the descriptor points into."""
     Nq, H, D = q.shape
     _need_cuda(q, cache_row_start, win, sink, seq_id, q_pos, idx, o, lse)
     io = A.F32 if q.dtype == torch.float32 else A.BF16
@@ -264,25 +295,45 @@ def _attn(prefill: bool, q: torch.Tensor, cache: Optional[KVCache], cache_row_st
         d.idx = _ptr(idx)
     w2 = win.reshape(-1, win.shape[-1])
     d.win, d.win_pitch = _ptr(w2), _pitch(w2)
-    d.sink = _ptr(sink.contiguous())
+    sink = sink.contiguous()
+    d.sink = _ptr(sink)
     d.seq_id = _ptr(seq_id)
     d.q_pos = _ptr(_i64(q_pos, Nq, "q_pos"))
     d.o = _ptr(o)
     d.lse = _ptr(lse)
-    op = A.OP_ATTN_PREFILL if prefill else A.OP_ATTN_DECODE
-    if noalloc:                           # the library's static scratch; no workspace
-        if prof is not None:
-            raise ValueError("the allocation-free entry point has no timing hook")
-        A.check(A.lib.hca_attn_decode_noalloc(ctypes.byref(d), _stream()))
-        return o
-    nb = A.workspace_bytes(op, d)
-    ws = _workspace(op, nb, q.device)
-    d.workspace, d.workspace_bytes = _ptr(ws), nb
+    ws = None
+    if workspace:
+        op = A.OP_ATTN_PREFILL if prefill else A.OP_ATTN_DECODE
+        nb = A.workspace_bytes(op, d)
+        ws = _workspace(op, nb, q.device)
+        d.workspace, d.workspace_bytes = _ptr(ws), nb
+    return d, o, (q, w2, sink, ws)
+
+
+def hca_decode_layer(attn: dict, pool: Optional[dict] = None, indexer: Optional[dict] = None,
+                     prof=None) -> torch.Tensor:
+    """One decode step of one layer in one library call (see include/hca.h): ``pool``,
+    ``indexer`` and ``attn`` hold the keyword arguments of hca_kv_compress,
+    hca_indexer_topk (CSA only; its idx is the one attention reads) and
+    hca_attn_decode.  ``prof`` brackets the scoring launch (CSA) or the attention
+    kernel (HCA, sliding window).  Returns o."""
+    keep = []
+    d = A.new_desc(A.DecodeLayerDesc)
+    if pool is not None:
+        pd, k1 = _kv_compress_desc(**pool)
+        keep += [pd, k1]
+        d.pool = ctypes.pointer(pd)
+    if indexer is not None:
+        idd, _idx, k2 = _indexer_desc(**indexer)
+        keep += [idd, k2]
+        d.indexer = ctypes.pointer(idd)
+    ad, o, k3 = _attn_desc(False, **attn)
+    keep += [ad, k3]
+    d.attn = ctypes.pointer(ad)
     if prof is not None:
-        A.check(A.lib.hca_profiled(op, ctypes.byref(d), _events(prof), _stream()))
+        A.check(A.lib.hca_profiled(A.OP_DECODE_LAYER, ctypes.byref(d), _events(prof), _stream()))
     else:
-        fn = A.lib.hca_attn_prefill if prefill else A.lib.hca_attn_decode
-        A.check(fn(ctypes.byref(d), _stream()))
+        A.check(A.lib.hca_decode_layer(ctypes.byref(d), _stream()))
     return o
 
 

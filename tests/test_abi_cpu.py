@@ -44,10 +44,11 @@ def test_constants_match_the_header():
 
 
 def test_version_and_struct_sizes():
-    assert A.lib.hca_abi_version() == 6
+    assert A.lib.hca_abi_version() == 7
     for op, cls in [(A.OP_KV_COMPRESS, A.KvCompressDesc), (A.OP_INDEXER_TOPK, A.IndexerTopkDesc),
                     (A.OP_ATTN_DECODE, A.AttnDesc), (A.OP_ATTN_PREFILL, A.AttnDesc),
                     (A.OP_QKV_PROLOGUE, A.QkvPrologueDesc), (A.OP_OUT_PROJ, A.OutProjDesc),
+                    (A.OP_DECODE_LAYER, A.DecodeLayerDesc),
                     (A.STRUCT_KV_PLANES, A.KvPlanes), (A.STRUCT_IDX_PLANES, A.IdxPlanes),
                     (A.STRUCT_PROFILE_EVENTS, A.ProfileEvents)]:
         assert A.lib.hca_struct_size(op) == ctypes.sizeof(cls), cls
@@ -185,6 +186,36 @@ def attn_desc(**kw):
     for k, v in kw.items():
         setattr(d, k, v)
     return d
+
+
+def test_decode_layer_validation_before_any_launch():
+    # every check of the three descriptors, and their agreement, runs on the host
+    # before anything is launched (FAKE pointers are never dereferenced)
+    def layer(pool=None, indexer=None, attn=None, **kw):
+        d = A.new_desc(A.DecodeLayerDesc)
+        d.pool = None if pool is None else ctypes.pointer(pool)
+        d.indexer = None if indexer is None else ctypes.pointer(indexer)
+        d.attn = None if attn is None else ctypes.pointer(attn)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+    ws = dict(workspace=FAKE, workspace_bytes=1 << 40)
+    assert A.lib.hca_decode_layer(None, None) == -1
+    assert call("hca_decode_layer", layer()) == -1                                   # no attn
+    assert call("hca_decode_layer", layer(attn=attn_desc(**ws), struct_size=4)) == -8
+    assert call("hca_decode_layer", layer(attn=attn_desc(**ws))) == -2              # CSA without indexer
+    assert b"indexer" in A.lib.hca_last_error()
+    hca = attn_desc(mode=A.MODE_HCA, m=128, k=0, idx=None, max_visible=8192, **ws)
+    assert call("hca_decode_layer", layer(indexer=idx_desc(**ws), attn=hca)) == -2  # indexer outside CSA
+    assert call("hca_decode_layer", layer(pool=kv_desc(m=0), attn=hca)) == -2       # the pool's own check
+    assert call("hca_decode_layer", layer(pool=kv_desc(), attn=hca)) == -2          # pool m 4 != attn m 128
+    assert b"m" in A.lib.hca_last_error()
+    for bad in [dict(Nq=7), dict(k=256), dict(m=8), dict(idx=FAKE + 4096)]:
+        assert call("hca_decode_layer", layer(indexer=idx_desc(**{**ws, **bad}), attn=attn_desc(**ws))) == -2, bad
+    assert call("hca_decode_layer", layer(indexer=idx_desc(**ws), attn=attn_desc(H=40, **ws))) == -5
+    n = ctypes.c_size_t(1)
+    assert A.lib.hca_workspace_bytes(A.OP_DECODE_LAYER, ctypes.byref(layer()), ctypes.byref(n)) == 0
+    assert n.value == 0
 
 
 def test_attention_validation():
@@ -356,7 +387,8 @@ def test_struct_field_offsets_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     structs = {"hca_kv_compress_desc": A.KvCompressDesc, "hca_indexer_topk_desc": A.IndexerTopkDesc,
                "hca_attn_desc": A.AttnDesc, "hca_kv_planes": A.KvPlanes, "hca_idx_planes": A.IdxPlanes,
-               "hca_qkv_prologue_desc": A.QkvPrologueDesc, "hca_out_proj_desc": A.OutProjDesc}
+               "hca_qkv_prologue_desc": A.QkvPrologueDesc, "hca_out_proj_desc": A.OutProjDesc,
+               "hca_decode_layer_desc": A.DecodeLayerDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hca.h"', "int main(void) {"]
     for cname, cls in structs.items():
         for f in cls._fields_:
