@@ -16,7 +16,8 @@ after a 1M prefix (TFLOP/s of the scoring kernel).
 Inputs are seeded synthetic data shaped like those workloads, resident in HBM
 before timing; each workload is replicated until the replicas exceed 1 GiB and the
 steps rotate through them, so the 256 MiB last-level cache cannot serve them.
-``roofline`` reports the dominant kernel (the CSA indexer scoring kernel) against
+``roofline`` reports the dominant kernel (the CSA indexer scoring launch, which also
+carries the step's pooling) against
 the 8 TB/s HBM peak, timed by HIP events recorded around it on its own stream.
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the primary
 workload on this machine's host cores.
@@ -87,8 +88,10 @@ def prefill_indexer_flops(prefix, T, H_I=64, d_I=128):
 # ------------------------------------------------ committed counter evidence
 def committed_traffic(summary="profiles/hbm_counters.ragged_pair_32.md"):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has changed
-    since those counters were taken (or no summary exists)."""
+    FETCH_SIZE / WRITE_SIZE summary, or None when a source the kernel is compiled
+    from has changed since those counters were taken (or no summary exists).  The
+    summary lists its sources as ``kernel_source`` / ``kernel_source_sha256`` pairs
+    (comma-separated, in the same order)."""
     import hashlib
     try:
         text = open(os.path.join(ROOT, summary)).read()
@@ -100,9 +103,13 @@ def committed_traffic(summary="profiles/hbm_counters.ragged_pair_32.md"):
         if k in ("kernel_source", "kernel_source_sha256", "traffic_bytes_per_launch"):
             fields[k] = v.strip()
     try:
-        src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"]:
+        srcs = [x.strip() for x in fields["kernel_source"].split(",")]
+        shas = [x.strip() for x in fields["kernel_source_sha256"].split(",")]
+        if len(srcs) != len(shas):
             return None
+        for src, sha in zip(srcs, shas):
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+                return None
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
         return None
@@ -303,7 +310,8 @@ def main():
             config={"workload": "ragged_pair_32", "batch": w5.B, "context_lengths": L,
                     "layers": "CSA (m=4, FP8 indexer 64x128, top-512) + HCA (m=128)",
                     "heads": 64, "head_dim": 512, "window": 128, "replicas": len(sets)},
-            roofline={"bound": "hbm", "kernel": "score_quant_kernel<FP8> (CSA indexer scoring)",
+            roofline={"bound": "hbm",
+                      "kernel": "score_pool_kernel<FP8> (CSA indexer scoring; the step's pooling rides in it)",
                       "achieved": round(ckeys / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                       "unit": "GB/s", "frac": round(ckeys / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       "traffic": committed_traffic(), "algorithmic_bytes_per_launch": ckeys,

@@ -22,6 +22,7 @@
 
 #include "device_common.hpp"
 #include "hca_internal.hpp"
+#include "pool_block.hpp"
 #include "../../include/hca.h"
 
 namespace hca {
@@ -395,8 +396,17 @@ __device__ __forceinline__ int find_query(const int* pref, int nq, int c) {
   return lo;
 }
 
-template <int layout>
-__global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
+// POOL (decode layouts Flat and SplitFlat): the grid's first pool_wgs workgroups pool
+// one block each (HCA: a block's tokens complete its sequence's newest entry) and
+// count themselves; the rest run the attention plan over gridDim.x - pool_wgs
+// workgroups, and the one that stages the chunk holding a query's newest entry V - 1
+// waits for every count first.  The pooling workgroups lead the dispatch order, so
+// they are running whenever a workgroup waits; the wait is bounded all the same.
+typedef PoolSmem<kThreads, 16, false> AttnPoolSmem;       // blocks of m <= 128 tokens, no index stream
+constexpr uint32_t kPoolSpinMax = 1u << 22;
+
+template <int layout, bool POOL>
+__device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs& pool) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[KC * kKsPitch];
   __shared__ __attribute__((aligned(16))) float4 s_sx[8][4][64];
   __shared__ __attribute__((aligned(16))) __bf16 Pt[8][KC * kPtPitch];
@@ -418,16 +428,51 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
   constexpr bool split_flat = layout == kLayoutSplitFlat;
   constexpr bool fixed_split = layout == kLayoutSplit || layout == kLayoutSplitFlat;
 
+  static_assert(sizeof(AttnPoolSmem) <= sizeof(Ks), "a pooling workgroup's LDS fits in the key tile");
+  if constexpr (POOL) {
+    if ((int)blockIdx.x < a.pool_wgs) {
+      if ((int)blockIdx.x < pool.n_blocks) {
+        pool_d512_block<kThreads, 16, false>(pool, blockIdx.x, *reinterpret_cast<AttnPoolSmem*>(Ks));
+        // every thread's stores complete, then the XCD's cache is written back before
+        // the count is raised
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          atomicAdd(a.pool_done, 1u);
+        }
+      }
+      return;                                       // uniform over the workgroup
+    }
+  }
+  // this workgroup's place in the attention plan, and the plan's workgroup count
+  const int bid = (int)blockIdx.x - (POOL ? a.pool_wgs : 0);
+  const int nwg = (int)gridDim.x - (POOL ? a.pool_wgs : 0);
+  // wait for the pooling before staging the chunk that holds the newest entry
+  auto pool_wait = [&](const QInfo& qs, int p) {
+    if constexpr (POOL) {
+      if (!csa && qs.n_ent > 0 && p <= qs.n_ent - 1 && qs.n_ent - 1 < p + KC) {   // uniform
+        if (tid == 0) {
+          for (uint32_t it = 0; __hip_atomic_load(a.pool_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                                    (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
+            __builtin_amdgcn_s_sleep(2);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale copy of the new rows is read
+        }
+        __syncthreads();
+      }
+    }
+  };
+
   if (tid < 32) s_inv[tid] = a.inv_turn[tid];       // turns per position
   // ---- the chunk list and this workgroup's run [c0, c1)
   int nq_local, qbase, c0, c1;
   int run = 0, n_runs = 1;                          // fixed split: this run, the query's runs
   PartialPtrs pp{};
   if (per_query) {
-    qbase = blockIdx.x;
+    qbase = bid;
     if constexpr (layout == kLayoutSplit) {
-      qbase = blockIdx.x / a.split_runs;
-      run = blockIdx.x - qbase * a.split_runs;
+      qbase = bid / a.split_runs;
+      run = bid - qbase * a.split_runs;
     }
     nq_local = 1;
     if (tid == 0) {
@@ -481,8 +526,8 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
     if constexpr (split_flat) {
       // whole runs [r0, r1): a run is never cut, so its partial depends on its query alone
       const int runs = s_rpref[a.Nq];
-      const int per = (runs + gridDim.x - 1) / gridDim.x;
-      const int r0 = blockIdx.x * per, r1 = min(r0 + per, runs);
+      const int per = (runs + nwg - 1) / nwg;
+      const int r0 = bid * per, r1 = min(r0 + per, runs);
       c0 = c1 = 0;
       if (r0 < r1) {
         const int n0 = find_query(s_rpref, a.Nq, r0), n1 = find_query(s_rpref, a.Nq, r1 - 1);
@@ -492,7 +537,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
       pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
       // a query with no run (empty set: nothing visible, no window) gets the sink
       // alone, o = 0, from workgroup 0 (no run and no combine writes it)
-      if (blockIdx.x == 0) {
+      if (bid == 0) {
         for (int nq = 0; nq < a.Nq; ++nq) {
           if (s_rpref[nq + 1] != s_rpref[nq]) continue;       // uniform
           __bf16* o = reinterpret_cast<__bf16*>(a.o) + (int64_t)nq * a.H * kD;
@@ -501,14 +546,14 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
         }
       }
     } else {
-      int per = (total + gridDim.x - 1) / gridDim.x;
+      int per = (total + nwg - 1) / nwg;
       if (per < HCA_ATTN_MIN_CHUNKS) per = HCA_ATTN_MIN_CHUNKS;
       pp = partial_ptrs(a.workspace, a.Nq, a.H, 0);
-      if (blockIdx.x == 0) {
+      if (bid == 0) {
         for (int i = tid; i <= a.Nq; i += kThreads) pp.pref[i] = s_pref[i];
         if (tid == 0) pp.pref[a.Nq + 1] = per;
       }
-      c0 = blockIdx.x * per;
+      c0 = bid * per;
       c1 = min(c0 + per, total);
     }
     if (tid < a.Nq) s_qi[tid].row0 = row0;
@@ -557,6 +602,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
     const int ib_ = (c_st - idx_win) * KC;                                                     \
     const int j0_ = csa ? s_idx[ib_ + kk0] : 0, j1_ = csa ? s_idx[ib_ + kk1] : 0;              \
     if (p_st < qs_.n_ent) {                        /* uniform: the chunk holds entries */      \
+      pool_wait(qs_, p_st);                                                                    \
       e0 = entry_load(a, qs_, p_st + kk0, j0_, q16, csa);                                      \
       e1 = entry_load(a, qs_, p_st + kk1, j1_, q16, csa);                                      \
     } else {                                                                                   \
@@ -791,7 +837,7 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
         } else {
           size_t slot;
           if constexpr (fixed_split) slot = (size_t)n * a.split_runs + (seg0 - s_pref[nl]) / a.split_chunks;
-          else slot = (size_t)blockIdx.x + n;
+          else slot = (size_t)bid + n;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int h = hrow0 + i;
@@ -816,6 +862,18 @@ __global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
       __syncthreads();
     }
   }
+}
+
+template <int layout>
+__global__ void __launch_bounds__(kThreads) attn_mqa_kernel(AttnArgs a) {
+  const PoolArgs none{};
+  attn_mqa_body<layout, false>(a, none);
+}
+
+// the same attention with the step's pooling in the leading workgroups (decode)
+template <int layout>
+__global__ void __launch_bounds__(kThreads) attn_pool_kernel(AttnArgs a, PoolArgs p) {
+  attn_mqa_body<layout, true>(a, p);
 }
 
 #undef HCA_ISSUE
@@ -966,18 +1024,56 @@ hipError_t attention_static_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+// bytes of the split partials (the prefix header, max and sum, o); the fused pooling's
+// count follows them
+size_t partial_bytes(int Nq, int H, int runs) {
+  const size_t slots = partial_slots(Nq, runs);
+  return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + round256(slots * H * kD * 2);
+}
+
+__global__ void __launch_bounds__(64) clear_count_kernel(uint32_t* p) {
+  if (threadIdx.x == 0) *p = 0u;
+}
+
+// The step's pooling can ride in the attention launch: a decode plan shared over the
+// workgroups (few queries), BF16 rows of 512 dims without an index stream in blocks of
+// 17 to 128 tokens (the configuration the pooling kernel itself uses for them: the same
+// bits), and few enough blocks that pooling and attention workgroups are resident
+// together.
+bool attn_pool_fusable(const AttnArgs& a, const PoolArgs& p) {
+  if (a.io_f32 || a.prefill || a.mode == HCA_MODE_CSA || !a.workspace) return false;
+  if (!decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible)) return false;
+  return pool_fast_path(p) && p.m > 16 && p.m <= 128 && p.idx_fmt < 0 && p.n_blocks <= 64;
+}
+}  // namespace
+
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
                                  int64_t max_visible, int io_f32, int prefill, int split_chunks) {
   (void)D;
   if (io_f32 || prefill) return 0;
   const int64_t runs = attention_split_runs(mode, k, n_win, max_visible, split_chunks);
   if (runs <= 0 && !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
-  const size_t slots = partial_slots(Nq, (int)runs);
-  return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + slots * H * kD * 2;
+  return partial_bytes(Nq, H, (int)runs) + 256;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.Nq == 0) return hipSuccess;
+hipError_t launch_attention(const AttnArgs& a0, hipStream_t s, const PoolArgs* pool) {
+  if (pool && pool->n_blocks == 0) pool = nullptr;
+  if (pool && (a0.Nq == 0 || !attn_pool_fusable(a0, *pool))) {   // pooled by its own launch, first
+    const hipError_t e = launch_pool(*pool, s);
+    if (e != hipSuccess) return e;
+    pool = nullptr;
+  }
+  if (a0.Nq == 0) return hipSuccess;
+  AttnArgs a = a0;
+  if (pool) {
+    // the count lives after the partials; cleared before the launch that raises it
+    a.pool_done = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) +
+                                              partial_bytes(a.Nq, a.H, a.split_runs > 0 ? a.split_runs : 0));
+    a.pool_wgs = pool->n_blocks;
+    a.pool_target = pool->n_blocks;
+    hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(64), 0, s, a.pool_done);
+  }
   if (a.io_f32) {
     if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.Nq, a.H), dim3(256), 0, s, a);
@@ -989,7 +1085,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const bool flat = decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible);
     const unsigned grid = flat ? HCA_ATTN_GRID : (unsigned)((int64_t)a.Nq * a.split_runs);
     if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);
-    if (flat) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplitFlat>, dim3(grid), dim3(kThreads), 0, s, a);
+    if (pool)          // one CU each: the pooling workgroups take the place of plan workgroups
+      hipLaunchKernelGGL(attn_pool_kernel<kLayoutSplitFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, a, *pool);
+    else if (flat) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplitFlat>, dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplit>, dim3(grid), dim3(kThreads), 0, s, a);
     if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
     if (a.split_runs > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H / 4), dim3(256), 0, s, a);
@@ -999,7 +1097,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   b.split_runs = 0;                        // prefill never splits a query
   const bool dec = decode_layout(b.Nq, b.prefill, b.mode, b.k, b.n_win, b.max_visible);
   if (b.prof_begin) (void)hipEventRecord(b.prof_begin, s);
-  if (dec) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b);
+  if (pool)            // one CU each: the pooling workgroups take the place of plan workgroups
+    hipLaunchKernelGGL(attn_pool_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b, *pool);
+  else if (dec) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b);
   else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutQuery>, dim3(b.Nq), dim3(kThreads), 0, s, b);
   if (b.prof_end) (void)hipEventRecord(b.prof_end, s);
   if (dec) hipLaunchKernelGGL(combine_kernel, dim3(b.Nq, b.H / 4), dim3(256), 0, s, b);

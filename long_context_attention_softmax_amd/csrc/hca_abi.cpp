@@ -541,10 +541,10 @@ int decode_layer_call(const hca_decode_layer_desc* d, void* stream, const hca_pr
   hipError_t e = hipSuccess;
   if (csa) {
     e = hca::launch_indexer_topk(ia, s, pool);           // pools inside the scoring launch where it can
-  } else if (pool) {
-    e = hca::launch_pool(pa, s);
+    if (e == hipSuccess && aa.Nq > 0) e = hca::launch_attention(aa, s);
+  } else {
+    e = hca::launch_attention(aa, s, pool);              // pools inside the attention launch where it can
   }
-  if (e == hipSuccess && aa.Nq > 0) e = hca::launch_attention(aa, s);
   return launched(e);
 }
 }  // namespace

@@ -82,8 +82,14 @@ struct AttnArgs {
   const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged entries (page_shift >= 0)
   int split_chunks, split_runs;       // decode fixed split: chunks per run, most runs of a query (0 = off)
   double inv_turn[32];                // BF16 path: rope_base^(-2i/64) / (2 pi), turns per position
+  // fused decode pooling (HCA): workgroups [0, pool_wgs) pool the step's blocks and count
+  // themselves in *pool_done; the one staging a query's newest entry waits for pool_target
+  int pool_wgs, pool_target;
+  uint32_t* pool_done;
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// pool (optional, decode): blocks to pool before attention, in the same call; fused
+// into the attention launch where the launch plan allows, else launched first
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, const PoolArgs* pool = nullptr);
 size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_win,
                                  int64_t max_visible, int io_f32, int prefill, int split_chunks);
 // most runs of one query under a fixed split of split_chunks chunks (0 when split_chunks <= 0)

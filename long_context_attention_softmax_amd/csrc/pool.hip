@@ -277,7 +277,8 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
     if (a.m <= 16 && y) hipLaunchKernelGGL((pool_d512_kernel<256, 4, true>), dim3(a.n_blocks), dim3(256), 0, s, a);
     else if (a.m <= 16) hipLaunchKernelGGL((pool_d512_kernel<256, 4, false>), dim3(a.n_blocks), dim3(256), 0, s, a);
     else if (y) hipLaunchKernelGGL((pool_d512_kernel<512, 16, true>), dim3(a.n_blocks), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((pool_d512_kernel<1024, 8, false>), dim3(a.n_blocks), dim3(1024), 0, s, a);
+    // the configuration the attention launch pools with, so both give the same bits
+    else hipLaunchKernelGGL((pool_d512_kernel<512, 16, false>), dim3(a.n_blocks), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   if (a.raw_is_f32)

@@ -48,6 +48,16 @@ def test_committed_traffic_needs_the_profiled_source(tmp_path):
                      "    traffic_bytes_per_launch: 123\n")
     assert bench.committed_traffic(str(stale)) is None
     assert bench.committed_traffic(str(tmp_path / "missing.md")) is None
+    # several sources: every one must match
+    src2 = "long_context_attention_softmax_amd/csrc/pool_block.hpp"
+    sha2 = hashlib.sha256(open(os.path.join(ROOT, src2), "rb").read()).hexdigest()
+    two = tmp_path / "two.md"
+    two.write_text(f"    kernel_source: {src}, {src2}\n    kernel_source_sha256: {sha}, {sha2}\n"
+                   "    traffic_bytes_per_launch: 456\n")
+    assert bench.committed_traffic(str(two)) == 456
+    two.write_text(f"    kernel_source: {src}, {src2}\n    kernel_source_sha256: {sha}, {'1' * 64}\n"
+                   "    traffic_bytes_per_launch: 456\n")
+    assert bench.committed_traffic(str(two)) is None
 
 
 def test_seeded_workloads_are_reproducible():
