@@ -305,6 +305,32 @@ __device__ __forceinline__ EntryRegs entry_load(const AttnArgs& a, const QInfo& 
   return e;
 }
 
+// entry_load with device-coherent 32-bit loads, which bypass the XCD's L2: the chunk
+// that holds the entry this launch has just pooled reads it this way, so a line of
+// that entry cached on this XCD before the pooling wrote it (448-byte FP8 rows and
+// 4-byte scales share lines with the previous entry's) can never be returned
+__device__ __forceinline__ uint32_t ld_dev32(const char* p) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<char*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ EntryRegs entry_load_dev(const AttnArgs& a, const QInfo& qi, int p, int jrow, int q,
+                                                    bool csa) {
+  EntryRegs e;
+  e.kind = key_kind(qi, p, jrow, csa);
+  const int64_t j = e.kind == kEntry ? (csa ? (int64_t)jrow : (int64_t)p) : 0;
+  const int64_t row = cache_row(a.page_table, a.page_pitch, a.page_shift, qi.b, qi.row0, j);
+  const char* nope = a.c_nope + row * a.c_nope_pitch + 8 * q;
+  const char* f3 = nope + 384 - 8 * (q & 8);
+  const char* r3 = a.c_rope + row * a.c_rope_pitch + 16 * (q & 7);
+  e.f0 = (u2){ld_dev32(nope), ld_dev32(nope + 4)};
+  e.f1 = (u2){ld_dev32(nope + 128), ld_dev32(nope + 132)};
+  e.f2 = (u2){ld_dev32(nope + 256), ld_dev32(nope + 260)};
+  e.f3 = (u2){ld_dev32(f3), ld_dev32(f3 + 4)};
+  e.r3 = (u4){ld_dev32(r3), ld_dev32(r3 + 4), ld_dev32(r3 + 8), ld_dev32(r3 + 12)};
+  e.sc = __uint_as_float(ld_dev32(reinterpret_cast<const char*>(a.c_scale + row)));
+  return e;
+}
+
 // rotate 8 BF16 dims of a window token's RoPE slice: `own` holds pair indices
 // i0 .. i0+7, `mate` the other member of each pair; first = own is the first half
 __device__ __forceinline__ u4 rope8(u4 own, u4 mate, int i0, bool first, int64_t u, const double* s_inv) {
@@ -448,19 +474,19 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
   // this workgroup's place in the attention plan, and the plan's workgroup count
   const int bid = (int)blockIdx.x - (POOL ? a.pool_wgs : 0);
   const int nwg = (int)gridDim.x - (POOL ? a.pool_wgs : 0);
-  // wait for the pooling before staging the chunk that holds the newest entry
-  auto pool_wait = [&](const QInfo& qs, int p) {
-    if constexpr (POOL) {
-      if (!csa && qs.n_ent > 0 && p <= qs.n_ent - 1 && qs.n_ent - 1 < p + KC) {   // uniform
-        if (tid == 0) {
-          for (uint32_t it = 0; __hip_atomic_load(a.pool_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                                    (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
-            __builtin_amdgcn_s_sleep(2);
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale copy of the new rows is read
-        }
-        __syncthreads();
-      }
+  // the chunk that holds a query's newest entry (HCA: set position n_ent - 1) waits
+  // for the pooling, then reads its entries with device-coherent loads
+  auto pool_chunk = [&](const QInfo& qs, int p) {
+    return POOL && !csa && qs.n_ent > 0 && p <= qs.n_ent - 1 && qs.n_ent - 1 < p + KC;
+  };
+  auto pool_wait = [&]() {
+    if (tid == 0) {
+      for (uint32_t it = 0; __hip_atomic_load(a.pool_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                                (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
+        __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    __syncthreads();
   };
 
   if (tid < 32) s_inv[tid] = a.inv_turn[tid];       // turns per position
@@ -601,8 +627,11 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
     const QInfo& qs_ = s_qi[ns];                                                               \
     const int ib_ = (c_st - idx_win) * KC;                                                     \
     const int j0_ = csa ? s_idx[ib_ + kk0] : 0, j1_ = csa ? s_idx[ib_ + kk1] : 0;              \
-    if (p_st < qs_.n_ent) {                        /* uniform: the chunk holds entries */      \
-      pool_wait(qs_, p_st);                                                                    \
+    if (p_st < qs_.n_ent && pool_chunk(qs_, p_st)) {   /* uniform: the newly pooled entry */  \
+      pool_wait();                                                                             \
+      e0 = entry_load_dev(a, qs_, p_st + kk0, j0_, q16, csa);                                  \
+      e1 = entry_load_dev(a, qs_, p_st + kk1, j1_, q16, csa);                                  \
+    } else if (p_st < qs_.n_ent) {                 /* uniform: the chunk holds entries */      \
       e0 = entry_load(a, qs_, p_st + kk0, j0_, q16, csa);                                      \
       e1 = entry_load(a, qs_, p_st + kk1, j1_, q16, csa);                                      \
     } else {                                                                                   \

@@ -1283,7 +1283,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
 template <int FMT, bool XQ, int TPW>
 void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s, const PoolArgs* pool = nullptr) {
   const bool h2 = a.H_I == 64;
-  if constexpr (!XQ) {
+  if constexpr (!XQ && FMT == HCA_FP8_E4M3) {          // the formats pool_fusable admits
     if (pool) {                                          // grid rows [0, pool_rows) pool
       const dim3 gp(grid.x, grid.y + (unsigned)a.pool_rows);
       if (a.page_shift >= 0) {
@@ -1363,7 +1363,7 @@ void launch_score_phase(const GroupPlan& p, hipStream_t s, const PoolArgs* pool 
     const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
     constexpr int T8 = HCA_SCORE_TPW, T4 = HCA_SCORE_TPW4, T4D = HCA_SCORE_TPW4D;
     if (a.fmt == HCA_FP8_E4M3) launch_score<HCA_FP8_E4M3, false, T8>(a, g2, s, pool);
-    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s, pool);
+    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s);
     else if (HCA_SCORE_XCD_MAJOR) launch_score<HCA_MXFP4, true, T4>(a, gx, s);
     else launch_score<HCA_MXFP4, false, T4>(a, g2, s);
   }
@@ -1461,18 +1461,21 @@ size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
 }
 
 namespace {
-// tiles per wave of the chunk-major scoring launch a decode call takes
-int kFusedTpw(const IndexerArgs& a) { return a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : HCA_SCORE_TPW4D; }
+// tiles per wave of the chunk-major FP8 scoring launch
+int kFusedTpw(const IndexerArgs&) { return HCA_SCORE_TPW; }
 
-// The step's pooling can ride in the scoring launch: one query group scored chunk-major
-// (FP8, or MXFP4 with few queries), blocks of at most 16 BF16 rows of 512 dims with an
-// index stream (the fast pooling path at 256 threads), and at least one key to score.
+// The step's pooling can ride in the scoring launch: one query group scored chunk-major,
+// FP8 keys whose rows fill whole 128-byte cache lines (pitch and base multiples of 128:
+// a new row then shares no line with a row another workgroup reads, so after its wait
+// and acquire the waiting workgroup cannot meet a stale copy of it, whatever the
+// workgroup-to-XCD mapping), blocks of at most 16 BF16 rows of 512 dims with an index
+// stream (the fast pooling path at 256 threads), and at least one key to score.
+// (MXFP4 rows are 64 bytes with 4-byte scales, which neighbouring rows share.)
 bool pool_fusable(const IndexerArgs& a, const PoolArgs& p) {
-  if (a.fmt == HCA_F32 || a.max_visible <= 0) return false;
+  if (a.fmt != HCA_FP8_E4M3 || a.max_visible <= 0) return false;
+  if (a.key_pitch % 128 != 0 || reinterpret_cast<uintptr_t>(a.keys) % 128 != 0) return false;
   if (indexer_group(a.Nq, a.max_visible, a.fmt, a.k) < a.Nq) return false;
-  const bool many = a.Nq >= kDigitMinQ || a.many;
-  if (a.fmt == HCA_MXFP4 && (a.Nq >= kFewQ || many)) return false;
-  return pool_fast_path(p) && p.m <= 16 && p.idx_fmt >= 0;
+  return pool_fast_path(p) && p.m <= 16 && p.idx_fmt >= 0 && p.out_idx == a.keys && p.idx_pitch == a.key_pitch;
 }
 }  // namespace
 
