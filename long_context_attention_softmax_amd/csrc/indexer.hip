@@ -405,19 +405,32 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  // POOL: the wave whose tiles hold the query's newest entry V - 1 waits for the
+  // pooling just before it loads that tile (its earlier tiles stream meanwhile), then
+  // acquires; a wave wholly past V loads nothing (its lanes would all read entry
+  // V - 1 as padding), so no other wave ever reads the new row
+  int t_wait = -1;                                      // uniform over the wave
+  bool idle = false;
   if constexpr (POOL) {
-    if (V - 1 < ebase + entries_per_wg_t(TPW)) {         // uniform: this range holds entry V - 1
-      if (tid == 0) {
+    const int64_t rel = V - 1 - wbase;
+    if (rel >= 0 && rel < 32 * kTilesPerWave) t_wait = (int)(rel >> 5);
+    idle = rel < 0;
+  }
+  auto pool_wait = [&](int t) {
+    if constexpr (POOL) {
+      if (t == t_wait) {
         for (uint32_t it = 0; ld_dev(a.pool_done) < (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
           __builtin_amdgcn_s_sleep(2);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale copy of the new rows is read
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
-      __syncthreads();
     }
-  }
+  };
 #pragma unroll
   for (int t = 0; t < kRing; ++t) {
-    if (t < kTilesPerWave) load_tile(t, kr[t], ks[t]);
+    if (t < kTilesPerWave && !idle) {
+      pool_wait(t);
+      load_tile(t, kr[t], ks[t]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   v8i qf4[2][2];
@@ -445,6 +458,7 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
   // row (a multiple of 64 floats), so a 16-byte group is either in the row or past it
   float* const sc_row = reinterpret_cast<float*>(a.scores) + (int64_t)n * a.score_pitch;
   const __amdgpu_buffer_rsrc_t srange = score_range(sc_row, kStage ? 4u * (uint32_t)a.score_pitch : 4u * (uint32_t)V);
+  if (!idle) {
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
     const uint32_t j = j0 + 32u * (uint32_t)t;
@@ -458,7 +472,10 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
         kb[2 * q + 1] = fp8x8_to_bf16(kr[slot][q].z, kr[slot][q].w);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (t + kRing < kTilesPerWave) load_tile(t + kRing, kr[slot], ks[slot]);
+      if (t + kRing < kTilesPerWave) {
+        pool_wait(t + kRing);
+        load_tile(t + kRing, kr[slot], ks[slot]);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
@@ -499,7 +516,8 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
       atomicAdd(&s_hist[(b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 21], 1u);
     }
   }
-  if (kStage) {
+  }
+  if (kStage && !idle) {
     // the wave's 32 x tiles scores in entry order, 16 bytes per lane; entries past V
     // land in the row's padding (never read), groups past the row are dropped
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -527,9 +545,10 @@ score_quant_kernel(IndexerArgs a) {
   score_quant_body<FMT, XQ, HT, TPW, PAGED, false>(a, none);
 }
 
-// the same scoring with the step's pooling in the leading grid rows (decode)
+// the same scoring with the step's pooling in the leading grid rows (decode); three
+// waves per SIMD, as the scoring kernel reaches by itself
 template <int FMT, int HT, int TPW, bool PAGED>
-__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 2)))
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(3)))
 score_pool_kernel(IndexerArgs a, PoolArgs p) {
   score_quant_body<FMT, false, HT, TPW, PAGED, true>(a, p);
 }
