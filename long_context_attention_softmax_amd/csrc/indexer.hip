@@ -405,16 +405,16 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // POOL: the wave whose tiles hold the query's newest entry V - 1 waits for the
-  // pooling just before it loads that tile (its earlier tiles stream meanwhile), then
-  // acquires; a wave wholly past V loads nothing (its lanes would all read entry
-  // V - 1 as padding), so no other wave ever reads the new row
-  int t_wait = -1;                                      // uniform over the wave
-  bool idle = false;
+  // A wave wholly past V (in a query's last chunk) loads and scores nothing: its lanes
+  // would all read entry V - 1 as padding.  POOL: the wave whose tiles hold the
+  // query's newest entry V - 1 waits for the pooling just before it loads that tile
+  // (its earlier tiles stream meanwhile), then acquires; with the idle waves skipped,
+  // no other wave ever reads the new row.
+  const int64_t rel = V - 1 - wbase;
+  const bool idle = rel < 0;                            // uniform over the wave
+  int t_wait = -1;
   if constexpr (POOL) {
-    const int64_t rel = V - 1 - wbase;
     if (rel >= 0 && rel < 32 * kTilesPerWave) t_wait = (int)(rel >> 5);
-    idle = rel < 0;
   }
   auto pool_wait = [&](int t) {
     if constexpr (POOL) {
