@@ -627,16 +627,26 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
     const QInfo& qs_ = s_qi[ns];                                                               \
     const int ib_ = (c_st - idx_win) * KC;                                                     \
     const int j0_ = csa ? s_idx[ib_ + kk0] : 0, j1_ = csa ? s_idx[ib_ + kk1] : 0;              \
-    if (p_st < qs_.n_ent && pool_chunk(qs_, p_st)) {   /* uniform: the newly pooled entry */  \
-      pool_wait();                                                                             \
-      e0 = entry_load_dev(a, qs_, p_st + kk0, j0_, q16, csa);                                  \
-      e1 = entry_load_dev(a, qs_, p_st + kk1, j1_, q16, csa);                                  \
+    if (p_st < qs_.n_ent && pool_chunk(qs_, p_st)) {   /* uniform: the newly pooled entry, */ \
+      defer_ = true;                               /* loaded after the current chunk */        \
     } else if (p_st < qs_.n_ent) {                 /* uniform: the chunk holds entries */      \
       e0 = entry_load(a, qs_, p_st + kk0, j0_, q16, csa);                                      \
       e1 = entry_load(a, qs_, p_st + kk1, j1_, q16, csa);                                      \
     } else {                                                                                   \
       e0.kind = key_kind(qs_, p_st + kk0, j0_, csa);                                           \
       e1.kind = key_kind(qs_, p_st + kk1, j1_, csa);                                           \
+    }                                                                                          \
+  } while (0)
+// the deferred chunk (it holds the entry this launch pools): wait for the pooling once
+// the current chunk has been computed, then read its entries with coherent loads
+#define HCA_DEFERRED()                                                                         \
+  do {                                                                                         \
+    if (defer_) {                                  /* uniform */                               \
+      pool_wait();                                                                             \
+      const QInfo& qs_ = s_qi[ns];                                                             \
+      e0 = entry_load_dev(a, qs_, p_st + kk0, 0, q16, csa);                                    \
+      e1 = entry_load_dev(a, qs_, p_st + kk1, 0, q16, csa);                                    \
+      defer_ = false;                                                                          \
     }                                                                                          \
   } while (0)
 #define HCA_COMMIT()                                                                           \
@@ -688,8 +698,10 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
     for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
   };
   int c_st = c0;
+  bool defer_ = false;
   HCA_ISSUE();
   if (active) q_issue(nl);                           // in flight with the first chunk's keys
+  HCA_DEFERRED();
   HCA_COMMIT();                                      // (waits for both)
   if (active) q_finish(nl);
   __syncthreads();                                   // first tile
@@ -881,6 +893,7 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
       }
     }
     if (more) {
+      HCA_DEFERRED();
       __syncthreads();                     // every wave is done with Ks, Pt, s_sx
       HCA_COMMIT();                        // (also waits for the next query's rows)
       if (last_of_query) {
@@ -906,6 +919,7 @@ __global__ void __launch_bounds__(kThreads) attn_pool_kernel(AttnArgs a, PoolArg
 }
 
 #undef HCA_ISSUE
+#undef HCA_DEFERRED
 #undef HCA_COMMIT
 
 // merge the runs of one (query, head) in run order, with the sink: run s holds
