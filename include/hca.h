@@ -406,8 +406,8 @@ typedef struct hca_out_proj_desc {
  * other entry that a query of this call reads leaves its scores and output
  * undefined (every access stays inside the buffers: no fault, no hang).
  * Under it, a CSA step with FP8 keys in rows of a multiple of 128 bytes (pitch and
- * base), whose blocks hold at most 16 BF16 rows of 512 dims with an index stream,
- * pools inside the scoring launch; a decode HCA step of at most 256 queries whose
+ * base), or MXFP4 keys and fewer than 256 queries, whose blocks hold at most 16 BF16
+ * rows of 512 dims with an index stream, pools inside the scoring launch; a decode HCA step of at most 256 queries whose
  * blocks hold 17 to 128 such rows (no index stream), at most 64 of them, pools
  * inside the attention launch.  The pooling workgroups lead the grid, and only the
  * workgroup that reads a query's newest entry waits for them, inside the device and

@@ -352,7 +352,14 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
     const uint32_t ts = min((uint32_t)wbase + 32u * (uint32_t)min(lane, TPW - 1), jmax & ~31u);
     page_of_tile = a.page_table[(int64_t)bseq * a.page_pitch + (ts >> a.page_shift)];
   }
-  auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2]) {
+  // COH: device-coherent 32-bit loads that bypass the L1 and L2 (the MXFP4 tile that
+  // holds a newly pooled entry: its 64-byte rows and 4-byte scales share cache lines
+  // with neighbouring rows that plain loads may have cached before the pooling wrote)
+  auto ld32 = [](const void* q) {
+    return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(q)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto load_tile = [&](int t, uint4 (&dst)[4], int (&dsc)[2], bool coh = false) {
     uint32_t j = min(j0 + 32u * (uint32_t)t, jmax);
     const char* kb = kseq;
     const uint8_t* sb = sseq;
@@ -367,6 +374,11 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
       const uint4* p = reinterpret_cast<const uint4*>(key);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = p[q];
+    } else if (coh) {
+      const char* sw = reinterpret_cast<const char*>(sb) + (uint32_t)__umul24(j, (uint32_t)a.key_scale_pitch);
+      dst[0] = make_uint4(ld32(key), ld32(key + 4), ld32(key + 8), ld32(key + 12));
+      dst[1] = make_uint4(ld32(key + 32), ld32(key + 36), ld32(key + 40), ld32(key + 44));
+      dsc[0] = (int)(ld32(sw) >> (8 * u));
     } else {
       dst[0] = *reinterpret_cast<const uint4*>(key);
       dst[1] = *reinterpret_cast<const uint4*>(key + 32);
@@ -416,20 +428,23 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
   if constexpr (POOL) {
     if (rel >= 0 && rel < 32 * kTilesPerWave) t_wait = (int)(rel >> 5);
   }
+  // (MXFP4 rows share cache lines, so that tile is read with coherent loads)
   auto pool_wait = [&](int t) {
     if constexpr (POOL) {
       if (t == t_wait) {
         for (uint32_t it = 0; ld_dev(a.pool_done) < (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
           __builtin_amdgcn_s_sleep(2);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return FMT == HCA_MXFP4;
       }
     }
+    return false;
   };
 #pragma unroll
   for (int t = 0; t < kRing; ++t) {
     if (t < kTilesPerWave && !idle) {
-      pool_wait(t);
-      load_tile(t, kr[t], ks[t]);
+      const bool coh = pool_wait(t);
+      load_tile(t, kr[t], ks[t], coh);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -473,7 +488,7 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t + kRing < kTilesPerWave) {
-        pool_wait(t + kRing);
+        (void)pool_wait(t + kRing);
         load_tile(t + kRing, kr[slot], ks[slot]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -491,7 +506,10 @@ __device__ __forceinline__ void score_quant_body(const IndexerArgs& a, const Poo
       const v8i kv1 = {(int)kr[slot][1].x, (int)kr[slot][1].y, (int)kr[slot][1].z, (int)kr[slot][1].w, 0, 0, 0, 0};
       const int ksw = ks[slot][0];
       __builtin_amdgcn_sched_barrier(0);
-      if (t + kRing < kTilesPerWave) load_tile(t + kRing, kr[slot], ks[slot]);
+      if (t + kRing < kTilesPerWave) {
+        const bool coh = pool_wait(t + kRing);
+        load_tile(t + kRing, kr[slot], ks[slot], coh);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
@@ -545,10 +563,10 @@ score_quant_kernel(IndexerArgs a) {
   score_quant_body<FMT, XQ, HT, TPW, PAGED, false>(a, none);
 }
 
-// the same scoring with the step's pooling in the leading grid rows (decode); three
-// waves per SIMD, as the scoring kernel reaches by itself
+// the same scoring with the step's pooling in the leading grid rows (decode), at the
+// scoring kernel's own occupancy (FP8: three waves per SIMD)
 template <int FMT, int HT, int TPW, bool PAGED>
-__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(FMT == HCA_MXFP4 ? HCA_SCORE_WAVES : 3)))
 score_pool_kernel(IndexerArgs a, PoolArgs p) {
   score_quant_body<FMT, false, HT, TPW, PAGED, true>(a, p);
 }
@@ -1302,7 +1320,7 @@ WsLayout ws_layout(int Nq, int64_t max_visible, int fmt, int k) {
 template <int FMT, bool XQ, int TPW>
 void launch_score(const IndexerArgs& a, dim3 grid, hipStream_t s, const PoolArgs* pool = nullptr) {
   const bool h2 = a.H_I == 64;
-  if constexpr (!XQ && FMT == HCA_FP8_E4M3) {          // the formats pool_fusable admits
+  if constexpr (!XQ && TPW <= 16) {                    // the decode tilings pool_fusable admits
     if (pool) {                                          // grid rows [0, pool_rows) pool
       const dim3 gp(grid.x, grid.y + (unsigned)a.pool_rows);
       if (a.page_shift >= 0) {
@@ -1382,7 +1400,7 @@ void launch_score_phase(const GroupPlan& p, hipStream_t s, const PoolArgs* pool 
     const dim3 g2((unsigned)chunks, a.Nq), gx((unsigned)(chunks * (((int64_t)a.Nq + 7) / 8 * 8)));
     constexpr int T8 = HCA_SCORE_TPW, T4 = HCA_SCORE_TPW4, T4D = HCA_SCORE_TPW4D;
     if (a.fmt == HCA_FP8_E4M3) launch_score<HCA_FP8_E4M3, false, T8>(a, g2, s, pool);
-    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s);
+    else if (few4) launch_score<HCA_MXFP4, false, T4D>(a, g2, s, pool);
     else if (HCA_SCORE_XCD_MAJOR) launch_score<HCA_MXFP4, true, T4>(a, gx, s);
     else launch_score<HCA_MXFP4, false, T4>(a, g2, s);
   }
@@ -1480,20 +1498,25 @@ size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
 }
 
 namespace {
-// tiles per wave of the chunk-major FP8 scoring launch
-int kFusedTpw(const IndexerArgs&) { return HCA_SCORE_TPW; }
+// tiles per wave of the chunk-major scoring launch a decode call takes
+int kFusedTpw(const IndexerArgs& a) { return a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : HCA_SCORE_TPW4D; }
 
-// The step's pooling can ride in the scoring launch: one query group scored chunk-major,
-// FP8 keys whose rows fill whole 128-byte cache lines (pitch and base multiples of 128:
-// a new row then shares no line with a row another workgroup reads, so after its wait
-// and acquire the waiting workgroup cannot meet a stale copy of it, whatever the
-// workgroup-to-XCD mapping), blocks of at most 16 BF16 rows of 512 dims with an index
-// stream (the fast pooling path at 256 threads), and at least one key to score.
-// (MXFP4 rows are 64 bytes with 4-byte scales, which neighbouring rows share.)
+// The step's pooling can ride in the scoring launch: one query group scored chunk-major
+// (FP8, or MXFP4 with few queries), blocks of at most 16 BF16 rows of 512 dims with an
+// index stream (the fast pooling path at 256 threads), and at least one key to score.
+// No stale copy of a new row can be read: FP8 rows must fill whole 128-byte cache lines
+// (pitch and base multiples of 128), so a new row shares no line with a row another
+// wave reads, and after its wait and acquire the one wave that reads it cannot meet a
+// cached copy, whatever the workgroup-to-XCD mapping; MXFP4 rows (64 bytes, 4-byte
+// scales) share lines with their neighbours, so the tile holding the new row is read
+// with coherent loads.
 bool pool_fusable(const IndexerArgs& a, const PoolArgs& p) {
-  if (a.fmt != HCA_FP8_E4M3 || a.max_visible <= 0) return false;
-  if (a.key_pitch % 128 != 0 || reinterpret_cast<uintptr_t>(a.keys) % 128 != 0) return false;
+  if (a.fmt == HCA_F32 || a.max_visible <= 0) return false;
   if (indexer_group(a.Nq, a.max_visible, a.fmt, a.k) < a.Nq) return false;
+  if (a.fmt == HCA_FP8_E4M3 && (a.key_pitch % 128 != 0 || reinterpret_cast<uintptr_t>(a.keys) % 128 != 0))
+    return false;
+  const bool many = a.Nq >= kDigitMinQ || a.many;
+  if (a.fmt == HCA_MXFP4 && (a.Nq >= kFewQ || many)) return false;
   return pool_fast_path(p) && p.m <= 16 && p.idx_fmt >= 0 && p.out_idx == a.keys && p.idx_pitch == a.key_pitch;
 }
 }  // namespace

@@ -7,8 +7,8 @@ index key).  Before each run the rows the step pools are overwritten with the
 largest codes, so a scoring or attention workgroup that read a pooled row before the
 pooling wrote it would change the result: the FP8 pooling that rides in the
 scoring (CSA, FP8 keys) or attention (HCA) launch is checked for its wait, not only
-for its arithmetic.  Cases: FP8 indexer keys (pooling inside the scoring launch) and
-MXFP4 ones (pooling launched first), paged caches, many blocks per launch (64
+for its arithmetic.  Cases: FP8 and MXFP4 indexer keys (pooling inside the scoring
+launch; the MXFP4 tile that holds the new row read with coherent loads), paged caches, many blocks per launch (64
 sequences, all completing a block), the pooled entry as the only entry, HCA layers
 (pooling inside the attention launch, default plan and fixed split), the f32 tiny
 layers (separate launches), and the profiled form."""
