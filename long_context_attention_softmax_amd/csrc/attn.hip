@@ -423,13 +423,13 @@ __device__ __forceinline__ int find_query(const int* pref, int nq, int c) {
 }
 
 // POOL (decode layouts Flat and SplitFlat): the grid's first pool_wgs workgroups pool
-// one block each (HCA: a block's tokens complete its sequence's newest entry) and
-// count themselves; the rest run the attention plan over gridDim.x - pool_wgs
-// workgroups, and the one that stages the chunk holding a query's newest entry V - 1
-// waits for every count first.  The pooling workgroups lead the dispatch order, so
-// they are running whenever a workgroup waits; the wait is bounded all the same.
+// one block each (HCA: a block's tokens complete its sequence's newest entry) and set
+// their flags to the call's epoch; the rest run the attention plan over
+// gridDim.x - pool_wgs workgroups, and the one that stages the chunk holding a query's
+// newest entry V - 1 waits for every flag first.  The pooling workgroups lead the
+// dispatch order, so they are running whenever a workgroup waits; the wait is bounded
+// all the same.
 typedef PoolSmem<kThreads, 16, false> AttnPoolSmem;       // blocks of m <= 128 tokens, no index stream
-constexpr uint32_t kPoolSpinMax = 1u << 22;
 
 template <int layout, bool POOL>
 __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs& pool) {
@@ -459,14 +459,7 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
     if ((int)blockIdx.x < a.pool_wgs) {
       if ((int)blockIdx.x < pool.n_blocks) {
         pool_d512_block<kThreads, 16, false>(pool, blockIdx.x, *reinterpret_cast<AttnPoolSmem*>(Ks));
-        // every thread's stores complete, then the XCD's cache is written back before
-        // the count is raised
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        if (tid == 0) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          atomicAdd(a.pool_done, 1u);
-        }
+        flag_set(a.flags + blockIdx.x, a.epoch);   // stores written back, then the block's flag
       }
       return;                                       // uniform over the workgroup
     }
@@ -480,12 +473,7 @@ __device__ __forceinline__ void attn_mqa_body(const AttnArgs& a, const PoolArgs&
     return POOL && !csa && qs.n_ent > 0 && p <= qs.n_ent - 1 && qs.n_ent - 1 < p + KC;
   };
   auto pool_wait = [&]() {
-    if (tid == 0) {
-      for (uint32_t it = 0; __hip_atomic_load(a.pool_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                                (uint32_t)a.pool_target && it < kPoolSpinMax; ++it)
-        __builtin_amdgcn_s_sleep(2);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
+    if (wave == 0) flags_wait(a.flags, a.pool_wgs, a.epoch);   // every block's flag, then acquire
     __syncthreads();
   };
 
@@ -1068,15 +1056,12 @@ hipError_t attention_static_scratch(void** ptr) {
 }
 
 namespace {
+constexpr int kMaxAttnPoolBlocks = 64;     // blocks one fused attention launch pools at most
 // bytes of the split partials (the prefix header, max and sum, o); the fused pooling's
-// count follows them
+// flags follow them
 size_t partial_bytes(int Nq, int H, int runs) {
   const size_t slots = partial_slots(Nq, runs);
   return round256((size_t)(Nq + 2) * 4) + 2 * round256(slots * H * 4) + round256(slots * H * kD * 2);
-}
-
-__global__ void __launch_bounds__(64) clear_count_kernel(uint32_t* p) {
-  if (threadIdx.x == 0) *p = 0u;
 }
 
 // The step's pooling can ride in the attention launch: a decode plan shared over the
@@ -1087,7 +1072,7 @@ __global__ void __launch_bounds__(64) clear_count_kernel(uint32_t* p) {
 bool attn_pool_fusable(const AttnArgs& a, const PoolArgs& p) {
   if (a.io_f32 || a.prefill || a.mode == HCA_MODE_CSA || !a.workspace) return false;
   if (!decode_layout(a.Nq, a.prefill, a.mode, a.k, a.n_win, a.max_visible)) return false;
-  return pool_fast_path(p) && p.m > 16 && p.m <= 128 && p.idx_fmt < 0 && p.n_blocks <= 64;
+  return pool_fast_path(p) && p.m > 16 && p.m <= 128 && p.idx_fmt < 0 && p.n_blocks <= kMaxAttnPoolBlocks;
 }
 }  // namespace
 
@@ -1097,7 +1082,7 @@ size_t attention_workspace_bytes(int Nq, int H, int D, int mode, int k, int n_wi
   if (io_f32 || prefill) return 0;
   const int64_t runs = attention_split_runs(mode, k, n_win, max_visible, split_chunks);
   if (runs <= 0 && !decode_layout(Nq, prefill, mode, k, n_win, max_visible)) return 0;
-  return partial_bytes(Nq, H, (int)runs) + 256;
+  return partial_bytes(Nq, H, (int)runs) + 8 * kMaxAttnPoolBlocks;   // + the fused pooling's flags
 }
 
 hipError_t launch_attention(const AttnArgs& a0, hipStream_t s, const PoolArgs* pool) {
@@ -1110,12 +1095,11 @@ hipError_t launch_attention(const AttnArgs& a0, hipStream_t s, const PoolArgs* p
   if (a0.Nq == 0) return hipSuccess;
   AttnArgs a = a0;
   if (pool) {
-    // the count lives after the partials; cleared before the launch that raises it
-    a.pool_done = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) +
-                                              partial_bytes(a.Nq, a.H, a.split_runs > 0 ? a.split_runs : 0));
+    // the blocks' epoch flags live after the partials (no clearing: a fresh epoch per call)
+    a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) +
+                                          partial_bytes(a.Nq, a.H, a.split_runs > 0 ? a.split_runs : 0));
     a.pool_wgs = pool->n_blocks;
-    a.pool_target = pool->n_blocks;
-    hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(64), 0, s, a.pool_done);
+    a.epoch = fused_epoch();
   }
   if (a.io_f32) {
     if (a.prof_begin) (void)hipEventRecord(a.prof_begin, s);

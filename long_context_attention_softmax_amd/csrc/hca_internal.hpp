@@ -58,6 +58,8 @@ struct IndexerArgs {
 // call; fused into the scoring launch where the launch plan allows, else launched first
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s, const PoolArgs* pool = nullptr);
 bool pool_fast_path(const PoolArgs& a);
+// a fresh 64-bit epoch for one fused launch (never 0)
+uint64_t fused_epoch();
 size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k);
 // queries per launch group of a call with Nq queries (its workspace holds one group)
 int indexer_group(int Nq, int64_t max_visible, int fmt, int k);
@@ -82,10 +84,12 @@ struct AttnArgs {
   const int32_t* page_table; int64_t page_pitch; int page_shift;   // paged entries (page_shift >= 0)
   int split_chunks, split_runs;       // decode fixed split: chunks per run, most runs of a query (0 = off)
   double inv_turn[32];                // BF16 path: rope_base^(-2i/64) / (2 pi), turns per position
-  // fused decode pooling (HCA): workgroups [0, pool_wgs) pool the step's blocks and count
-  // themselves in *pool_done; the one staging a query's newest entry waits for pool_target
-  int pool_wgs, pool_target;
-  uint32_t* pool_done;
+  // fused decode pooling (HCA): workgroups [0, pool_wgs) pool the step's blocks, each
+  // setting its flag (flags[0 .. pool_wgs)) to epoch; the one staging a query's newest
+  // entry waits for all of them
+  int pool_wgs;
+  uint64_t* flags;
+  uint64_t epoch;
 };
 // pool (optional, decode): blocks to pool before attention, in the same call; fused
 // into the attention launch where the launch plan allows, else launched first

@@ -14,6 +14,10 @@
 #include "../../include/hca.h"
 #include "pool_block.hpp"
 
+#include <atomic>
+#include <chrono>
+#include <random>
+
 namespace hca {
 
 namespace {
@@ -262,6 +266,15 @@ __global__ void __launch_bounds__(NT) pool_d512_kernel(PoolArgs a) {
 }
 
 }  // namespace
+
+uint64_t fused_epoch() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
+  }()};
+  return next.fetch_add(2);                            // odd values only: never 0
+}
 
 bool pool_fast_path(const PoolArgs& a) {
   return !a.raw_is_f32 && a.D == kFastD && a.D_r == kFastDr && a.m <= 128 &&

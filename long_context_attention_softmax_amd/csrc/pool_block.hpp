@@ -15,6 +15,38 @@ namespace hca {
 
 constexpr int kFastD = 512, kFastDr = 64, kFastMaxDI = 256;
 
+// ---------------------------------------------------------------- fused launches
+// A pooling workgroup of a fused attention launch signals its block with a 64-bit flag
+// set to the call's epoch, a number the host draws once per call (hca::fused_epoch: a
+// counter seeded at random per process), so no flag needs clearing before the launch:
+// a flag left by an earlier call, or uninitialised memory, holds another value (a
+// chance match is one in 2^64).
+constexpr uint32_t kFlagSpinMax = 1u << 22;              // polls before a wait gives up
+
+// every thread of the workgroup: its stores complete and written back past the XCD's
+// cache, then the workgroup's flag set
+__device__ __forceinline__ void flag_set(uint64_t* flag, uint64_t epoch) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// one whole wave: until flags[0 .. n) all hold epoch (bounded), then acquire
+__device__ __forceinline__ void flags_wait(uint64_t* flags, int n, uint64_t epoch) {
+  const int lane = threadIdx.x & 63;
+  for (uint32_t it = 0; it < kFlagSpinMax; ++it) {
+    bool ok = true;
+    for (int i = lane; i < n; i += 64)
+      ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // LDS of one pooling workgroup of NT threads, TOK tokens per wave
 template <int NT, int TOK, bool Y>
 struct PoolSmem {
