@@ -919,6 +919,10 @@ __global__ void __launch_bounds__(kThreads) attn_pool_kernel(AttnArgs a, PoolArg
 // reduced with cross-lane operations (lane t holds runs t, t + 64, ...; its own runs
 // in order, then a fixed butterfly), the weights go through the wave's own LDS row,
 // and lane t merges dims 8t .. 8t + 7 of every run in run order.
+#ifndef HCA_COMBINE_BATCH
+#define HCA_COMBINE_BATCH 16
+#endif
+constexpr int kCombineBatch = HCA_COMBINE_BATCH;          // runs whose rows are in flight together
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   __shared__ float s_w[4][kMaxRuns];
   const int n = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -974,14 +978,15 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const __bf16* po = pp.o + slot0 * kD + 8 * lane;
   const size_t ostride = sstride * kD;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // eight runs' rows requested at once, then added in run order
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    uint4 v[8];
+  // kCombineBatch runs' rows requested at once, then added in run order (the order,
+  // and so the bits, do not depend on the batch)
+  for (int s0 = 0; s0 < S; s0 += kCombineBatch) {
+    uint4 v[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kCombineBatch; ++u)
       v[u] = s0 + u < S ? *reinterpret_cast<const uint4*>(po + (size_t)(s0 + u) * ostride) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kCombineBatch; ++u) {
       if (s0 + u < S) {
         const float w = s_w[wave][s0 + u];
         const uint32_t* vw = &v[u].x;
