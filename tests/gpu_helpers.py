@@ -108,21 +108,29 @@ MAX_ERR = {"quant": [0.0, 0.0], "f32": [0.0, 0.0]}
 
 
 def run_and_compare(lay, g, dev=None, queries=None, prefill=False, tol=None, check_scores=True,
-                    page_rows=None, oracle_threads=1):
+                    page_rows=None, oracle_threads=1, fused=False):
     """Run the layer's step on the GPU and compare every stage with the oracle.
-    ``page_rows`` lays the compressed cache out in shuffled pages of that size.
+    ``page_rows`` lays the compressed cache out in shuffled pages of that size;
+    ``fused`` runs the decode step as one hca_decode_layer call (pooling, top-k and
+    attention; the selected scores still come back) instead of three calls.
 
     Returns (oracle result, device layer, output error)."""
     from long_context_attention_softmax_amd.layer import DeviceLayer
+    from long_context_attention_softmax_amd.ops import hca_decode_layer
     dev = dev or DeviceLayer.from_host(lay, g, page_rows=page_rows)
     tol = tol if tol is not None else (TOL_F32 if dev.f32 else TOL_QUANT)
-    dev.pool()
     score = None
     if dev.mode == 0:
         score = torch.zeros((dev.Nq, g.topk), dtype=torch.float64 if dev.f32 else torch.float32,
                             device=dev.device)
-        dev.select(score=score)
-    o = dev.attend(prefill=prefill)
+    if fused and not prefill:
+        o = hca_decode_layer(dev._attend_kw(), pool=dev._pool_kw(),
+                             indexer=dev._select_kw(score=score) if dev.mode == 0 else None)
+    else:
+        dev.pool()
+        if dev.mode == 0:
+            dev.select(score=score)
+        o = dev.attend(prefill=prefill)
     torch.cuda.synchronize()
     ref = oracle_layer(lay, g, queries=queries, threads=oracle_threads)
     qs = ref["queries"]

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import to_np
+from gpu_helpers import run_and_compare, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -135,3 +135,13 @@ def test_decode_layer_profiled(gpu):
     for lay in w.layers:
         _print(f"decode layer profiled {lay.mode}")
         _compare(lay, w.g, prof=True)
+
+
+@pytest.mark.parametrize("idx_fmt", ["fp8", "mxfp4"])
+def test_decode_layer_matches_the_oracle(gpu, idx_fmt):
+    # the fused step against the oracle directly: pooled codes, exact top-k and its
+    # scores, outputs within the bars
+    w = synth.ragged_pair(seed=47, B=10, lo=2048, hi=300000, round_every4=True, idx_fmt=idx_fmt)
+    for lay in w.layers:
+        _print(f"decode layer vs oracle {lay.mode} {idx_fmt}: {len(lay.pool['out_row'])} blocks pooled")
+        run_and_compare(lay, w.g, fused=True, oracle_threads=8)
