@@ -689,8 +689,19 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   const float* sc = reinterpret_cast<const float*>(a.scores) + (int64_t)n * a.score_pitch;
   const int64_t j1 = j0 + kChunk1 < V ? j0 + kChunk1 : V;
   const int64_t jt = j0 + (int64_t)kPerThread1 * tid;
-  uint32_t key[kPerThread1];
-  load_chunk_keys(sc, jt, j1, key);
+  // raw score bits; the first digit is taken from them exactly as the scoring kernel
+  // histogrammed it (a score is never -0), the full orderable key only for the keys
+  // that are appended
+  uint32_t bits[kPerThread1];
+#pragma unroll
+  for (int v = 0; v < kPerThread1 / 4; ++v) {
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jt + 4 * v < j1) f = *reinterpret_cast<const float4*>(sc + jt + 4 * v);   // rows padded to 64
+    bits[4 * v] = __float_as_uint(f.x); bits[4 * v + 1] = __float_as_uint(f.y);
+    bits[4 * v + 2] = __float_as_uint(f.z); bits[4 * v + 3] = __float_as_uint(f.w);
+  }
+  const int64_t rem = j1 - jt;
+  const int nv = rem <= 0 ? 0 : (rem >= kPerThread1 ? kPerThread1 : (int)rem);   // this thread's scores
   uint32_t d1;
   if constexpr (PRE) {
     d1 = ws.d1[n];
@@ -707,18 +718,14 @@ __global__ void __launch_bounds__(256) select_collect_kernel(IndexerArgs a, Sele
   uint32_t gt = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread1; ++e) {
-    if (jt + e < j1) {
-      const uint32_t dg = key[e] >> 21;
-      gt += dg > d1;
-      if (dg == d1) {
-        const uint32_t p = atomicAdd(&s_n, 1u);           // LDS: at most kChunk1 per chunk
-        s_ck[p] = key[e];
-        s_cj[p] = (uint16_t)(jt + e - j0);
-      } else if (merged && dg > d1) {
-        const uint32_t p = kChunk1 - 1 - atomicAdd(&s_na, 1u);
-        s_ck[p] = key[e];
-        s_cj[p] = (uint16_t)(jt + e - j0);
-      }
+    const uint32_t b = bits[e];
+    const uint32_t dg = (b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 21;
+    const bool in = e < nv;
+    gt += (in && dg > d1) ? 1u : 0u;
+    if (in && dg >= d1 && (dg == d1 || merged)) {      // rare: a candidate, or a key above d1
+      const uint32_t p = dg == d1 ? atomicAdd(&s_n, 1u) : kChunk1 - 1 - atomicAdd(&s_na, 1u);
+      s_ck[p] = float_key(__uint_as_float(b));
+      s_cj[p] = (uint16_t)(jt + e - j0);
     }
   }
   uint32_t tot;
