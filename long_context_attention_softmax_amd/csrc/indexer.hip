@@ -1506,7 +1506,7 @@ size_t indexer_workspace_bytes(int Nq, int64_t max_visible, int fmt, int k) {
 
 namespace {
 // tiles per wave of the chunk-major scoring launch a decode call takes
-int kFusedTpw(const IndexerArgs& a) { return a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : HCA_SCORE_TPW4D; }
+int fused_tpw(const IndexerArgs& a) { return a.fmt == HCA_FP8_E4M3 ? HCA_SCORE_TPW : HCA_SCORE_TPW4D; }
 
 // The step's pooling can ride in the scoring launch: one query group scored chunk-major
 // (FP8, or MXFP4 with few queries), blocks of at most 16 BF16 rows of 512 dims with an
@@ -1551,7 +1551,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, hipStream_t s, const PoolA
   if (G >= a0.Nq) {                                      // one group, one stream
     GroupPlan p = plan_group(a0);
     if (pool) {
-      const int64_t chunks = (p.a.max_visible + entries_per_wg_t(kFusedTpw(p.a)) - 1) / entries_per_wg_t(kFusedTpw(p.a));
+      const int64_t chunks = (p.a.max_visible + entries_per_wg_t(fused_tpw(p.a)) - 1) / entries_per_wg_t(fused_tpw(p.a));
       const int64_t cx = chunks > 0 ? chunks : 1;
       p.a.pool_rows = (int)((pool->n_blocks + cx - 1) / cx);
       p.a.pool_target = pool->n_blocks;
