@@ -258,10 +258,10 @@ __device__ __forceinline__ float head_sum(const v16f (&acc)[2], const float (&wv
 // come through the page table, one page per 32-entry tile.
 // POOL (decode, chunk-major): the grid's leading pool_rows rows pool the step's
 // blocks (the block's tokens complete its sequence's newest entry) and count
-// themselves; the one workgroup per query whose range holds that query's newest
-// entry V - 1 waits for every count before it loads a key.  The pooling workgroups
-// lead the dispatch order, so they are running whenever a workgroup waits; the wait
-// is bounded all the same.
+// themselves; in the workgroup whose range holds a query's newest entry V - 1, the
+// one wave whose tiles hold it waits for every count just before it loads that tile.
+// The pooling workgroups lead the dispatch order, so they are running whenever a
+// wave waits; the wait is bounded all the same.
 typedef PoolSmem<kScoreThreads, 4, true> ScorePoolSmem;     // blocks of m <= 16 tokens
 constexpr uint32_t kPoolSpinMax = 1u << 22;
 
