@@ -915,18 +915,27 @@ __global__ void __launch_bounds__(kThreads) attn_pool_kernel(AttnArgs a, PoolArg
 // with w_s = 2^(m_s - M) l_s
 // Fixed split (split_runs > 0): query n's runs are slots n * split_runs + s, s <
 // its run count; the attention kernel has already finished queries with one run.
-// One wave per (query, head), four heads per workgroup: the runs' (max, sum) are
-// reduced with cross-lane operations (lane t holds runs t, t + 64, ...; its own runs
-// in order, then a fixed butterfly), the weights go through the wave's own LDS row,
-// and lane t merges dims 8t .. 8t + 7 of every run in run order.
-#ifndef HCA_COMBINE_BATCH
-#define HCA_COMBINE_BATCH 16
+// One wave per (query, head, P-th part of the dims), four heads per workgroup: every
+// wave reduces the runs' (max, sum) itself with cross-lane operations (lane t holds
+// runs t, t + 64, ...; its own runs in order, then a fixed butterfly), the weights go
+// through the wave's own LDS row, and lane t merges 8 / P consecutive dims of its part
+// (part blockIdx.z) of every run in run order.  With very few queries (a grid under
+// half the CUs, e.g. 4 queries of 64 heads merging about 63 runs each) the dims are
+// split in four, so 4x the workgroups, and 2x the runs per wave, have their rows in
+// flight; each element's sum is the same.
+#ifndef HCA_COMBINE_SPLIT_BELOW
+#define HCA_COMBINE_SPLIT_BELOW 128
 #endif
-constexpr int kCombineBatch = HCA_COMBINE_BATCH;          // runs whose rows are in flight together
+constexpr int kCombineSplitBelow = HCA_COMBINE_SPLIT_BELOW;   // workgroups of the unsplit grid
+template <int P>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
+  static_assert(P == 1 || P == 4, "dims per lane: 8 or 2");
+  constexpr int W = 4 / P;                                // 32-bit words (2 dims each) per lane and run
+  constexpr int kBatch = P == 1 ? 16 : 32;                // runs whose rows are in flight together
   __shared__ float s_w[4][kMaxRuns];
   const int n = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave;                    // H is a multiple of 16
+  const int d0 = (kD / P) * blockIdx.z + 2 * W * lane;    // this lane's first dim
   PartialPtrs pp = partial_ptrs(a.workspace, a.Nq, a.H, a.split_runs);
   const float sig = a.sink[h] * (float)kLog2e;
   __bf16* out = reinterpret_cast<__bf16*>(a.o) + ((int64_t)n * a.H + h) * kD;
@@ -935,8 +944,9 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int cnt = a.split_runs > 0 ? (query_info(a, n).n_set + KC - 1) / KC : pp.pref[n + 1] - pp.pref[n];
   if (cnt == 0) {                          // empty set (no window, nothing visible): the sink alone, o = 0
     if (a.split_runs > 0) return;          // written by the attention kernel
-    *reinterpret_cast<uint4*>(out + 8 * lane) = (uint4){0u, 0u, 0u, 0u};
-    if (a.lse && lane == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
+#pragma unroll
+    for (int e = 0; e < W; ++e) reinterpret_cast<uint32_t*>(out + d0)[e] = 0u;
+    if (a.lse && blockIdx.z == 0 && lane == 0) a.lse[(int64_t)n * a.H + h] = a.sink[h];
     return;
   }
   if (a.split_runs > 0) {
@@ -975,35 +985,48 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const float den = exp2f(sig - M) + wave_sum(ws);
   const float inv = 1.0f / den;
   // the wave's own LDS writes above are complete before these reads (in-order LDS)
-  const __bf16* po = pp.o + slot0 * kD + 8 * lane;
+  const __bf16* po = pp.o + slot0 * kD + d0;
   const size_t ostride = sstride * kD;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // kCombineBatch runs' rows requested at once, then added in run order (the order,
-  // and so the bits, do not depend on the batch)
-  for (int s0 = 0; s0 < S; s0 += kCombineBatch) {
-    uint4 v[kCombineBatch];
+  float acc[2 * W];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)
-      v[u] = s0 + u < S ? *reinterpret_cast<const uint4*>(po + (size_t)(s0 + u) * ostride) : make_uint4(0, 0, 0, 0);
+  for (int e = 0; e < 2 * W; ++e) acc[e] = 0.f;
+  // kBatch runs' rows requested at once, then added in run order (the order, and so
+  // the bits, do not depend on the batch or the split)
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    uint32_t v[kBatch][W];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(po + (size_t)(s0 + u) * ostride);
+      if constexpr (W == 4) {
+        const uint4 q = s0 + u < S ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        const uint32_t* qw = &q.x;
+#pragma unroll
+        for (int e = 0; e < W; ++e) v[u][e] = qw[e];
+      } else {
+        v[u][0] = s0 + u < S ? *src : 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
       if (s0 + u < S) {
         const float w = s_w[wave][s0 + u];
-        const uint32_t* vw = &v[u].x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_to_f32((uint16_t)vw[e]) * w;
-          acc[2 * e + 1] += bf16_to_f32((uint16_t)(vw[e] >> 16)) * w;
+        for (int e = 0; e < W; ++e) {
+          acc[2 * e] += bf16_to_f32((uint16_t)v[u][e]) * w;
+          acc[2 * e + 1] += bf16_to_f32((uint16_t)(v[u][e] >> 16)) * w;
         }
       }
     }
   }
-  uint4 o4;
-  uint32_t* ow = &o4.x;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ow[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-  *reinterpret_cast<uint4*>(out + 8 * lane) = o4;
-  if (a.lse && lane == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
+  for (int e = 0; e < W; ++e) reinterpret_cast<uint32_t*>(out + d0)[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  if (a.lse && blockIdx.z == 0 && lane == 0) a.lse[(int64_t)n * a.H + h] = (M + log2f(den)) / (float)kLog2e;
+}
+
+void launch_combine(const AttnArgs& a, hipStream_t s) {
+  const int wgs = a.Nq * (a.H / 4);
+  if (wgs < kCombineSplitBelow) hipLaunchKernelGGL(combine_kernel<4>, dim3(a.Nq, a.H / 4, 4), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(combine_kernel<1>, dim3(a.Nq, a.H / 4, 1), dim3(256), 0, s, a);
 }
 
 // Decode layout: few queries spread over one flattened chunk list (chunk counts
@@ -1122,7 +1145,7 @@ hipError_t launch_attention(const AttnArgs& a0, hipStream_t s, const PoolArgs* p
     else if (flat) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplitFlat>, dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutSplit>, dim3(grid), dim3(kThreads), 0, s, a);
     if (a.prof_end) (void)hipEventRecord(a.prof_end, s);
-    if (a.split_runs > 1) hipLaunchKernelGGL(combine_kernel, dim3(a.Nq, a.H / 4), dim3(256), 0, s, a);
+    if (a.split_runs > 1) launch_combine(a, s);
     return hipGetLastError();
   }
   AttnArgs b = a;
@@ -1134,7 +1157,7 @@ hipError_t launch_attention(const AttnArgs& a0, hipStream_t s, const PoolArgs* p
   else if (dec) hipLaunchKernelGGL(attn_mqa_kernel<kLayoutFlat>, dim3(HCA_ATTN_GRID), dim3(kThreads), 0, s, b);
   else hipLaunchKernelGGL(attn_mqa_kernel<kLayoutQuery>, dim3(b.Nq), dim3(kThreads), 0, s, b);
   if (b.prof_end) (void)hipEventRecord(b.prof_end, s);
-  if (dec) hipLaunchKernelGGL(combine_kernel, dim3(b.Nq, b.H / 4), dim3(256), 0, s, b);
+  if (dec) launch_combine(b, s);
   return hipGetLastError();
 }
 
